@@ -1,0 +1,426 @@
+"""Pins for the CPU oracle, independent of the oracle's own code.
+
+Each check ties the oracle to something it does not compute itself: a
+library routine (numpy's stable argsort, torch's number-format casts), a
+brute force written here in plain Python, a closed form, an invariant, a
+hand-worked example, or the receive bound printed in "Enabling
+trillion-parameter models on AWS EFA", section "Send and receive buffers".
+"""
+import bisect
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import ep_workloads as W
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# Brute-force helpers written independently of the oracle
+# ---------------------------------------------------------------------------
+
+def _all_finite_bf16():
+    """Every finite bf16 value as (exact Fraction, bit pattern), sorted."""
+    bits = np.arange(0, 0x10000, dtype=np.uint32)
+    vals = ((bits << 16).astype(np.uint32)).view(np.float32)
+    out = {}
+    for b, v in zip(bits.tolist(), vals.tolist()):
+        if np.isfinite(v):
+            fr = Fraction(v)
+            # keep +0 for zero, the even pattern wins ties below anyway
+            if fr not in out or (b & 0x8000) == 0:
+                out[fr] = b
+    keys = sorted(out)
+    return keys, [out[k] for k in keys]
+
+
+_BF16_TABLE = None
+
+
+def brute_bf16_round(x: Fraction) -> int:
+    """Nearest bf16 to an exact rational, ties to the even pattern."""
+    global _BF16_TABLE
+    if _BF16_TABLE is None:
+        _BF16_TABLE = _all_finite_bf16()
+    keys, bits = _BF16_TABLE
+    if x == 0:
+        return 0
+    if x < 0:                       # round the magnitude, keep the sign (-0)
+        return 0x8000 | brute_bf16_round(-x)
+    i = bisect.bisect_left(keys, x)
+    if i < len(keys) and keys[i] == x:
+        return bits[i]
+    lo, hi = keys[i - 1], keys[i]
+    dlo, dhi = x - lo, hi - x
+    if dlo < dhi:
+        return bits[i - 1]
+    if dhi < dlo:
+        return bits[i]
+    return bits[i - 1] if bits[i - 1] % 2 == 0 else bits[i]
+
+
+def bf16_value(b: int) -> Fraction:
+    return Fraction(float(np.array([b << 16], np.uint32).view(np.float32)[0]))
+
+
+def brute_plan(idx, N, T, E, R, cap):
+    """Layout by sorting tuples, one destination at a time (plain Python)."""
+    L = E // N
+    send_pos = np.full((N, T, R), -1, np.int64)
+    for s in range(N):
+        slots = [(int(idx[s, t, k]), t, k) for t in range(T) for k in range(R)
+                 if 0 <= idx[s, t, k] < E]
+        for p, (_, t, k) in enumerate(sorted(slots)):
+            send_pos[s, t, k] = p
+    grp_pos = np.full((N, T, R), -1, np.int64)
+    totals = []
+    for d in range(N):
+        mine = [(int(idx[s, t, k]) - d * L, s, t, k)
+                for s in range(N) for t in range(T) for k in range(R)
+                if 0 <= idx[s, t, k] < E and idx[s, t, k] // L == d]
+        for p, (_, s, t, k) in enumerate(sorted(mine)):
+            grp_pos[s, t, k] = p if p < cap else -1
+        totals.append(len(mine))
+    return send_pos, grp_pos, totals
+
+
+def random_idx(rng, N, T, E, R, distinct=True):
+    if distinct:
+        return np.argsort(rng.random((N, T, E)), axis=-1)[..., :R].astype(np.int32)
+    return rng.integers(0, E, size=(N, T, R), dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+def test_rounding_mode():
+    assert oracle.lib().oracle_rounding_mode_is_nearest() == 1
+
+
+def test_f32_to_bf16_matches_torch():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),   # subnormal
+        (rng.standard_normal(2000) * 1e38).astype(np.float32),    # near max
+        np.array([0.0, -0.0, 1.0, -1.0, 3.3895314e38, 1.00390625,
+                  1.01171875, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8], np.float32),
+    ])
+    # every representable tie in one binade: 1 + (2m+1) * 2^-8
+    vals = np.concatenate([vals, (1.0 + (2 * np.arange(128) + 1) * 2.0 ** -8).astype(np.float32)])
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f32_to_bf16(float(v)) for v in vals], np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_f64_to_bf16_matches_brute_force():
+    """Single rounding from double, checked against the nearest of all bf16."""
+    rng = np.random.default_rng(2)
+    vals = list(rng.standard_normal(3000) * 10.0)
+    vals += list(rng.standard_normal(300) * 1e-39)
+    # double-rounding traps: a float cast first would round these to a tie
+    vals += [1.0 + 2 ** -8 + 2 ** -30, 1.0 + 2 ** -8 - 2 ** -30,
+             -(1.0 + 2 ** -8 + 2 ** -40), 3.0 + 2 ** -7 + 2 ** -35]
+    for v in vals:
+        assert oracle.f64_to_bf16(v) == brute_bf16_round(Fraction(v)), v
+    # 1 + 2^-8 + 2^-30 lies above the tie between 1 and 1 + 2^-7
+    assert oracle.f64_to_bf16(1.0 + 2 ** -8 + 2 ** -30) == 0x3F81
+    assert oracle.f64_to_bf16(1.0 + 2 ** -8) == 0x3F80          # tie -> even
+
+
+def test_bf16_to_f32_exact():
+    for b in [0x0000, 0x8000, 0x3F80, 0xBF80, 0x7F7F, 0x0001, 0x4049]:
+        assert oracle.bf16_to_f32(b) == float(np.array([b << 16], np.uint32).view(np.float32)[0])
+
+
+def test_e4m3_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    got = np.array([oracle.e4m3_to_f32(int(c)) for c in codes], np.float32)
+    nan = np.isnan(want)
+    assert nan.sum() == 2                       # S.1111.111 only
+    assert np.isnan(got[nan]).all()
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+# ---------------------------------------------------------------------------
+# Receive bound (printed formula)
+# ---------------------------------------------------------------------------
+
+def test_recv_bound_golden():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "recv_bound.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) >= 5
+    for name, N, T, E, R, bound in rows:
+        assert oracle.recv_bound(int(N), int(T), int(E), int(R)) == int(bound), name
+
+
+# ---------------------------------------------------------------------------
+# Plan
+# ---------------------------------------------------------------------------
+
+HAND_IDX = np.array([[[1, 2], [0, 1]], [[3, 1], [1, 0]]], np.int32)
+
+
+def test_plan_hand_worked_example():
+    """N=2, T=2, E=4, R=2 (L=2), worked out by hand from the definitions."""
+    p = oracle.plan(2, 2, 4, 2, 8, HAND_IDX)
+    assert p["status"] == 0
+    np.testing.assert_array_equal(p["cnt"], [[1, 2, 1, 0], [1, 2, 0, 1]])
+    np.testing.assert_array_equal(p["send_off"], [[0, 1, 3, 4, 4], [0, 1, 3, 3, 4]])
+    np.testing.assert_array_equal(p["send_pos"], [[[1, 3], [0, 2]], [[3, 1], [2, 0]]])
+    np.testing.assert_array_equal(p["recv_off"], [[0, 3, 6], [0, 1, 2]])
+    np.testing.assert_array_equal(p["grp_off"], [[0, 2, 6], [0, 1, 2]])
+    np.testing.assert_array_equal(p["grp_pos"], [[[2, 0], [0, 3]], [[1, 4], [5, 1]]])
+
+
+def test_payload_hand_worked_example():
+    """Token rows tagged by (s, t); send, receive and grouped rows by hand."""
+    sh = W.Shape("hand", 2, 2, 8, 4, 2)
+    wl = W.make_workload(sh, idx=HAND_IDX)
+    tag = np.zeros((2, 2, 16), np.uint8)
+    for s in range(2):
+        for t in range(2):
+            tag[s, t, :] = 10 * s + t + 1           # x_st tagged as 10s+t+1
+    wl.planes = [tag]
+    r = oracle.run(wl, cap=8)
+    first = lambda a: a[..., 0].tolist()
+    # x00=1, x01=2, x10=11, x11=12
+    assert first(r["send"][0]) == [[2, 1, 2, 1], [12, 11, 12, 11]]
+    assert first(r["recv"][0])[0] == [2, 1, 2, 12, 11, 12]
+    assert first(r["recv"][0])[1][:2] == [1, 11]
+    assert first(r["grouped"][0])[0] == [2, 12, 1, 2, 11, 12]
+    assert first(r["grouped"][0])[1][:2] == [1, 11]
+
+
+@pytest.mark.parametrize("N,T,E,R,distinct,seed", [
+    (4, 16, 16, 2, True, 0), (3, 7, 9, 3, True, 1), (1, 9, 5, 2, True, 2),
+    (5, 4, 5, 1, True, 3), (2, 6, 8, 4, False, 4), (6, 3, 12, 5, False, 5),
+])
+def test_plan_matches_brute_force(N, T, E, R, distinct, seed):
+    rng = np.random.default_rng(seed)
+    idx = random_idx(rng, N, T, E, R, distinct)
+    cap = oracle.recv_bound(N, T, E, R)
+    p = oracle.plan(N, T, E, R, cap, idx)
+    sp, gp, totals = brute_plan(idx, N, T, E, R, cap)
+    np.testing.assert_array_equal(p["send_pos"], sp)
+    np.testing.assert_array_equal(p["grp_pos"], gp)
+    np.testing.assert_array_equal(p["recv_off"][:, N], totals)
+    assert p["status"] == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_zipf", "decode", "worst"])
+def test_plan_matches_stable_argsort(name):
+    """Send order of a source is numpy's stable argsort of its expert ids."""
+    sh = W.CONFIGS[name]
+    wl = W.make_workload(sh)
+    N, T, E, R = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk
+    L = E // N
+    p = oracle.plan(N, T, E, R, oracle.recv_bound(N, T, E, R), wl.idx)
+    assert p["status"] == 0
+    for s in range(N):
+        flat = wl.idx[s].ravel()
+        order = np.argsort(flat, kind="stable")
+        inv = np.empty_like(order)
+        inv[order] = np.arange(order.size)
+        np.testing.assert_array_equal(p["send_pos"][s].ravel(), inv)
+        np.testing.assert_array_equal(p["cnt"][s], np.bincount(flat, minlength=E))
+    # grouped order of destination d: stable argsort of (local expert) over
+    # the slot stream of all sources in (s, t, k) order, restricted to d.
+    allflat = wl.idx.reshape(-1)
+    gpf = p["grp_pos"].reshape(-1)
+    for d in range(N):
+        sel = np.nonzero(allflat // L == d)[0]
+        order = sel[np.argsort(allflat[sel] - d * L, kind="stable")]
+        np.testing.assert_array_equal(gpf[order], np.arange(order.size))
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_zipf", "decode", "worst", "decode_zipf"])
+def test_plan_invariants(name):
+    sh = W.CONFIGS[name]
+    wl = W.make_workload(sh)
+    N, T, E, R = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk
+    L = E // N
+    bound = oracle.recv_bound(N, T, E, R)
+    p = oracle.plan(N, T, E, R, bound, wl.idx)
+    assert (p["cnt"].sum(axis=1) == T * R).all()
+    rows = np.array([[p["send_off"][s, (d + 1) * L] - p["send_off"][s, d * L]
+                      for d in range(N)] for s in range(N)])
+    assert (rows.sum(axis=1) == T * R).all()            # per-destination counts
+    for s in range(N):
+        assert sorted(p["send_pos"][s].ravel().tolist()) == list(range(T * R))
+    totals = p["recv_off"][:, N]
+    assert totals.sum() == N * T * R
+    assert (totals <= bound).all()
+    np.testing.assert_array_equal(p["grp_off"][:, L], totals)
+    d_of = wl.idx // L
+    for d in range(N):
+        g = np.sort(p["grp_pos"][d_of == d])
+        np.testing.assert_array_equal(g, np.arange(totals[d]))
+    if name == "worst":
+        assert totals[0] == bound and (totals[1:] == 0).all()
+
+
+def test_plan_single_rank_grouped_equals_send():
+    rng = np.random.default_rng(7)
+    idx = random_idx(rng, 1, 33, 6, 3)
+    p = oracle.plan(1, 33, 6, 3, oracle.recv_bound(1, 33, 6, 3), idx)
+    np.testing.assert_array_equal(p["grp_pos"], p["send_pos"])
+    np.testing.assert_array_equal(p["recv_off"], [[0, 99]])
+
+
+def test_plan_topk1_is_counting_sort():
+    rng = np.random.default_rng(8)
+    N, T, E = 4, 50, 8
+    idx = rng.integers(0, E, size=(N, T, 1), dtype=np.int32)
+    p = oracle.plan(N, T, E, 1, oracle.recv_bound(N, T, E, 1), idx)
+    for s in range(N):
+        order = np.argsort(idx[s, :, 0], kind="stable")
+        np.testing.assert_array_equal(p["send_pos"][s, order, 0], np.arange(T))
+
+
+def test_plan_bad_expert_and_capacity():
+    idx = HAND_IDX.copy()
+    idx[0, 0, 1] = 4          # out of range
+    idx[1, 1, 0] = -1         # out of range
+    p = oracle.plan(2, 2, 4, 2, 8, idx)
+    assert p["status"] == oracle.STATUS_BAD_EXPERT
+    assert p["send_pos"][0, 0, 1] == -1 and p["grp_pos"][1, 1, 0] == -1
+    assert p["cnt"].sum() == 6
+    # capacity 4: destination 0 needs 5 rows now, row 4 is dropped
+    p = oracle.plan(2, 2, 4, 2, 4, idx)
+    assert p["status"] == oracle.STATUS_BAD_EXPERT | oracle.STATUS_CAPACITY
+    assert (p["grp_pos"] < 4).all()
+    assert (p["grp_pos"] == -1).sum() == 3
+    assert p["recv_off"][0, 2] == 5
+
+
+# ---------------------------------------------------------------------------
+# Payload and combine
+# ---------------------------------------------------------------------------
+
+def _src_of_grouped(p, idx, N, E):
+    L = E // N
+    src = {}
+    for s, t, k in np.ndindex(idx.shape):
+        g = p["grp_pos"][s, t, k]
+        if g >= 0:
+            src[(int(idx[s, t, k]) // L, int(g))] = (s, t)
+    return src
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_zipf"])
+def test_grouped_rows_are_source_rows(name):
+    sh = W.CONFIGS[name]
+    wl = W.make_workload(sh)
+    r = oracle.run(wl)
+    p = r["plan"]
+    src = _src_of_grouped(p, wl.idx, sh.n_ranks, sh.n_experts)
+    assert len(src) == sh.n_ranks * sh.tokens * sh.topk
+    for (d, g), (s, t) in src.items():
+        np.testing.assert_array_equal(r["grouped"][0][d, g], wl.planes[0][s, t])
+    for s in range(sh.n_ranks):   # send rows are x rows, per send_pos
+        for t, k in np.ndindex(sh.tokens, sh.topk):
+            np.testing.assert_array_equal(r["send"][0][s, p["send_pos"][s, t, k]],
+                                          wl.planes[0][s, t])
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_zipf"])
+def test_combine_identity_closed_form(name):
+    """Identity experts and weights summing to one give back x exactly."""
+    wl = W.make_workload(W.CONFIGS[name])
+    r = oracle.run(wl)
+    np.testing.assert_array_equal(r["out"], wl.x_bf16)
+
+
+def test_combine_identity_repeated_ids():
+    """All slots on rank 0 with repeated expert ids: still x exactly."""
+    sh = W.Shape("mini_worst", 8, 8, 64, 32, 8, routing="rank0")
+    wl = W.make_workload(sh)
+    r = oracle.run(wl)
+    assert r["plan"]["recv_off"][0, 8] == oracle.recv_bound(8, 8, 32, 8)
+    np.testing.assert_array_equal(r["out"], wl.x_bf16)
+
+
+def _np_expert_scale(x_bits, a):
+    """bf16(x * a) with a float32 multiply (numpy) and torch's bf16 cast."""
+    prod = W.bf16_bits_to_f32(x_bits) * np.float32(a)
+    return torch.from_numpy(prod.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_combine_exact_brute_force_scale_expert():
+    """Exact rational weighted sum, nearest bf16 by search, no layout."""
+    sh = W.Shape("small_scale", 4, 6, 16, 8, 3, expert="scale", seed=3)
+    wl = W.make_workload(sh)
+    r = oracle.run(wl)
+    for s, t in np.ndindex(sh.n_ranks, sh.tokens):
+        ys = [_np_expert_scale(wl.x_bf16[s, t], wl.alpha[e]) for e in wl.idx[s, t]]
+        for h in range(sh.hidden):
+            acc = sum(Fraction(float(wl.weights[s, t, k])) * bf16_value(int(ys[k][h]))
+                      for k in range(sh.topk))
+            assert r["out"][s, t, h] == brute_bf16_round(acc), (s, t, h)
+
+
+def test_combine_scale_expert_approx_closed_form():
+    """out ~= x * sum_k w_k alpha_k within two bf16 roundings."""
+    sh = W.Shape("mid_scale", 8, 32, 512, 64, 8, expert="scale", seed=5)
+    wl = W.make_workload(sh)
+    r = oracle.run(wl)
+    x = W.bf16_bits_to_f32(wl.x_bf16).astype(np.float64)
+    f = (wl.weights.astype(np.float64) * wl.alpha[wl.idx].astype(np.float64)).sum(-1)
+    want = x * f[..., None]
+    got = W.bf16_bits_to_f32(r["out"]).astype(np.float64)
+    nz = want != 0
+    rel = np.abs(got[nz] - want[nz]) / np.abs(want[nz])
+    assert rel.max() <= 2 * 2.0 ** -8
+
+
+def test_expert_dequant_matches_torch():
+    sh = W.Shape("small_fp8", 2, 4, 512, 8, 2, payload=W.PAYLOAD_FP8_B128,
+                 expert="dequant", seed=6)
+    wl = W.make_workload(sh)
+    codes, scales = wl.planes[0], wl.planes[1].view(np.float32)
+    for s, t in np.ndindex(2, 4):
+        got = oracle.expert_row([codes[s, t], wl.planes[1][s, t]], 0, 1, 512, None)
+        deq = torch.from_numpy(codes[s, t].copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+        prod = deq * np.repeat(scales[s, t], 128)
+        want = torch.from_numpy(prod.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, want)
+    # dequantised rows stay within the e4m3 half-ulp of the bf16 input
+    r = oracle.run(wl)
+    x = W.bf16_bits_to_f32(wl.x_bf16)
+    y = W.bf16_bits_to_f32(r["out"])
+    big = np.abs(x) > 0.05 * np.abs(x).max()
+    assert (np.abs(y - x)[big] <= (2.0 ** -4 + 2.0 ** -8) * np.abs(x)[big] + 1e-30).all()
+
+
+def test_combine_token_rounds_once():
+    """Exact sum 1 + 2^-8 + 2^-30 sits just above a bf16 tie: a single
+    rounding of the exact sum gives 1 + 2^-7; rounding a float partial sum
+    first would land on the tie and give 1."""
+    one = np.array([0x3F80], np.uint16)
+    w = np.array([1.0 + 2.0 ** -8, 2.0 ** -30], np.float32)
+    assert oracle.combine_token(w, [one, one])[0] == 0x3F81
+    w = np.array([1.0 + 2.0 ** -8, -(2.0 ** -30)], np.float32)
+    assert oracle.combine_token(w, [one, one])[0] == 0x3F80
+    w = np.array([0.25, 0.75], np.float32)               # dropped slot skipped
+    assert oracle.combine_token(w, [None, one])[0] == 0x3F40
+
+
+def test_combine_skips_dropped_slots():
+    sh = W.Shape("drop", 2, 2, 8, 4, 2)
+    idx = HAND_IDX.copy()
+    idx[0, 0, 1] = 9
+    wl = W.make_workload(sh, idx=idx)
+    r = oracle.run(wl, cap=8)
+    w = wl.weights[0, 0, 0]
+    x = W.bf16_bits_to_f32(wl.x_bf16[0, 0]).astype(np.float64)
+    want = np.array([brute_bf16_round(Fraction(float(w)) * Fraction(float(v))) for v in x])
+    np.testing.assert_array_equal(r["out"][0, 0], want)
