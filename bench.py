@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark: one MoE dispatch + combine step of the whole EP group on one GPU.
+
+A step is ep_plan -> ep_dispatch_pack -> ep_dispatch_recv -> ep_combine over
+the decode-scale workload (N=32 virtual ranks x T=128 tokens, H=7168 bf16,
+E=256 experts, top-8 uniform routing, softmax weights). The stand-in expert
+(per-expert scale) runs once before timing; its output is what combine reads
+in every timed step, so no expert work is inside the timed region.
+
+Prints one JSON line. `value` is the effective HBM throughput of the step:
+the algorithmic bytes of dispatch + combine divided by the step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per dispatch+combine and effective HBM GB/s (% of peak) on 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(sh, row_d: int) -> dict:
+    """Bytes the method must move, per stage and per step.
+
+    x read once, the send buffer written and read (the transfer is pulled by
+    the receiver), the grouped layout written, the expert output read, the
+    combined tokens written, plus the routing ids and weights.
+    """
+    N, T, R, H = sh.n_ranks, sh.tokens, sh.topk, sh.hidden
+    NT, NTR, row_c = N * T, N * T * R, 2 * H
+    stages = {
+        "plan": 4 * NTR,                                  # routing ids
+        "pack": NT * row_d + NTR * row_d,                 # read x, write send
+        "recv": 2 * NTR * row_d,                          # read send, write grouped
+        "combine": NTR * row_c + NT * row_c + 4 * NTR,    # read y and weights, write out
+    }
+    return {"stages": stages, "step": sum(stages.values())}
+
+
+def cpu_baseline(sh, wl, budget_s: float) -> dict:
+    """The oracle as it stands, single thread, on the same workload."""
+    import numpy as np
+    import oracle
+
+    N, T, E, R, H = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk, sh.hidden
+    cap = oracle.recv_bound(N, T, E, R)
+    times = []
+    t_begin = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        p = oracle.plan(N, T, E, R, cap, wl.idx)
+        totals = p["recv_off"][:, N]
+        rows = int(min(cap, int(totals.max())))
+        send = [oracle.dispatch_pack(pl, p) for pl in wl.planes]
+        recv = [oracle.transfer(s, p, rows) for s in send]
+        grouped = [oracle.unpack(r, p, rows) for r in recv]
+        t1 = time.perf_counter()
+        y = oracle.expert_op(grouped, p, H, sh.payload, wl.alpha)   # stand-in, not timed
+        t2 = time.perf_counter()
+        out = oracle.combine(y, wl.weights, wl.idx, p)
+        t3 = time.perf_counter()
+        times.append((t1 - t0) + (t3 - t2))
+        del send, recv, grouped, y, out
+        if time.perf_counter() - t_begin >= budget_s or len(times) >= 5:
+            break
+    return {"seconds": times, "median_s": statistics.median(times), "runs": len(times)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle CPU work for the baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the EP group's ranks are virtual ranks on one "
+              f"MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_ep_plan_amd as ep
+    import ep_workloads as W
+
+    torch.cuda.set_device(0)
+    sh = W.CONFIGS[args.config]
+    wl = W.make_workload(sh)
+    d = ep.make_desc(sh.n_ranks, sh.tokens, sh.hidden, sh.n_experts, sh.topk, sh.payload)
+    b = ep.Buffers(d, device="cuda:0")
+    b.idx.copy_(torch.from_numpy(wl.idx))
+    b.weights.copy_(torch.from_numpy(wl.weights))
+    for q, plane in enumerate(wl.planes):
+        b.x[q].copy_(torch.from_numpy(plane))
+    alpha = torch.from_numpy(wl.alpha).cuda() if wl.alpha is not None else None
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    row_d = sum(ep.row_bytes(d, q) for q in range(ep.num_planes(d)))
+
+    # expert outputs once (outside timing)
+    ep.plan(d, b.idx, b.plan_ws, b.status, sp)
+    ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)
+    ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp)
+    ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out, sp)
+    torch.cuda.synchronize()
+    if int(b.status.item()) != 0:
+        print(f"plan status {b.status.item()}", file=sys.stderr)
+        return 1
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ep.plan(d, b.idx, b.plan_ws, b.status, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp)
+        if ev is not None:
+            ev[3].record(stream)
+        ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, sp)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    stage_names = ["plan", "pack", "recv", "combine"]
+    per = {n: [] for n in stage_names}
+    steps_ms = []
+    for ev in events:
+        for j, n in enumerate(stage_names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]))
+        steps_ms.append(ev[0].elapsed_time(ev[4]))
+    total_ms = events[0][0].elapsed_time(events[-1][4])
+    ms_per_step = total_ms / args.steps
+    ab = algorithmic_bytes(sh, row_d)
+    eff = ab["step"] / (ms_per_step * 1e-3) / 1e9
+
+    # the dominant kernel: the receiver (largest algorithmic bytes)
+    dom = max(ab["stages"], key=lambda k: ab["stages"][k])
+    dom_ms = statistics.mean(per[dom])
+    achieved = ab["stages"][dom] / (dom_ms * 1e-3) / 1e9
+
+    # copy ceiling of this GPU with the library's own row-copy loop (context)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        ep.probe_copy(dst, src, nbytes, sp)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        ep.probe_copy(dst, src, nbytes, sp)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    cpu = None
+    if args.cpu_budget > 0:
+        base = cpu_baseline(sh, wl, args.cpu_budget)
+        cpu = {
+            "value": ab["step"] / base["median_s"] / 1e9,
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": (f"the whole {sh.name} workload, {base['runs']} run(s) of the plain-C "
+                       f"oracle (plan, pack, per-pair transfer, unpack, combine; stand-in "
+                       f"expert not timed), median {base['median_s']:.3f} s"),
+            "us_per_step": base["median_s"] * 1e6,
+        }
+
+    res = {
+        "metric": METRIC,
+        "value": round(eff, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{sh.name}: N={sh.n_ranks} virtual ranks, T={sh.tokens} tokens/rank, "
+                         f"H={sh.hidden} bf16, E={sh.n_experts} experts, top-{sh.topk} "
+                         f"{sh.routing} routing, softmax weights, expert = per-expert scale"),
+            "parallelism": "ep (virtual ranks on one GPU)",
+            "global_batch": sh.n_ranks * sh.tokens,
+        },
+        "us_per_dispatch_combine": round(ms_per_step * 1e3, 2),
+        "frac_of_hbm_peak": round(eff / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": ab["step"],
+        "stages_us": {n: round(statistics.mean(per[n]) * 1e3, 2) for n in stage_names},
+        "step_us_p10_p50_p90": [round(float(np.percentile(steps_ms, q)) * 1e3, 2)
+                                for q in (10, 50, 90)],
+        "wall_ms": round(wall_ms, 3),
+        "roofline": {
+            "kernel": f"ep_dispatch_{dom}" if dom in ("pack", "recv") else f"ep_{dom}",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes": ab["stages"][dom],
+            "avg_us": round(dom_ms * 1e3, 2),
+        },
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

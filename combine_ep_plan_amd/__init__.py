@@ -1,0 +1,242 @@
+"""Python binding of the gfx950 MoE expert-parallel dispatch/combine library.
+
+Thin ctypes layer over the C ABI in ``include/ep.h``: the functions below
+have the same names as the C entry points and only marshal arguments
+(tensor data pointers, the current HIP stream). Every step of the path runs
+in the library's HIP kernels; there is no fallback. If the compiled library
+is missing, importing this package raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libep_mi355x.so")
+
+EP_OK = 0
+EP_ERR_INVALID_ARG = -1
+EP_ERR_UNSUPPORTED = -2
+EP_ERR_DEVICE_MISMATCH = -3
+EP_ERR_HIP = -4
+EP_STATUS_BAD_EXPERT = 1
+EP_STATUS_CAPACITY = 2
+EP_PAYLOAD_BF16 = 0
+EP_PAYLOAD_FP8_B128 = 1
+
+# Every entry point the C header declares (checked by the tests).
+EXPORTS = (
+    "ep_recv_bound", "ep_capacity", "ep_num_planes", "ep_row_bytes",
+    "ep_plan_bytes", "ep_plan_views", "ep_plan", "ep_dispatch_pack",
+    "ep_dispatch_transfer", "ep_dispatch_unpack", "ep_dispatch_recv",
+    "ep_expert_stub", "ep_combine", "ep_probe_copy", "ep_status_string",
+    "ep_last_error",
+)
+
+
+class EPError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where} failed ({code}): {msg}")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    """ep_desc: N, T, H, E, R, payload, cap_rows (0 = worst-case bound)."""
+    _fields_ = [
+        ("n_ranks", ctypes.c_int32), ("tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+        ("topk", ctypes.c_int32), ("payload", ctypes.c_int32),
+        ("cap_rows", ctypes.c_int64),
+    ]
+
+
+class PlanView(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos",
+        "src_off", "comb_row")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, D = ctypes.c_void_p, ctypes.POINTER(Desc)
+    sig = {
+        "ep_recv_bound": (ctypes.c_int64, [D]),
+        "ep_capacity": (ctypes.c_int64, [D]),
+        "ep_num_planes": (ctypes.c_int, [D]),
+        "ep_row_bytes": (ctypes.c_int64, [D, ctypes.c_int]),
+        "ep_plan_bytes": (ctypes.c_size_t, [D]),
+        "ep_plan_views": (ctypes.c_int, [D, P, ctypes.POINTER(PlanView)]),
+        "ep_plan": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_dispatch_pack": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_dispatch_transfer": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_dispatch_unpack": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_dispatch_recv": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_expert_stub": (ctypes.c_int, [D, P, P, P, P, P]),
+        "ep_combine": (ctypes.c_int, [D, P, P, P, P, P]),
+        "ep_probe_copy": (ctypes.c_int, [P, P, ctypes.c_size_t, P]),
+        "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "ep_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# Marshalling helpers
+# ---------------------------------------------------------------------------
+
+def make_desc(n_ranks, tokens, hidden, n_experts, topk,
+              payload=EP_PAYLOAD_BF16, cap_rows=0) -> Desc:
+    return Desc(n_ranks, tokens, hidden, n_experts, topk, payload, cap_rows)
+
+
+def _addr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _planes(ts: Sequence) -> ctypes.Array:
+    ts = list(ts) + [None] * (2 - len(ts))
+    return (ctypes.c_void_p * 2)(*[_addr(t) for t in ts[:2]])
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str) -> int:
+    if rc != EP_OK:
+        raise EPError(rc, where, _lib.ep_last_error().decode())
+    return rc
+
+
+def status_string(code: int) -> str:
+    return _lib.ep_status_string(code).decode()
+
+
+def last_error() -> str:
+    return _lib.ep_last_error().decode()
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def recv_bound(d: Desc) -> int:
+    return int(_lib.ep_recv_bound(ctypes.byref(d)))
+
+
+def capacity(d: Desc) -> int:
+    return int(_lib.ep_capacity(ctypes.byref(d)))
+
+
+def num_planes(d: Desc) -> int:
+    return int(_lib.ep_num_planes(ctypes.byref(d)))
+
+
+def row_bytes(d: Desc, plane: int) -> int:
+    return int(_lib.ep_row_bytes(ctypes.byref(d), plane))
+
+
+def plan_bytes(d: Desc) -> int:
+    return int(_lib.ep_plan_bytes(ctypes.byref(d)))
+
+
+def plan_views(d: Desc, plan_ws) -> PlanView:
+    v = PlanView()
+    _check(_lib.ep_plan_views(ctypes.byref(d), _addr(plan_ws), ctypes.byref(v)), "ep_plan_views")
+    return v
+
+
+def plan(d: Desc, topk_idx, plan_ws, status, stream=None) -> None:
+    _check(_lib.ep_plan(ctypes.byref(d), _addr(topk_idx), _addr(plan_ws), _addr(status),
+                        _stream(stream)), "ep_plan")
+
+
+def dispatch_pack(d: Desc, x: Sequence, plan_ws, send: Sequence, stream=None) -> None:
+    _check(_lib.ep_dispatch_pack(ctypes.byref(d), _planes(x), _addr(plan_ws), _planes(send),
+                                 _stream(stream)), "ep_dispatch_pack")
+
+
+def dispatch_transfer(d: Desc, send: Sequence, plan_ws, recv: Sequence, stream=None) -> None:
+    _check(_lib.ep_dispatch_transfer(ctypes.byref(d), _planes(send), _addr(plan_ws),
+                                     _planes(recv), _stream(stream)), "ep_dispatch_transfer")
+
+
+def dispatch_unpack(d: Desc, recv: Sequence, plan_ws, grouped: Sequence, stream=None) -> None:
+    _check(_lib.ep_dispatch_unpack(ctypes.byref(d), _planes(recv), _addr(plan_ws),
+                                   _planes(grouped), _stream(stream)), "ep_dispatch_unpack")
+
+
+def dispatch_recv(d: Desc, send: Sequence, plan_ws, grouped: Sequence, stream=None) -> None:
+    _check(_lib.ep_dispatch_recv(ctypes.byref(d), _planes(send), _addr(plan_ws),
+                                 _planes(grouped), _stream(stream)), "ep_dispatch_recv")
+
+
+def expert_stub(d: Desc, grouped: Sequence, alpha, plan_ws, expert_out, stream=None) -> None:
+    _check(_lib.ep_expert_stub(ctypes.byref(d), _planes(grouped), _addr(alpha), _addr(plan_ws),
+                               _addr(expert_out), _stream(stream)), "ep_expert_stub")
+
+
+def combine(d: Desc, expert_out, weights, plan_ws, out, stream=None) -> None:
+    _check(_lib.ep_combine(ctypes.byref(d), _addr(expert_out), _addr(weights), _addr(plan_ws),
+                           _addr(out), _stream(stream)), "ep_combine")
+
+
+def probe_copy(dst, src, nbytes: int, stream=None) -> None:
+    _check(_lib.ep_probe_copy(_addr(dst), _addr(src), nbytes, _stream(stream)), "ep_probe_copy")
+
+
+# ---------------------------------------------------------------------------
+# Device buffers for one descriptor (torch allocations; plumbing only)
+# ---------------------------------------------------------------------------
+
+class Buffers:
+    """Caller-owned device buffers of one dispatch/combine step."""
+
+    def __init__(self, d: Desc, device="cuda", staged: bool = False):
+        import torch
+        self.desc = d
+        N, T, H, R = d.n_ranks, d.tokens, d.hidden, d.topk
+        cap = capacity(d)
+        if cap < 0:
+            raise EPError(EP_ERR_INVALID_ARG, "Buffers", last_error())
+        self.cap = cap
+        self.planes = num_planes(d)
+        rows = [row_bytes(d, p) for p in range(self.planes)]
+        u8 = torch.uint8
+        self.idx = torch.empty((N, T, R), dtype=torch.int32, device=device)
+        self.weights = torch.empty((N, T, R), dtype=torch.float32, device=device)
+        self.x = [torch.empty((N, T, r), dtype=u8, device=device) for r in rows]
+        self.send = [torch.empty((N, T * R, r), dtype=u8, device=device) for r in rows]
+        self.grouped = [torch.empty((N, cap, r), dtype=u8, device=device) for r in rows]
+        self.recv = ([torch.empty((N, cap, r), dtype=u8, device=device) for r in rows]
+                     if staged else None)
+        self.expert_out = torch.empty((N, cap, H), dtype=torch.int16, device=device)
+        self.out = torch.empty((N, T, H), dtype=torch.int16, device=device)
+        self.plan_ws = torch.empty(plan_bytes(d), dtype=u8, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)

@@ -1,0 +1,43 @@
+"""Compile the gfx950 HIP library in-tree (hipcc, no JIT cache)."""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libep_mi355x.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-fvisibility=hidden",
+    "-Wall", "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE,
+]
+
+
+def sources() -> list:
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(
+        glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles; writes the library next to this file."""
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC] + FLAGS + sources() + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,364 @@
+// C ABI of the dispatch/combine library: descriptor checks, plan workspace
+// layout, device selection from the stream, and kernel launches.
+//
+// The device of every call is the stream's device, made current for the
+// duration of the call and restored afterwards; the calling thread's current
+// device is never assumed (a transfer thread that never selected its GPU
+// silently used the wrong one in the KV-transfer study "NIXL LIBFABRIC
+// backend, same-node transfer", section on the wrong-current-device bug).
+#include "../../include/ep.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "ep_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return EP_ERR_HIP;
+}
+
+constexpr int64_t kMaxWaves = (int64_t)1 << 26;  // grid.x * 64 threads < 2^32
+
+int64_t bound_of(const ep_desc* d) {
+  const int64_t L = d->n_experts / d->n_ranks;
+  const int64_t m = d->topk > L ? d->topk : L;
+  return (int64_t)d->n_ranks * d->tokens * m;
+}
+
+// Validate a descriptor and derive sizes. Returns EP_OK or a negative code.
+int derive(const ep_desc* d, ep::Dims* o) {
+  if (!d) return fail(EP_ERR_INVALID_ARG, "null descriptor");
+  if (d->n_ranks <= 0 || d->tokens < 0 || d->hidden <= 0 || d->n_experts <= 0 || d->topk <= 0)
+    return fail(EP_ERR_INVALID_ARG, "sizes must be positive (tokens may be 0)");
+  if (d->n_experts % d->n_ranks != 0)
+    return fail(EP_ERR_INVALID_ARG, "n_experts must be a multiple of n_ranks");
+  if (d->payload != EP_PAYLOAD_BF16 && d->payload != EP_PAYLOAD_FP8_B128)
+    return fail(EP_ERR_INVALID_ARG, "unknown payload");
+  if (d->payload == EP_PAYLOAD_BF16 && d->hidden % 8 != 0)
+    return fail(EP_ERR_INVALID_ARG, "bf16 payload needs hidden % 8 == 0");
+  if (d->payload == EP_PAYLOAD_FP8_B128 && d->hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "fp8 payload needs hidden % 128 == 0");
+  if (d->cap_rows < 0) return fail(EP_ERR_INVALID_ARG, "cap_rows must be >= 0");
+  if (d->n_experts > EP_MAX_EXPERTS) return fail(EP_ERR_UNSUPPORTED, "too many experts");
+  if (d->topk > EP_MAX_TOPK) return fail(EP_ERR_UNSUPPORTED, "topk too large");
+  const int64_t cap = d->cap_rows > 0 ? d->cap_rows : bound_of(d);
+  const int64_t NTR = (int64_t)d->n_ranks * d->tokens * d->topk;
+  // A zero capacity only arises from the bound with no tokens at all.
+  if ((int64_t)d->n_ranks * cap >= ((int64_t)1 << 31))
+    return fail(EP_ERR_UNSUPPORTED, "n_ranks * cap_rows must be < 2^31");
+  if (NTR >= kMaxWaves) return fail(EP_ERR_UNSUPPORTED, "n_ranks * tokens * topk must be < 2^26");
+  o->N = d->n_ranks;
+  o->T = d->tokens;
+  o->H = d->hidden;
+  o->E = d->n_experts;
+  o->R = d->topk;
+  o->L = d->n_experts / d->n_ranks;
+  o->payload = d->payload;
+  o->planes = d->payload == EP_PAYLOAD_BF16 ? 1 : 2;
+  o->cap = cap;
+  o->TR = (int64_t)d->tokens * d->topk;
+  o->NT = (int64_t)d->n_ranks * d->tokens;
+  o->NTR = NTR;
+  if (d->payload == EP_PAYLOAD_BF16) {
+    o->row[0] = 2 * (int64_t)d->hidden;
+    o->row[1] = 0;
+  } else {
+    o->row[0] = d->hidden;
+    o->row[1] = 4 * (int64_t)(d->hidden / 128);
+  }
+  const int64_t nch = (o->TR + ep::kPlanChunk - 1) / ep::kPlanChunk;
+  o->nchunks = (int)(nch > 0 ? nch : 1);
+  return EP_OK;
+}
+
+// Plan workspace: int32 arrays, each starting on a 256-byte boundary.
+struct Layout {
+  size_t off[9];
+  size_t bytes;
+};
+
+Layout layout_of(const ep::Dims& d) {
+  const size_t n[9] = {
+      (size_t)d.N * d.E,                       // cnt
+      (size_t)d.N * (d.E + 1),                 // send_off
+      (size_t)d.NTR,                           // send_pos
+      (size_t)d.N * (d.N + 1),                 // recv_off
+      (size_t)d.N * (d.L + 1),                 // grp_off
+      (size_t)d.NTR,                           // grp_pos
+      (size_t)d.N * d.E,                       // src_off
+      (size_t)d.NTR,                           // comb_row
+      (size_t)d.N * d.nchunks * d.E,           // chunk_cnt
+  };
+  Layout l{};
+  size_t at = 0;
+  for (int i = 0; i < 9; ++i) {
+    l.off[i] = at;
+    at += (n[i] * sizeof(int32_t) + 255) & ~(size_t)255;
+  }
+  l.bytes = at > 0 ? at : 256;
+  return l;
+}
+
+ep::PlanPtrs plan_ptrs(const ep::Dims& d, const void* ws) {
+  const Layout l = layout_of(d);
+  char* b = (char*)ws;
+  ep::PlanPtrs p;
+  p.cnt = (int32_t*)(b + l.off[0]);
+  p.send_off = (int32_t*)(b + l.off[1]);
+  p.send_pos = (int32_t*)(b + l.off[2]);
+  p.recv_off = (int32_t*)(b + l.off[3]);
+  p.grp_off = (int32_t*)(b + l.off[4]);
+  p.grp_pos = (int32_t*)(b + l.off[5]);
+  p.src_off = (int32_t*)(b + l.off[6]);
+  p.comb_row = (int32_t*)(b + l.off[7]);
+  p.chunk_cnt = (int32_t*)(b + l.off[8]);
+  return p;
+}
+
+// Makes the stream's device current for the lifetime of the object.
+class DeviceScope {
+ public:
+  explicit DeviceScope(hipStream_t s) {
+    err_ = hipGetDevice(&prev_);
+    if (err_ != hipSuccess) return;
+    err_ = hipStreamGetDevice(s, &dev_);
+    if (err_ != hipSuccess) return;
+    if (dev_ != prev_) err_ = hipSetDevice(dev_);
+  }
+  ~DeviceScope() {
+    if (err_ == hipSuccess && dev_ != prev_) (void)hipSetDevice(prev_);
+  }
+  hipError_t error() const { return err_; }
+  int device() const { return dev_; }
+
+ private:
+  int prev_ = -1;
+  int dev_ = -1;
+  hipError_t err_ = hipSuccess;
+};
+
+// A non-empty buffer must be device (or managed) memory of the stream's GPU;
+// an empty one (bytes == 0) is never touched and may be anything.
+int check_ptr(const void* p, int dev, const char* name, int64_t bytes = 1) {
+  if (bytes == 0) return EP_OK;
+  if (!p) return fail(EP_ERR_INVALID_ARG, (std::string("null pointer: ") + name).c_str());
+  hipPointerAttribute_t a;
+  std::memset(&a, 0, sizeof a);
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(EP_ERR_INVALID_ARG, (std::string("not device memory: ") + name).c_str());
+  }
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged)
+    return fail(EP_ERR_INVALID_ARG, (std::string("not device memory: ") + name).c_str());
+  if (a.type == hipMemoryTypeDevice && a.device != dev)
+    return fail(EP_ERR_DEVICE_MISMATCH,
+                (std::string("buffer on another device: ") + name).c_str());
+  return EP_OK;
+}
+
+// rows: rows of every plane buffer (its bytes are rows * row bytes).
+int check_planes(const ep::Dims& d, const void* const* pl, int dev, const char* name,
+                 int64_t rows) {
+  if (!pl) return fail(EP_ERR_INVALID_ARG, (std::string("null plane array: ") + name).c_str());
+  for (int q = 0; q < d.planes; ++q) {
+    const int rc = check_ptr(pl[q], dev, name, rows * d.row[q]);
+    if (rc != EP_OK) return rc;
+  }
+  if (d.planes == 1 && pl[1] != nullptr)
+    return fail(EP_ERR_INVALID_ARG, (std::string("plane 1 must be NULL for bf16: ") + name).c_str());
+  return EP_OK;
+}
+
+// Common prologue: descriptor, device scope, workspace pointer.
+#define EP_PROLOGUE(desc, stream, ws)                                    \
+  ep::Dims dims;                                                         \
+  {                                                                      \
+    const int rc_ = derive(desc, &dims);                                 \
+    if (rc_ != EP_OK) return rc_;                                        \
+  }                                                                      \
+  DeviceScope scope(stream);                                             \
+  if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device"); \
+  {                                                                      \
+    const int rc_ = check_ptr(ws, scope.device(), "plan_ws");            \
+    if (rc_ != EP_OK) return rc_;                                        \
+  }                                                                      \
+  const ep::PlanPtrs pp = plan_ptrs(dims, ws);
+
+#define EP_CHECK(expr)            \
+  do {                            \
+    const int rc_ = (expr);       \
+    if (rc_ != EP_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int64_t ep_recv_bound(const ep_desc* d) {
+  ep::Dims dims;
+  if (derive(d, &dims) != EP_OK) return -1;
+  return bound_of(d);
+}
+
+int64_t ep_capacity(const ep_desc* d) {
+  ep::Dims dims;
+  if (derive(d, &dims) != EP_OK) return -1;
+  return dims.cap;
+}
+
+int ep_num_planes(const ep_desc* d) {
+  ep::Dims dims;
+  if (derive(d, &dims) != EP_OK) return -1;
+  return dims.planes;
+}
+
+int64_t ep_row_bytes(const ep_desc* d, int plane) {
+  ep::Dims dims;
+  if (derive(d, &dims) != EP_OK) return -1;
+  if (plane < 0 || plane > 1) return 0;
+  return dims.row[plane];
+}
+
+size_t ep_plan_bytes(const ep_desc* d) {
+  ep::Dims dims;
+  if (derive(d, &dims) != EP_OK) return 0;
+  return layout_of(dims).bytes;
+}
+
+int ep_plan_views(const ep_desc* d, void* plan_ws, ep_plan_view* v) {
+  ep::Dims dims;
+  EP_CHECK(derive(d, &dims));
+  if (!plan_ws || !v) return fail(EP_ERR_INVALID_ARG, "null workspace or view");
+  const ep::PlanPtrs p = plan_ptrs(dims, plan_ws);
+  v->cnt = p.cnt;
+  v->send_off = p.send_off;
+  v->send_pos = p.send_pos;
+  v->recv_off = p.recv_off;
+  v->grp_off = p.grp_off;
+  v->grp_pos = p.grp_pos;
+  v->src_off = p.src_off;
+  v->comb_row = p.comb_row;
+  return EP_OK;
+}
+
+int ep_plan(const ep_desc* d, const int32_t* topk_idx, void* plan_ws, int32_t* status,
+            hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_ptr(status, scope.device(), "status"));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  const hipError_t e = ep::launch_plan(dims, topk_idx, pp, status, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_plan");
+  return EP_OK;
+}
+
+int ep_dispatch_pack(const ep_desc* d, const void* const x[2], const void* plan_ws,
+                     void* const send[2], hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_planes(dims, (const void* const*)x, scope.device(), "x", dims.NT));
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  const hipError_t e = ep::launch_pack(dims, x, pp, send, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_pack");
+  return EP_OK;
+}
+
+int ep_dispatch_transfer(const ep_desc* d, const void* const send[2], const void* plan_ws,
+                         void* const recv[2], hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  EP_CHECK(check_planes(dims, (const void* const*)recv, scope.device(), "recv", dims.N * dims.cap));
+  const hipError_t e = ep::launch_transfer(dims, send, pp, recv, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_transfer");
+  return EP_OK;
+}
+
+int ep_dispatch_unpack(const ep_desc* d, const void* const recv[2], const void* plan_ws,
+                       void* const grouped[2], hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_planes(dims, (const void* const*)recv, scope.device(), "recv", dims.N * dims.cap));
+  EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
+  const hipError_t e = ep::launch_unpack(dims, recv, pp, grouped, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_unpack");
+  return EP_OK;
+}
+
+int ep_dispatch_recv(const ep_desc* d, const void* const send[2], const void* plan_ws,
+                     void* const grouped[2], hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
+  const hipError_t e = ep::launch_recv(dims, send, pp, grouped, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_recv");
+  return EP_OK;
+}
+
+int ep_expert_stub(const ep_desc* d, const void* const grouped[2], const float* alpha,
+                   const void* plan_ws, uint16_t* expert_out, hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
+  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap));
+  if (alpha) {
+    if (dims.payload != EP_PAYLOAD_BF16)
+      return fail(EP_ERR_INVALID_ARG, "alpha applies to the bf16 payload only");
+    EP_CHECK(check_ptr(alpha, scope.device(), "alpha"));
+  }
+  const hipError_t e = ep::launch_expert_stub(dims, grouped, alpha, pp, expert_out, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_expert_stub");
+  return EP_OK;
+}
+
+int ep_combine(const ep_desc* d, const uint16_t* expert_out, const float* weights,
+               const void* plan_ws, uint16_t* out, hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap));
+  EP_CHECK(check_ptr(out, scope.device(), "out", dims.NT));
+  EP_CHECK(check_ptr(weights, scope.device(), "weights", dims.NTR));
+  const hipError_t e = ep::launch_combine(dims, expert_out, weights, pp, out, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_combine");
+  return EP_OK;
+}
+
+int ep_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes % 16 != 0) return fail(EP_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if (bytes / 16 >= (size_t)kMaxWaves * 64 * 14)
+    return fail(EP_ERR_UNSUPPORTED, "copy too large");
+  DeviceScope scope(stream);
+  if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");
+  EP_CHECK(check_ptr(dst, scope.device(), "dst"));
+  EP_CHECK(check_ptr(src, scope.device(), "src"));
+  const hipError_t e = ep::launch_probe_copy(dst, src, bytes, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_probe_copy");
+  return EP_OK;
+}
+
+const char* ep_status_string(int code) {
+  switch (code) {
+    case EP_OK: return "ok";
+    case EP_ERR_INVALID_ARG: return "invalid argument";
+    case EP_ERR_UNSUPPORTED: return "unsupported size";
+    case EP_ERR_DEVICE_MISMATCH: return "buffer on another device";
+    case EP_ERR_HIP: return "HIP runtime error";
+    case EP_STATUS_BAD_EXPERT: return "expert id out of range (slot dropped)";
+    case EP_STATUS_CAPACITY: return "receive capacity exceeded (rows dropped)";
+    case EP_STATUS_BAD_EXPERT | EP_STATUS_CAPACITY:
+      return "expert id out of range and receive capacity exceeded";
+    default: return "unknown code";
+  }
+}
+
+const char* ep_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

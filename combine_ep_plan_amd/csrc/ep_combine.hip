@@ -1,0 +1,173 @@
+// Combine receiver and the stand-in expert.
+//
+// Method: "Enabling trillion-parameter models on AWS EFA", section
+// "Dispatch and combine": with the routing known from dispatch, combine
+// returns each token's expert outputs to its source rank and accumulates
+// their routing-weighted average into the output tensor; accumulation
+// happens on the receiving (source) side only.
+//
+// One wave per output token. For each column block the wave loads the
+// token's R expert rows (two at a time, so two rows are in flight) and
+// accumulates w_k * y_k in fp32 with fused multiply-adds in k order, then
+// rounds once to bf16 (nearest, ties to even) and stores 16 bytes per lane.
+#include "ep_device.hpp"
+#include "ep_kernels.hpp"
+
+namespace ep {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWavesPerBlock * kWave;
+constexpr int kCombV = 7;   // 16-byte chunks (8 bf16) per lane per pass
+
+__device__ __forceinline__ int wave_index() {
+  return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+}
+
+template <int V>
+__device__ __forceinline__ void fma_row(float (&acc)[V][8], const RowRegs<V>& r, float w) {
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t q[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      acc[i][2 * h] = __builtin_fmaf(w, bf16_lo(q[h]), acc[i][2 * h]);
+      acc[i][2 * h + 1] = __builtin_fmaf(w, bf16_hi(q[h]), acc[i][2 * h + 1]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void combine_kernel(const uint16_t* __restrict__ y,
+                                                         const float* __restrict__ w,
+                                                         const int32_t* __restrict__ comb_row,
+                                                         uint16_t* __restrict__ out, int64_t NT,
+                                                         int R, int H, int64_t rows_in) {
+  const int tok = wave_index();
+  if (tok >= NT) return;
+  const int32_t* rows = comb_row + (size_t)tok * R;
+  const float* wt = w + (size_t)tok * R;
+  const int n16 = H / 8;
+  const uint4* ybase = (const uint4*)y;
+  uint4* o = (uint4*)(out + (size_t)tok * H);
+  for (int base = 0; base < n16; base += kWave * kCombV) {
+    float acc[kCombV][8];
+#pragma unroll
+    for (int i = 0; i < kCombV; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    int k = 0;
+    for (; k + 1 < R; k += 2) {
+      // rows outside [0, rows_in) (dropped slots) contribute nothing
+      const int r0 = rows[k] < rows_in ? rows[k] : -1;
+      const int r1 = rows[k + 1] < rows_in ? rows[k + 1] : -1;
+      RowRegs<kCombV> v0, v1;
+      if (r0 >= 0) load_row16(v0, ybase + (size_t)r0 * n16, base, n16);
+      if (r1 >= 0) load_row16(v1, ybase + (size_t)r1 * n16, base, n16);
+      if (r0 >= 0) fma_row(acc, v0, wt[k]);
+      if (r1 >= 0) fma_row(acc, v1, wt[k + 1]);
+    }
+    if (k < R) {
+      const int r0 = rows[k] < rows_in ? rows[k] : -1;
+      if (r0 >= 0) {
+        RowRegs<kCombV> v0;
+        load_row16(v0, ybase + (size_t)r0 * n16, base, n16);
+        fma_row(acc, v0, wt[k]);
+      }
+    }
+    RowRegs<kCombV> res;
+#pragma unroll
+    for (int i = 0; i < kCombV; ++i) {
+      res.v[i].x = f32_to_bf16_bits(acc[i][0]) | (f32_to_bf16_bits(acc[i][1]) << 16);
+      res.v[i].y = f32_to_bf16_bits(acc[i][2]) | (f32_to_bf16_bits(acc[i][3]) << 16);
+      res.v[i].z = f32_to_bf16_bits(acc[i][4]) | (f32_to_bf16_bits(acc[i][5]) << 16);
+      res.v[i].w = f32_to_bf16_bits(acc[i][6]) | (f32_to_bf16_bits(acc[i][7]) << 16);
+    }
+    store_row16(res, o, base, n16);
+  }
+}
+
+// Stand-in expert: one wave per delivered grouped row r of rank d; its local
+// expert j is the one with grp_off[d][j] <= r < grp_off[d][j+1].
+__global__ __launch_bounds__(kBlock) void expert_stub_kernel(
+    const uint8_t* __restrict__ g0, const uint8_t* __restrict__ g1,
+    const float* __restrict__ alpha, const int32_t* __restrict__ grp_off,
+    uint16_t* __restrict__ y, int L, int H, int64_t cap, int payload) {
+  const int d = blockIdx.y;
+  const int r = wave_index();
+  const int32_t* go = grp_off + (size_t)d * (L + 1);
+  const int64_t lim = go[L] < cap ? go[L] : cap;
+  if (r >= lim) return;
+  int lo = 0, hi = L - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (go[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int e = d * L + lo;
+  const size_t grow = (size_t)d * cap + r;
+  uint16_t* yr = y + grow * H;
+  const int lane = lane_id();
+  if (payload == 0) {
+    const uint4* in = (const uint4*)(g0 + grow * (size_t)H * 2);
+    const float a = alpha ? alpha[e] : 1.0f;
+    for (int c = lane; c < H / 8; c += kWave) {
+      uint4 v = in[c];
+      if (alpha) {
+        uint32_t* q = (uint32_t*)&v;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t lo16 = f32_to_bf16_bits(bf16_lo(q[h]) * a);
+          const uint32_t hi16 = f32_to_bf16_bits(bf16_hi(q[h]) * a);
+          q[h] = lo16 | (hi16 << 16);
+        }
+      }
+      ((uint4*)yr)[c] = v;
+    }
+  } else {
+    const uint4* codes = (const uint4*)(g0 + grow * (size_t)H);
+    const float* scales = (const float*)(g1 + grow * (size_t)(H / 32));
+    for (int c = lane; c < H / 16; c += kWave) {
+      const uint4 v = codes[c];
+      const float sc = scales[(c * 16) / 128];
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t b0 = f32_to_bf16_bits(e4m3_to_f32(q[h] & 0xff) * sc);
+        const uint32_t b1 = f32_to_bf16_bits(e4m3_to_f32((q[h] >> 8) & 0xff) * sc);
+        const uint32_t b2 = f32_to_bf16_bits(e4m3_to_f32((q[h] >> 16) & 0xff) * sc);
+        const uint32_t b3 = f32_to_bf16_bits(e4m3_to_f32(q[h] >> 24) * sc);
+        o[2 * h] = b0 | (b1 << 16);
+        o[2 * h + 1] = b2 | (b3 << 16);
+      }
+      ((uint4*)yr)[2 * c] = make_uint4(o[0], o[1], o[2], o[3]);
+      ((uint4*)yr)[2 * c + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+unsigned blocks_for(int64_t waves) {
+  return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* w, const PlanPtrs& p,
+                          uint16_t* out, hipStream_t stream) {
+  if (d.NT == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(d.NT)), dim3(kBlock), 0, stream, y, w,
+                     p.comb_row, out, d.NT, d.R, d.H, (int64_t)d.N * d.cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_stub(const Dims& d, const void* const grouped[2], const float* alpha,
+                              const PlanPtrs& p, uint16_t* y, hipStream_t stream) {
+  const int64_t rows = d.cap < d.NTR ? d.cap : d.NTR;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(expert_stub_kernel, dim3(blocks_for(rows), d.N), dim3(kBlock), 0, stream,
+                     (const uint8_t*)grouped[0],
+                     d.planes > 1 ? (const uint8_t*)grouped[1] : nullptr, alpha, p.grp_off, y,
+                     d.L, d.H, d.cap, d.payload);
+  return hipGetLastError();
+}
+
+}  // namespace ep

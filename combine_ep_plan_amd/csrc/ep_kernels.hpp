@@ -1,0 +1,51 @@
+// Host-side launchers of the gfx950 kernels (one translation unit per
+// kernel family). All sizes are validated by the C ABI layer before these
+// are called; each launcher only shapes the grid and enqueues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// Sizes derived from a validated descriptor.
+struct Dims {
+  int N, T, H, E, R, L, payload, planes;
+  int64_t cap;       // rows per destination buffer
+  int64_t TR;        // slots (and send rows) per source
+  int64_t NT;        // tokens over all ranks
+  int64_t NTR;       // slots over all ranks
+  int64_t row[2];    // bytes per row of each payload plane (0 if absent)
+  int nchunks;       // plan chunks per source
+};
+
+// Plan workspace pointers (int32 arrays, see ep_plan_view).
+struct PlanPtrs {
+  int32_t *cnt, *send_off, *send_pos, *recv_off, *grp_off, *grp_pos, *src_off,
+      *comb_row, *chunk_cnt;
+};
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanSub = 4;                              // sub-chunks per block
+constexpr int kPlanChunk = kPlanThreads * kPlanSub;      // slots per block
+
+hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
+                       int32_t* status, hipStream_t stream);
+hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
+                       void* const send[2], hipStream_t stream);
+hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs& p,
+                       void* const grouped[2], hipStream_t stream);
+hipError_t launch_transfer(const Dims& d, const void* const send[2], const PlanPtrs& p,
+                           void* const recv[2], hipStream_t stream);
+hipError_t launch_unpack(const Dims& d, const void* const recv[2], const PlanPtrs& p,
+                         void* const grouped[2], hipStream_t stream);
+hipError_t launch_expert_stub(const Dims& d, const void* const grouped[2],
+                              const float* alpha, const PlanPtrs& p, uint16_t* y,
+                              hipStream_t stream);
+hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* w,
+                          const PlanPtrs& p, uint16_t* out, hipStream_t stream);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes,
+                             hipStream_t stream);
+
+}  // namespace ep

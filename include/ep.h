@@ -1,0 +1,219 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel dispatch/combine
+ * library.
+ *
+ * The method is the one described in "Enabling trillion-parameter models on
+ * AWS EFA" (Perplexity, 2025-11-04):
+ *   - section "Dispatch and combine": dispatch receives the tokens and each
+ *     token's experts from the model and moves every token to the ranks that
+ *     host its experts; after the grouped GEMM, combine brings the results
+ *     back to the source rank and forms the routing-weighted average;
+ *     both halves are split into a sender and a receiver;
+ *   - section "Send and receive buffers": per-expert token counts are
+ *     exchanged first so that each sender can place its rows contiguously
+ *     per peer (one bulk write per peer) and each receiver knows the offset
+ *     at which every source lands; a receiver needs room for at most
+ *     N * T * max(R, E/N) rows;
+ *   - timing figures of section "Dispatch and combine": per-expert counts,
+ *     then a running prefix sum gives the send-buffer offsets; the receiver
+ *     shuffles its receive buffer into the grouped-GEMM input; the combine
+ *     receiver accumulates the weighted tokens into the output tensor;
+ *   - section "Evaluation": hidden 7168, block-scaled fp8 dispatch, bf16
+ *     combine.
+ *
+ * One GPU holds all N ranks of the expert-parallel group ("virtual ranks"):
+ * every rank's buffers live in that GPU's HBM and the network write is a
+ * device-local copy. Every call handles all N ranks in one launch sequence.
+ *
+ * Notation: N ranks, T tokens per rank, H hidden size, E experts, R experts
+ * per token, L = E / N experts per rank. Expert e lives on rank e / L as
+ * local expert e % L. A slot is (s, t, k): source rank s, token t, choice k.
+ *
+ * Conventions shared by every call:
+ *   - All buffers are device memory owned by the caller, contiguous and
+ *     row-major in the shapes given below. The library allocates nothing and
+ *     keeps no state between calls; it is re-entrant.
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *     The device is taken from the stream (not from the calling thread);
+ *     buffers on another device give EP_ERR_DEVICE_MISMATCH.
+ *   - Host-side checks fail fast with a negative return and enqueue nothing.
+ *   - Conditions found on the device never cause out-of-bounds writes; they
+ *     OR a bit into the caller's device status word (EP_STATUS_*), which the
+ *     caller zeroes before ep_plan and reads after its own synchronisation.
+ *     Rows that cannot be delivered are dropped and documented as such.
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Only the functions below are exported from the shared library. */
+#define EP_API __attribute__((visibility("default")))
+
+/* Return codes (host side). */
+#define EP_OK 0
+#define EP_ERR_INVALID_ARG (-1)     /* bad descriptor, size or null pointer */
+#define EP_ERR_UNSUPPORTED (-2)     /* valid but outside this build's limits */
+#define EP_ERR_DEVICE_MISMATCH (-3) /* a buffer is not on the stream's GPU */
+#define EP_ERR_HIP (-4)             /* a HIP runtime call failed */
+
+/* Device status bits, OR-ed into *status by ep_plan. */
+#define EP_STATUS_BAD_EXPERT 1 /* an expert id outside [0, E): slot dropped */
+#define EP_STATUS_CAPACITY 2   /* a rank would receive more than cap rows */
+
+/* Payload formats of the dispatched rows. */
+#define EP_PAYLOAD_BF16 0     /* one plane: H bf16 values, 2H bytes per row */
+#define EP_PAYLOAD_FP8_B128 1 /* plane 0: H OCP e4m3fn codes (H bytes);
+                                 plane 1: H/128 fp32 block scales (H/32 B) */
+
+/* Largest sizes this build accepts (EP_ERR_UNSUPPORTED beyond them). */
+#define EP_MAX_EXPERTS 2048
+#define EP_MAX_TOPK 64
+
+/* Problem descriptor. cap_rows is the row capacity of every destination's
+ * receive and grouped buffers; 0 selects the worst-case bound
+ * N * T * max(R, E/N) ("Send and receive buffers"). Requirements:
+ * all sizes > 0 except tokens >= 0, E % N == 0, H % 8 == 0 (bf16) or
+ * H % 128 == 0 (fp8), R <= EP_MAX_TOPK, E <= EP_MAX_EXPERTS,
+ * N * cap_rows < 2^31 and N * T * R < 2^26. */
+typedef struct ep_desc {
+    int32_t n_ranks;   /* N */
+    int32_t tokens;    /* T, tokens per rank */
+    int32_t hidden;    /* H */
+    int32_t n_experts; /* E */
+    int32_t topk;      /* R */
+    int32_t payload;   /* EP_PAYLOAD_* */
+    int64_t cap_rows;  /* rows per destination buffer; 0 = worst-case bound */
+} ep_desc;
+
+/* Device pointers into a plan workspace (see ep_plan for the contents). */
+typedef struct ep_plan_view {
+    int32_t *cnt;      /* [N][E]     rows source s sends to expert e */
+    int32_t *send_off; /* [N][E+1]   exclusive prefix of cnt[s] over e */
+    int32_t *send_pos; /* [N][T][R]  send-buffer row of each slot, or -1 */
+    int32_t *recv_off; /* [N][N+1]   row at which rank d receives source s;
+                                     recv_off[d][N] = rows d receives */
+    int32_t *grp_off;  /* [N][L+1]   grouped-layout offset of local expert j */
+    int32_t *grp_pos;  /* [N][T][R]  grouped row of each slot on its expert's
+                                     rank, or -1 (bad id / over capacity) */
+    int32_t *src_off;  /* [N][E]     rows sources 0..s-1 send to expert e */
+    int32_t *comb_row; /* [N][T][R]  (e / L) * cap + grp_pos, or -1 */
+} ep_plan_view;
+
+/* Worst-case receive rows N * T * max(R, E/N) ("Send and receive buffers");
+ * -1 for an invalid descriptor. */
+EP_API int64_t ep_recv_bound(const ep_desc *d);
+
+/* Rows per destination buffer: cap_rows, or the bound when cap_rows == 0;
+ * -1 for an invalid descriptor. */
+EP_API int64_t ep_capacity(const ep_desc *d);
+
+/* Number of payload planes (1 for bf16, 2 for fp8) and the bytes of one row
+ * of plane p; 0 for an absent plane, -1 for an invalid descriptor. */
+EP_API int ep_num_planes(const ep_desc *d);
+EP_API int64_t ep_row_bytes(const ep_desc *d, int plane);
+
+/* Bytes of the plan workspace for this descriptor (0 if invalid). The
+ * caller allocates it on the device; it needs no initialisation. */
+EP_API size_t ep_plan_bytes(const ep_desc *d);
+
+/* Host-only: fill *v with pointers into plan_ws. No device access. */
+EP_API int ep_plan_views(const ep_desc *d, void *plan_ws, ep_plan_view *v);
+
+/* Plan ("Send and receive buffers"; counts and prefix sums of "Dispatch
+ * and combine"). topk_idx: int32 [N][T][R] expert ids. Writes the whole
+ * plan into plan_ws:
+ *   cnt[s][e]       = #slots of s with expert e;
+ *   send_off[s][e]  = sum_{e' < e} cnt[s][e']; rows for rank d are the
+ *                     contiguous segment [send_off[s][dL], send_off[s][dL+L]);
+ *   send_pos[s][t][k] = send_off[s][e] + #earlier slots (t', k') < (t, k) of
+ *                     s with the same expert (stable: token, then choice);
+ *   recv_off[d][s]  = sum_{s' < s} rows(s' -> d) (sources in rank order);
+ *   grp_off[d][j]   = sum_{j' < j} sum_s cnt[s][dL + j'];
+ *   src_off[s][e]   = sum_{s' < s} cnt[s'][e];
+ *   grp_pos[s][t][k] = grp_off[d][j] + src_off[s][e] + send_pos - send_off[s][e]
+ *                     (grouped order: local expert, source, token, choice);
+ *   comb_row        = d * cap + grp_pos.
+ * Slots with an id outside [0, E) get -1 and set EP_STATUS_BAD_EXPERT; rows
+ * with grp_pos >= cap get -1 and set EP_STATUS_CAPACITY. status: device
+ * int32, bits OR-ed in. Deterministic: equal inputs give equal bytes. */
+EP_API int ep_plan(const ep_desc *d, const int32_t *topk_idx, void *plan_ws,
+            int32_t *status, hipStream_t stream);
+
+/* Dispatch sender ("Dispatch and combine": the sender shuffles tokens into a
+ * send buffer so that each peer takes one bulk write). For each plane p:
+ * x[p] is [N][T][row_p], send[p] is [N][T*R][row_p];
+ * send[p][s][send_pos[s][t][k]] = x[p][s][t] byte for byte. Each token row
+ * is read once and written R times. Slots with send_pos = -1 are skipped.
+ * plane 1 pointers must be NULL for bf16. */
+EP_API int ep_dispatch_pack(const ep_desc *d, const void *const x[2],
+                     const void *plan_ws, void *const send[2],
+                     hipStream_t stream);
+
+/* The network write, materialised: for every pair (s, d) one bulk copy of
+ * s's segment for d into d's receive buffer at recv_off[d][s].
+ * recv[p] is [N][cap][row_p]; rows at or beyond cap are dropped. */
+EP_API int ep_dispatch_transfer(const ep_desc *d, const void *const send[2],
+                         const void *plan_ws, void *const recv[2],
+                         hipStream_t stream);
+
+/* Dispatch receiver on a materialised receive buffer: shuffle recv[p]
+ * ([N][cap][row_p], as written by ep_dispatch_transfer) into the grouped
+ * layout grouped[p] ([N][cap][row_p]; expert j of rank d owns rows
+ * [grp_off[d][j], grp_off[d][j+1])). */
+EP_API int ep_dispatch_unpack(const ep_desc *d, const void *const recv[2],
+                       const void *plan_ws, void *const grouped[2],
+                       hipStream_t stream);
+
+/* Dispatch receiver with the transfer fused in: each destination pulls its
+ * rows straight from the sources' send buffers (the pattern of intra-node
+ * peer-mapped buffers) into the grouped layout:
+ * grouped[p][e / L][grp_pos[s][t][k]] = send[p][s][send_pos[s][t][k]].
+ * Same result as ep_dispatch_transfer followed by ep_dispatch_unpack. */
+EP_API int ep_dispatch_recv(const ep_desc *d, const void *const send[2],
+                     const void *plan_ws, void *const grouped[2],
+                     hipStream_t stream);
+
+/* Stand-in for the grouped GEMM (outside the method; used by tests and the
+ * benchmark to produce expert outputs). expert_out is bf16 [N][cap][H].
+ * bf16 payload: y = x when alpha == NULL, else y = bf16(x * alpha[e]) with a
+ * float multiply; fp8 payload: y = bf16(decode(q) * scale of its 128-block).
+ * Only delivered rows are written. */
+EP_API int ep_expert_stub(const ep_desc *d, const void *const grouped[2],
+                   const float *alpha, const void *plan_ws,
+                   uint16_t *expert_out, hipStream_t stream);
+
+/* Combine receiver ("Dispatch and combine": the weighted average of a
+ * token's expert outputs, accumulated on its source rank).
+ * expert_out: bf16 [N][cap][H]; weights: fp32 [N][T][R]; out: bf16 [N][T][H].
+ * out[s][t][h] = bf16( sum_k w[s][t][k] * y[e_k / L][grp_pos[s][t][k]][h] ),
+ * summed in fp32 in k order (fused multiply-add), rounded once to bf16
+ * (nearest, ties to even). Dropped slots contribute nothing. */
+EP_API int ep_combine(const ep_desc *d, const uint16_t *expert_out,
+               const float *weights, const void *plan_ws, uint16_t *out,
+               hipStream_t stream);
+
+/* Copy `bytes` (a multiple of 16) from src to dst with the library's row
+ * copy loop: a bandwidth reference for measurements, not part of the
+ * method. */
+EP_API int ep_probe_copy(void *dst, const void *src, size_t bytes,
+                  hipStream_t stream);
+
+/* Text for a return code or status bit set; never NULL. */
+EP_API const char *ep_status_string(int code);
+
+/* Last host-side error message of the calling thread ("" if none). */
+EP_API const char *ep_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_H */

@@ -1,0 +1,88 @@
+"""Helpers for the GPU tests: run the library on a workload, read results."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import combine_ep_plan_amd as ep
+import ep_workloads as W
+
+PLAN_FIELDS = ("cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos",
+               "src_off", "comb_row")
+
+
+def note(msg: str) -> None:
+    """Name the case before any GPU step (a fault can end the process)."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def desc_of(sh: W.Shape, cap: int = 0) -> ep.Desc:
+    return ep.make_desc(sh.n_ranks, sh.tokens, sh.hidden, sh.n_experts, sh.topk,
+                        sh.payload, cap or sh.cap_rows)
+
+
+def upload(b: ep.Buffers, wl: W.Workload) -> None:
+    b.idx.copy_(torch.from_numpy(wl.idx))
+    b.weights.copy_(torch.from_numpy(wl.weights))
+    for q, plane in enumerate(wl.planes):
+        b.x[q].copy_(torch.from_numpy(plane))
+
+
+def run_path(d: ep.Desc, b: ep.Buffers, wl: W.Workload, staged: bool = False,
+             stream=None) -> None:
+    """plan -> pack -> (recv | transfer + unpack) -> stand-in expert -> combine."""
+    alpha = torch.from_numpy(wl.alpha).to(b.idx.device) if wl.alpha is not None else None
+    b.status.zero_()
+    ep.plan(d, b.idx, b.plan_ws, b.status, stream)
+    ep.dispatch_pack(d, b.x, b.plan_ws, b.send, stream)
+    if staged:
+        ep.dispatch_transfer(d, b.send, b.plan_ws, b.recv, stream)
+        ep.dispatch_unpack(d, b.recv, b.plan_ws, b.grouped, stream)
+    else:
+        ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, stream)
+    ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out, stream)
+    ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, stream)
+
+
+def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
+    """Copy every plan table of the workspace to host numpy arrays."""
+    N, T, E, R = d.n_ranks, d.tokens, d.n_experts, d.topk
+    L = E // N
+    shapes = {"cnt": (N, E), "send_off": (N, E + 1), "send_pos": (N, T, R),
+              "recv_off": (N, N + 1), "grp_off": (N, L + 1), "grp_pos": (N, T, R),
+              "src_off": (N, E), "comb_row": (N, T, R)}
+    v = ep.plan_views(d, b.plan_ws)
+    base = b.plan_ws.data_ptr()
+    ws = b.plan_ws.cpu().numpy()
+    out = {}
+    for f in PLAN_FIELDS:
+        off = getattr(v, f) - base
+        n = int(np.prod(shapes[f]))
+        out[f] = ws[off:off + 4 * n].view(np.int32).reshape(shapes[f]).copy()
+    return out
+
+
+def expected_plan_extras(p: dict, idx: np.ndarray, N: int, E: int, cap: int) -> dict:
+    """src_off and comb_row from the oracle's cnt and grp_pos (definitions)."""
+    L = E // N
+    cnt = p["cnt"].astype(np.int64)
+    src_off = np.vstack([np.zeros((1, E), np.int64), np.cumsum(cnt, axis=0)[:-1]])
+    comb = np.where(p["grp_pos"] >= 0, (idx // L).astype(np.int64) * cap + p["grp_pos"], -1)
+    return {"src_off": src_off.astype(np.int32), "comb_row": comb.astype(np.int32)}
+
+
+def bf16_close(got: np.ndarray, want: np.ndarray, rel: float = 8e-3) -> np.ndarray:
+    """Per element: |g - o| <= rel * |o| (so o == 0 requires g == 0)."""
+    g = W.bf16_bits_to_f32(got).astype(np.float64)
+    o = W.bf16_bits_to_f32(want).astype(np.float64)
+    return np.abs(g - o) <= rel * np.abs(o)
+
+
+def rows_of(t: torch.Tensor, d_idx: np.ndarray, r_idx: np.ndarray) -> np.ndarray:
+    """Gather rows t[d, r] on the device, return them on the host."""
+    dd = torch.from_numpy(d_idx.astype(np.int64)).to(t.device)
+    rr = torch.from_numpy(r_idx.astype(np.int64)).to(t.device)
+    return t[dd, rr].cpu().numpy()

@@ -1,0 +1,136 @@
+"""C ABI checks that need no GPU: exports, descriptor validation, sizes.
+
+None of these calls reaches a HIP runtime function that needs a device:
+descriptor checks fail before the device is looked up, and the size and
+view helpers are host-only.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_ep_plan_amd as ep
+import ep_workloads as W
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^EP_API\s+[\w\s\*]*?\b(ep_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_every_binding():
+    assert header_functions() == sorted(ep.EXPORTS)
+
+
+def test_library_exports_exactly_the_header():
+    out = subprocess.run(["nm", "-D", "--defined-only", ep.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("ep_")})
+    assert exported == header_functions()
+    for name in header_functions():
+        assert getattr(ep.lib(), name) is not None
+
+
+def test_library_is_gfx950():
+    """The embedded device code object targets gfx950 only."""
+    blob = open(ep.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+    for other in (b"--gfx942", b"--gfx90a", b"--gfx1100"):
+        assert other not in blob
+
+
+def _desc(**kw):
+    base = dict(n_ranks=4, tokens=16, hidden=256, n_experts=16, topk=2, payload=0, cap_rows=0)
+    base.update(kw)
+    return ep.make_desc(**base)
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_bound_matches_oracle_and_page_formula(name):
+    sh = W.CONFIGS[name]
+    d = ep.make_desc(sh.n_ranks, sh.tokens, sh.hidden, sh.n_experts, sh.topk, sh.payload)
+    assert ep.recv_bound(d) == oracle.recv_bound(sh.n_ranks, sh.tokens, sh.n_experts, sh.topk)
+    assert ep.capacity(d) == ep.recv_bound(d)
+    d.cap_rows = 1000
+    assert ep.capacity(d) == 1000
+
+
+def test_row_bytes_and_planes():
+    d = _desc()
+    assert ep.num_planes(d) == 1 and ep.row_bytes(d, 0) == 512 and ep.row_bytes(d, 1) == 0
+    d = _desc(hidden=7168, payload=ep.EP_PAYLOAD_FP8_B128)
+    assert ep.num_planes(d) == 2
+    assert ep.row_bytes(d, 0) == 7168 and ep.row_bytes(d, 1) == 224
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n_ranks=0), ep.EP_ERR_INVALID_ARG),
+    (dict(n_experts=15), ep.EP_ERR_INVALID_ARG),           # E % N != 0
+    (dict(hidden=250), ep.EP_ERR_INVALID_ARG),             # 16-byte bf16 rows
+    (dict(hidden=200, payload=1), ep.EP_ERR_INVALID_ARG),  # fp8 blocks of 128
+    (dict(payload=7), ep.EP_ERR_INVALID_ARG),
+    (dict(cap_rows=-1), ep.EP_ERR_INVALID_ARG),
+    (dict(topk=0), ep.EP_ERR_INVALID_ARG),
+    (dict(tokens=-1), ep.EP_ERR_INVALID_ARG),
+    (dict(n_experts=4096, n_ranks=4), ep.EP_ERR_UNSUPPORTED),
+    (dict(topk=65, n_experts=128), ep.EP_ERR_UNSUPPORTED),
+    (dict(n_ranks=64, tokens=1 << 20, topk=8, n_experts=512), ep.EP_ERR_UNSUPPORTED),
+])
+def test_invalid_descriptors_fail_fast(bad, code):
+    d = _desc(**bad)
+    assert ep.recv_bound(d) == -1
+    assert ep.plan_bytes(d) == 0
+    fake = 0x10000
+    for fn, args in [
+        (ep.lib().ep_plan, (ctypes.byref(d), fake, fake, fake, None)),
+        (ep.lib().ep_dispatch_pack, (ctypes.byref(d), None, fake, None, None)),
+        (ep.lib().ep_dispatch_recv, (ctypes.byref(d), None, fake, None, None)),
+        (ep.lib().ep_dispatch_transfer, (ctypes.byref(d), None, fake, None, None)),
+        (ep.lib().ep_dispatch_unpack, (ctypes.byref(d), None, fake, None, None)),
+        (ep.lib().ep_expert_stub, (ctypes.byref(d), None, None, fake, fake, None)),
+        (ep.lib().ep_combine, (ctypes.byref(d), fake, fake, fake, fake, None)),
+    ]:
+        assert fn(*args) == code
+        assert ep.last_error() != ""
+
+
+def test_null_descriptor():
+    assert ep.lib().ep_plan(None, None, None, None, None) == ep.EP_ERR_INVALID_ARG
+    assert ep.lib().ep_recv_bound(None) == -1
+
+
+def test_plan_views_layout():
+    d = _desc(n_ranks=8, tokens=4096, hidden=7168, n_experts=256, topk=8)
+    base = 1 << 20
+    v = ep.plan_views(d, base)
+    N, E, L, NTR = 8, 256, 32, 8 * 4096 * 8
+    names = ["cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos", "src_off", "comb_row"]
+    sizes = [N * E, N * (E + 1), NTR, N * (N + 1), N * (L + 1), NTR, N * E, NTR]
+    ptrs = [getattr(v, n) for n in names]
+    assert ptrs[0] == base
+    for p, q, n in zip(ptrs, ptrs[1:], sizes):
+        assert (p - base) % 256 == 0
+        assert q - p >= 4 * n                      # no overlap
+    assert ep.plan_bytes(d) >= ptrs[-1] - base + 4 * NTR
+
+
+def test_status_strings():
+    for c in [0, -1, -2, -3, -4, 1, 2, 3, 99]:
+        assert isinstance(ep.status_string(c), str) and ep.status_string(c)
+
+
+def test_oracle_and_library_share_nothing():
+    """The oracle builds from its own sources and never names the library."""
+    osrc = open(os.path.join(ROOT, "oracle", "ep_oracle.c")).read()
+    assert "ep.h" not in osrc and "combine_ep_plan_amd" not in osrc
+    for f in os.listdir(os.path.join(ROOT, "combine_ep_plan_amd", "csrc")):
+        text = open(os.path.join(ROOT, "combine_ep_plan_amd", "csrc", f)).read()
+        assert "oracle" not in text.lower(), f
+    pkg = open(os.path.join(ROOT, "combine_ep_plan_amd", "__init__.py")).read()
+    assert "import oracle" not in pkg and "from oracle" not in pkg
