@@ -60,6 +60,11 @@ class PlanView(ctypes.Structure):
 
 
 def _load() -> ctypes.CDLL:
+    # torch first: it loads its own HIP runtime, and the library's dependency
+    # on libamdhip64.so.7 must resolve to that same, already-loaded copy
+    # (two HIP runtimes in one process would not share devices or memory).
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")

@@ -78,7 +78,8 @@ def compare_full(sh, wl, cap=0, staged=False, check_closed_form=True):
     ok = bf16_close(out, ref["out"])
     assert ok.all(), f"combine: {int((~ok).sum())} elements off, first {np.argwhere(~ok)[:3]}"
     if check_closed_form and _identity_exact(sh, wl) and p["status"] == 0:
-        np.testing.assert_array_equal(out, wl.x_bf16)     # identity experts: out == x
+        # identity experts: out == x as numbers (+0 for -0 inputs)
+        np.testing.assert_array_equal(_unsign_zero(out), _unsign_zero(wl.x_bf16))
     return d, b, ref
 
 
@@ -250,6 +251,21 @@ def compare_full_size(name, n_slots=3000, n_tokens=300):
         np.testing.assert_array_equal(got[f], p[f], err_msg=f)
     for f, v in expected_plan_extras(p, wl.idx, N, E, cap).items():
         np.testing.assert_array_equal(got[f], v, err_msg=f)
+    # every send row and every delivered grouped row, on the device, against
+    # the token row the oracle's plan puts there
+    ss, tt_, kk = np.unravel_index(np.arange(N * T * R), (N, T, R))
+    ee = wl.idx.reshape(-1)
+    for q in range(len(wl.planes)):
+        for lo in range(0, N * T * R, 8192):
+            sl = slice(lo, min(lo + 8192, N * T * R))
+            si = torch.from_numpy(ss[sl]).cuda()
+            ti = torch.from_numpy(tt_[sl]).cuda()
+            want = b.x[q][si, ti]
+            spi = torch.from_numpy(p["send_pos"].reshape(-1)[sl].astype(np.int64)).cuda()
+            gpi = torch.from_numpy(p["grp_pos"].reshape(-1)[sl].astype(np.int64)).cuda()
+            di = torch.from_numpy((ee[sl] // L).astype(np.int64)).cuda()
+            assert torch.equal(b.send[q][si, spi], want), f"send rows {lo}.."
+            assert torch.equal(b.grouped[q][di, gpi], want), f"grouped rows {lo}.."
     rng = np.random.default_rng(123)
     slots = rng.choice(N * T * R, size=min(N * T * R, n_slots), replace=False)
     s, t, k = np.unravel_index(slots, (N, T, R))
@@ -294,19 +310,40 @@ def test_full_size_decode_zipf():
     compare_full_size("decode_zipf")
 
 
+def _unsign_zero(a):
+    """-0 and +0 are the same number: map the bf16 pattern 0x8000 to 0."""
+    return a.masked_fill(a == -32768, 0) if isinstance(a, torch.Tensor) else np.where(a == 0x8000, 0, a)
+
+
+def assert_tokens_equal(got: torch.Tensor, want: np.ndarray, what: str):
+    """Equality as numbers of [N][T][H] bf16 tensors (a weighted sum that
+    starts from +0 turns -0 inputs into +0), with a readable report."""
+    w = _unsign_zero(torch.from_numpy(want.view(np.int16)).to(got.device))
+    bad = (_unsign_zero(got) != w)
+    if bool(bad.any()):
+        tok = bad.any(dim=-1).nonzero().cpu().numpy()
+        n_el = int(bad.sum().item())
+        g = got.cpu().numpy().view(np.uint16)
+        s, t = tok[0]
+        h = np.nonzero(g[s, t] != want[s, t])[0][:8]
+        raise AssertionError(
+            f"{what}: {len(tok)} tokens / {n_el} elements differ; first (s,t)={tuple(tok[0])} "
+            f"h={h.tolist()} got={g[s, t][h].tolist()} want={want[s, t][h].tolist()}; "
+            f"tokens={tok[:10].tolist()}")
+
+
 def test_full_size_worst_all_to_rank0():
     sh, wl, b = compare_full_size("worst")
     # identity experts, weights summing to one: every output token equals x
-    assert torch.equal(b.out.cpu(), torch.from_numpy(wl.x_bf16.view(np.int16)))
+    assert_tokens_equal(b.out, wl.x_bf16, "worst combine")
 
 
 def test_full_size_prefill_fp8():
     sh, wl, b = compare_full_size("prefill", n_slots=2000, n_tokens=100)
     # identity on dequantised rows: every output token equals bf16(dequant(x))
-    got = b.out.cpu().numpy().view(np.uint16)
     N, T, H = sh.n_ranks, sh.tokens, sh.hidden
-    rng = np.random.default_rng(7)
+    want = np.empty((N, T, H), np.uint16)
     for s in range(N):
-        for t in rng.choice(T, size=256, replace=False):
-            want = oracle.expert_row([wl.planes[0][s, t], wl.planes[1][s, t]], 0, 1, H, None)
-            np.testing.assert_array_equal(got[s, t], want)
+        for t in range(T):
+            want[s, t] = oracle.expert_row([wl.planes[0][s, t], wl.planes[1][s, t]], 0, 1, H, None)
+    assert_tokens_equal(b.out, want, "prefill combine")
