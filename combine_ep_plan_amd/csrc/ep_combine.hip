@@ -47,8 +47,8 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint16_t* __restr
   const int32_t* rows = comb_row + (size_t)tok * R;
   const float* wt = w + (size_t)tok * R;
   const int n16 = H / 8;
-  const uint4* ybase = (const uint4*)y;
-  uint4* o = (uint4*)(out + (size_t)tok * H);
+  const u32x4* ybase = (const u32x4*)y;
+  u32x4* o = (u32x4*)(out + (size_t)tok * H);
   for (int base = 0; base < n16; base += kWave * kCombV) {
     float acc[kCombV][8];
 #pragma unroll
@@ -107,26 +107,25 @@ __global__ __launch_bounds__(kBlock) void expert_stub_kernel(
   uint16_t* yr = y + grow * H;
   const int lane = lane_id();
   if (payload == 0) {
-    const uint4* in = (const uint4*)(g0 + grow * (size_t)H * 2);
+    const u32x4* in = (const u32x4*)(g0 + grow * (size_t)H * 2);
     const float a = alpha ? alpha[e] : 1.0f;
     for (int c = lane; c < H / 8; c += kWave) {
-      uint4 v = in[c];
+      u32x4 v = load_stream(&in[c]);
       if (alpha) {
-        uint32_t* q = (uint32_t*)&v;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          const uint32_t lo16 = f32_to_bf16_bits(bf16_lo(q[h]) * a);
-          const uint32_t hi16 = f32_to_bf16_bits(bf16_hi(q[h]) * a);
-          q[h] = lo16 | (hi16 << 16);
+          const uint32_t lo16 = f32_to_bf16_bits(bf16_lo(v[h]) * a);
+          const uint32_t hi16 = f32_to_bf16_bits(bf16_hi(v[h]) * a);
+          v[h] = lo16 | (hi16 << 16);
         }
       }
-      ((uint4*)yr)[c] = v;
+      store_stream(&((u32x4*)yr)[c], v);
     }
   } else {
-    const uint4* codes = (const uint4*)(g0 + grow * (size_t)H);
+    const u32x4* codes = (const u32x4*)(g0 + grow * (size_t)H);
     const float* scales = (const float*)(g1 + grow * (size_t)(H / 32));
     for (int c = lane; c < H / 16; c += kWave) {
-      const uint4 v = codes[c];
+      const u32x4 v = load_stream(&codes[c]);
       const float sc = scales[(c * 16) / 128];
       const uint32_t q[4] = {v.x, v.y, v.z, v.w};
       uint32_t o[8];
@@ -139,8 +138,8 @@ __global__ __launch_bounds__(kBlock) void expert_stub_kernel(
         o[2 * h] = b0 | (b1 << 16);
         o[2 * h + 1] = b2 | (b3 << 16);
       }
-      ((uint4*)yr)[2 * c] = make_uint4(o[0], o[1], o[2], o[3]);
-      ((uint4*)yr)[2 * c + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+      store_stream(&((u32x4*)yr)[2 * c], u32x4{o[0], o[1], o[2], o[3]});
+      store_stream(&((u32x4*)yr)[2 * c + 1], u32x4{o[4], o[5], o[6], o[7]});
     }
   }
 }

@@ -39,8 +39,8 @@ __device__ __forceinline__ void wave_copy_row(const uint8_t* src,
     const int n16 = (int)(row >> 4);
     for (int base = 0; base < n16; base += kWave * kRowV) {
       RowRegs<kRowV> r;
-      load_row16(r, (const uint4*)src, base, n16);
-      store_row16(r, (uint4*)dst, base, n16);
+      load_row16(r, (const u32x4*)src, base, n16);
+      store_row16(r, (u32x4*)dst, base, n16);
     }
   } else {
     copy_row4((const uint32_t*)src, (uint32_t*)dst, row >> 2);
@@ -64,11 +64,11 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(Planes pl, const int32_t* 
       const int n16 = (int)(row >> 4);
       for (int base = 0; base < n16; base += kWave * kRowV) {
         RowRegs<kRowV> r;
-        load_row16(r, (const uint4*)src, base, n16);
+        load_row16(r, (const u32x4*)src, base, n16);
         for (int k = 0; k < R; ++k) {
           const int p = sp[k];
           if (p < 0 || p >= TR) continue;
-          store_row16(r, (uint4*)(dst0 + (size_t)p * row), base, n16);
+          store_row16(r, (u32x4*)(dst0 + (size_t)p * row), base, n16);
         }
       }
     } else {
@@ -166,8 +166,8 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(Planes pl, const int32_t
   }
 }
 
-__global__ __launch_bounds__(kBlock) void probe_copy_kernel(const uint4* __restrict__ src,
-                                                            uint4* __restrict__ dst, int64_t n16) {
+__global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4* src, u32x4* dst,
+                                                            int64_t n16) {
   const int64_t base = (int64_t)wave_index() * kWave * kRowV;
   if (base >= n16) return;
   const int64_t left = n16 - base;
@@ -235,7 +235,7 @@ hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream
   if (n16 == 0) return hipSuccess;
   const int64_t waves = (n16 + kWave * kRowV - 1) / (kWave * kRowV);
   hipLaunchKernelGGL(probe_copy_kernel, dim3(blocks_for(waves)), dim3(kBlock), 0, stream,
-                     (const uint4*)src, (uint4*)dst, n16);
+                     (const u32x4*)src, (u32x4*)dst, n16);
   return hipGetLastError();
 }
 
