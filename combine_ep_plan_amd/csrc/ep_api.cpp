@@ -86,12 +86,12 @@ int derive(const ep_desc* d, ep::Dims* o) {
 
 // Plan workspace: int32 arrays, each starting on a 256-byte boundary.
 struct Layout {
-  size_t off[9];
+  size_t off[10];
   size_t bytes;
 };
 
 Layout layout_of(const ep::Dims& d) {
-  const size_t n[9] = {
+  const size_t n[10] = {
       (size_t)d.N * d.E,                       // cnt
       (size_t)d.N * (d.E + 1),                 // send_off
       (size_t)d.NTR,                           // send_pos
@@ -100,11 +100,12 @@ Layout layout_of(const ep::Dims& d) {
       (size_t)d.NTR,                           // grp_pos
       (size_t)d.N * d.E,                       // src_off
       (size_t)d.NTR,                           // comb_row
+      (size_t)d.NTR,                           // grp_slot
       (size_t)d.N * d.nchunks * d.E,           // chunk_cnt
   };
   Layout l{};
   size_t at = 0;
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < 10; ++i) {
     l.off[i] = at;
     at += (n[i] * sizeof(int32_t) + 255) & ~(size_t)255;
   }
@@ -124,7 +125,8 @@ ep::PlanPtrs plan_ptrs(const ep::Dims& d, const void* ws) {
   p.grp_pos = (int32_t*)(b + l.off[5]);
   p.src_off = (int32_t*)(b + l.off[6]);
   p.comb_row = (int32_t*)(b + l.off[7]);
-  p.chunk_cnt = (int32_t*)(b + l.off[8]);
+  p.grp_slot = (int32_t*)(b + l.off[8]);
+  p.chunk_cnt = (int32_t*)(b + l.off[9]);
   return p;
 }
 
@@ -252,6 +254,7 @@ int ep_plan_views(const ep_desc* d, void* plan_ws, ep_plan_view* v) {
   v->grp_pos = p.grp_pos;
   v->src_off = p.src_off;
   v->comb_row = p.comb_row;
+  v->grp_slot = p.grp_slot;
   return EP_OK;
 }
 

@@ -81,19 +81,26 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(Planes pl, const int32_t* 
   }
 }
 
-// Receiver with the transfer fused in: one wave per slot pulls the slot's
-// send row of its source straight into the grouped row on its expert's rank
-// (comb_row = rank * cap + grouped position). Every row index is range
-// checked, so no plan content can make the kernel leave its buffers.
-__global__ __launch_bounds__(kBlock) void recv_kernel(Planes pl, const int32_t* __restrict__ send_pos,
+// Receiver with the transfer fused in: wave j pulls the j-th row of the
+// receive order (grp_slot: each rank's grouped rows in turn) from its
+// source's send buffer into the grouped layout on its expert's rank
+// (comb_row = rank * cap + grouped position). Visiting rows in receive
+// order makes every rank's grouped buffer a sequential write stream (the
+// pulls from the send buffers are the scattered side, which costs less).
+// Every row index is range checked, so no plan content can make the kernel
+// leave its buffers.
+__global__ __launch_bounds__(kBlock) void recv_kernel(Planes pl, const int32_t* __restrict__ grp_slot,
+                                                      const int32_t* __restrict__ send_pos,
                                                       const int32_t* __restrict__ comb_row,
-                                                      int64_t NTR, int64_t TR, int64_t rows_out) {
-  const int slot = wave_index();
-  if (slot >= NTR) return;
+                                                      int NTR, int TR, int64_t rows_out) {
+  const int j = wave_index();
+  if (j >= NTR) return;
+  const int slot = grp_slot[j];
+  if (slot < 0 || slot >= NTR) return;
   const int p = send_pos[slot];
   const int g = comb_row[slot];
   if (p < 0 || p >= TR || g < 0 || g >= rows_out) return;
-  const int s = (int)(slot / TR);
+  const int s = slot / TR;
   for (int q = 0; q < pl.planes; ++q) {
     const int64_t row = pl.row[q];
     wave_copy_row(pl.src[q] + ((size_t)s * TR + p) * row, pl.dst[q] + (size_t)g * row, row);
@@ -206,8 +213,8 @@ hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs&
                        void* const grouped[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
   hipLaunchKernelGGL(recv_kernel, dim3(blocks_for(d.NTR)), dim3(kBlock), 0, stream,
-                     make_planes(d, send, grouped), p.send_pos, p.comb_row, d.NTR, d.TR,
-                     (int64_t)d.N * d.cap);
+                     make_planes(d, send, grouped), p.grp_slot, p.send_pos, p.comb_row,
+                     (int)d.NTR, (int)d.TR, (int64_t)d.N * d.cap);
   return hipGetLastError();
 }
 

@@ -137,15 +137,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
   int32_t* sro = pre + E;            // [E]   rows earlier sources send to e
   int32_t* sros = sro + E;           // [E+1] prefix of sro over experts
   int32_t* gsc = sros + (E + 1);     // [E+1] prefix of column totals
-  int32_t* scratch = gsc + (E + 1);  // [kPlanThreads / 64]
+  int32_t* dstart = gsc + (E + 1);   // [N+1] first receive-order row of rank d
+  int32_t* scratch = dstart + (N + 1);  // [kPlanThreads / 64], then partial sums
   const int s = blockIdx.y;
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
 
-  // The exchange: every block reads the counts of all sources.
-  for (int e = tid; e < E; e += kPlanThreads) {
-    int mine = 0, mypre = 0, before = 0, total = 0;
-    for (int s2 = 0; s2 < N; ++s2) {
+  // The exchange: every block reads the counts of all sources. The column
+  // sums over sources are split across G thread groups (sources s2 = g,
+  // g + G, ...) so that all threads issue loads, then reduced through LDS.
+  const int G = E >= kPlanThreads ? 1 : kPlanThreads / E;
+  int32_t* part_total = scratch + kPlanThreads / kWave;  // [G][E]
+  int32_t* part_before = part_total + G * E;             // [G][E]
+  for (int q = tid; q < G * E; q += kPlanThreads) {
+    const int g = q / E, e = q % E;
+    int total = 0, before = 0;
+#pragma unroll 4
+    for (int s2 = g; s2 < N; s2 += G) {
       const int32_t* cc = p.chunk_cnt + (size_t)s2 * nchunks * E + e;
       int sum = 0, part = 0;
       for (int c2 = 0; c2 < nchunks; ++c2) {
@@ -154,15 +162,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
         if (c2 < c) part += v;
       }
       total += sum;
-      if (s2 < s) {
-        before += sum;
-      } else if (s2 == s) {
-        mine = sum;
-        mypre = part;
+      if (s2 < s) before += sum;
+      if (s2 == s) {
+        soff[e] = sum;
+        pre[e] = part;
       }
     }
-    soff[e] = mine;
-    pre[e] = mypre;
+    part_total[q] = total;
+    part_before[q] = before;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int total = 0, before = 0;
+    for (int g = 0; g < G; ++g) {
+      total += part_total[g * E + e];
+      before += part_before[g * E + e];
+    }
     sro[e] = before;
     sros[e] = before;
     gsc[e] = total;
@@ -177,6 +192,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
   block_exclusive_scan(soff, E, scratch, &soff[E]);
   block_exclusive_scan(sros, E, scratch, &sros[E]);
   block_exclusive_scan(gsc, E, scratch, &gsc[E]);
+  // Receive order: the delivered rows of rank 0, then rank 1, ...
+  for (int d = tid; d < N; d += kPlanThreads) {
+    const int64_t total = gsc[(d + 1) * L] - gsc[d * L];
+    dstart[d] = (int32_t)(total < cap ? total : cap);
+  }
+  __syncthreads();
+  block_exclusive_scan(dstart, N, scratch, &dstart[N]);
 
   if (c == 0) {
     for (int e = tid; e <= E; e += kPlanThreads) p.send_off[(size_t)s * (E + 1) + e] = soff[e];
@@ -216,11 +238,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
     if (g < cap) {
       p.grp_pos[gi] = (int32_t)g;
       p.comb_row[gi] = (int32_t)((int64_t)d * cap + g);
+      p.grp_slot[dstart[d] + g] = (int32_t)gi;
     } else {
       p.grp_pos[gi] = -1;
       p.comb_row[gi] = -1;
     }
   }
+  // Receive-order entries past the last delivered row, shared by all blocks.
+  const int64_t nblocks = (int64_t)gridDim.x * gridDim.y;
+  const int64_t bl = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  for (int64_t j = dstart[N] + bl * kPlanThreads + tid; j < (int64_t)N * TR;
+       j += nblocks * kPlanThreads)
+    p.grp_slot[j] = -1;
 }
 
 }  // namespace
@@ -229,7 +258,9 @@ hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                        int32_t* status, hipStream_t stream) {
   constexpr int kWaves = kPlanThreads / kWave;
   const size_t lds_count = sizeof(int32_t) * (size_t)(kWaves + 1) * (d.E + 1);
-  const size_t lds_final = sizeof(int32_t) * ((size_t)5 * (d.E + 1) + kWaves);
+  const int groups = d.E >= kPlanThreads ? 1 : kPlanThreads / d.E;
+  const size_t lds_final = sizeof(int32_t) * ((size_t)5 * (d.E + 1) + (d.N + 1) + kWaves +
+                                              (size_t)2 * groups * d.E);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)plan_count_kernel,

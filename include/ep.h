@@ -105,6 +105,10 @@ typedef struct ep_plan_view {
                                      rank, or -1 (bad id / over capacity) */
     int32_t *src_off;  /* [N][E]     rows sources 0..s-1 send to expert e */
     int32_t *comb_row; /* [N][T][R]  (e / L) * cap + grp_pos, or -1 */
+    int32_t *grp_slot; /* [N*T*R]    slots in receive order: all delivered
+                                     rows of rank 0 in grouped order, then
+                                     rank 1, ...; slot id (s*T + t)*R + k;
+                                     -1 after the last delivered row */
 } ep_plan_view;
 
 /* Worst-case receive rows N * T * max(R, E/N) ("Send and receive buffers");
@@ -140,7 +144,10 @@ EP_API int ep_plan_views(const ep_desc *d, void *plan_ws, ep_plan_view *v);
  *   src_off[s][e]   = sum_{s' < s} cnt[s'][e];
  *   grp_pos[s][t][k] = grp_off[d][j] + src_off[s][e] + send_pos - send_off[s][e]
  *                     (grouped order: local expert, source, token, choice);
- *   comb_row        = d * cap + grp_pos.
+ *   comb_row        = d * cap + grp_pos;
+ *   grp_slot[j]     = the slot whose row is the j-th delivered row when the
+ *                     ranks' grouped layouts are concatenated in rank order
+ *                     (each truncated to cap rows); -1 for j past the end.
  * Slots with an id outside [0, E) get -1 and set EP_STATUS_BAD_EXPERT; rows
  * with grp_pos >= cap get -1 and set EP_STATUS_CAPACITY. status: device
  * int32, bits OR-ed in. Deterministic: equal inputs give equal bytes. */

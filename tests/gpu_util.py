@@ -10,7 +10,7 @@ import combine_ep_plan_amd as ep
 import ep_workloads as W
 
 PLAN_FIELDS = ("cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos",
-               "src_off", "comb_row")
+               "src_off", "comb_row", "grp_slot")
 
 
 def note(msg: str) -> None:
@@ -53,7 +53,7 @@ def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
     L = E // N
     shapes = {"cnt": (N, E), "send_off": (N, E + 1), "send_pos": (N, T, R),
               "recv_off": (N, N + 1), "grp_off": (N, L + 1), "grp_pos": (N, T, R),
-              "src_off": (N, E), "comb_row": (N, T, R)}
+              "src_off": (N, E), "comb_row": (N, T, R), "grp_slot": (N * T * R,)}
     v = ep.plan_views(d, b.plan_ws)
     base = b.plan_ws.data_ptr()
     ws = b.plan_ws.cpu().numpy()
@@ -66,12 +66,22 @@ def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
 
 
 def expected_plan_extras(p: dict, idx: np.ndarray, N: int, E: int, cap: int) -> dict:
-    """src_off and comb_row from the oracle's cnt and grp_pos (definitions)."""
+    """src_off, comb_row and grp_slot from the oracle's cnt and grp_pos,
+    by their definitions."""
     L = E // N
     cnt = p["cnt"].astype(np.int64)
     src_off = np.vstack([np.zeros((1, E), np.int64), np.cumsum(cnt, axis=0)[:-1]])
     comb = np.where(p["grp_pos"] >= 0, (idx // L).astype(np.int64) * cap + p["grp_pos"], -1)
-    return {"src_off": src_off.astype(np.int32), "comb_row": comb.astype(np.int32)}
+    # receive order: rank 0's delivered grouped rows, then rank 1's, ...
+    delivered = np.minimum(p["recv_off"][:, N].astype(np.int64), cap)
+    dstart = np.concatenate([[0], np.cumsum(delivered)])
+    grp_slot = np.full(idx.size, -1, np.int64)
+    gp = p["grp_pos"].reshape(-1)
+    dd = (idx.reshape(-1) // L)
+    ok = gp >= 0
+    grp_slot[dstart[dd[ok]] + gp[ok]] = np.nonzero(ok)[0]
+    return {"src_off": src_off.astype(np.int32), "comb_row": comb.astype(np.int32),
+            "grp_slot": grp_slot.astype(np.int32)}
 
 
 def bf16_close(got: np.ndarray, want: np.ndarray, rel: float = 8e-3) -> np.ndarray:
