@@ -44,6 +44,35 @@ def algorithmic_bytes(sh, row_d: int) -> dict:
     return {"stages": stages, "step": sum(stages.values())}
 
 
+def kernel_source_hash() -> str:
+    """Hash of the device sources (kernels and device headers), to tell
+    whether recorded counters still apply."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_ep_plan_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, or None if there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256_16") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["traffic_bytes"]
+
+
 def cpu_baseline(sh, wl, budget_s: float) -> dict:
     """The oracle as it stands, single thread, on the same workload."""
     import numpy as np
@@ -223,7 +252,8 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(args.config, f"{dom}_kernel"),
+            "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
             "algorithmic_bytes": ab["stages"][dom],
             "avg_us": round(dom_ms * 1e3, 2),
         },

@@ -3,9 +3,10 @@
 //
 // The device of every call is the stream's device, made current for the
 // duration of the call and restored afterwards; the calling thread's current
-// device is never assumed (a transfer thread that never selected its GPU
-// silently used the wrong one in the KV-transfer study "NIXL LIBFABRIC
-// backend, same-node transfer", section on the wrong-current-device bug).
+// device is never assumed. In the same-node KV-transfer study "EFA の同じ
+// ノード内の GPU 間通信: libfabric の shm と SAR" (sections 問題 and 直し方2),
+// a transfer thread that never selected its GPU silently fell back to a slow
+// path.
 #include "../../include/ep.h"
 
 #include <hip/hip_runtime.h>
