@@ -6,10 +6,14 @@
 // their routing-weighted average into the output tensor; accumulation
 // happens on the receiving (source) side only.
 //
-// One wave per output token. For each column block the wave loads the
-// token's R expert rows (two at a time, so two rows are in flight) and
-// accumulates w_k * y_k in fp32 with fused multiply-adds in k order, then
-// rounds once to bf16 (nearest, ties to even) and stores 16 bytes per lane.
+// Two waves per output token, each owning alternate column blocks of 64 x 7
+// 16-byte chunks (for H = 7168 each wave takes one half of the row). Per
+// block the wave loads two of the token's expert rows at a time (both in
+// flight) and accumulates w_k * y_k in fp32 with fused multiply-adds in k
+// order, then rounds once to bf16 (nearest, ties to even) and stores 16
+// bytes per lane. Splitting a token over two waves doubles the waves in
+// flight at 120 VGPRs per wave; keeping more rows in flight per wave
+// instead costs occupancy and measured slower.
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 
@@ -18,7 +22,9 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWavesPerBlock * kWave;
-constexpr int kCombV = 7;   // 16-byte chunks (8 bf16) per lane per pass
+constexpr int kCombV = 7;          // 16-byte chunks (8 bf16) per lane per block
+constexpr int kCombWaves = 2;      // waves per output token
+constexpr int kCombRows = 2;       // expert rows in flight per wave
 
 __device__ __forceinline__ int wave_index() {
   return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
@@ -28,11 +34,10 @@ template <int V>
 __device__ __forceinline__ void fma_row(float (&acc)[V][8], const RowRegs<V>& r, float w) {
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    const uint32_t q[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      acc[i][2 * h] = __builtin_fmaf(w, bf16_lo(q[h]), acc[i][2 * h]);
-      acc[i][2 * h + 1] = __builtin_fmaf(w, bf16_hi(q[h]), acc[i][2 * h + 1]);
+      acc[i][2 * h] = __builtin_fmaf(w, bf16_lo(r.v[i][h]), acc[i][2 * h]);
+      acc[i][2 * h + 1] = __builtin_fmaf(w, bf16_hi(r.v[i][h]), acc[i][2 * h + 1]);
     }
   }
 }
@@ -40,48 +45,43 @@ __device__ __forceinline__ void fma_row(float (&acc)[V][8], const RowRegs<V>& r,
 __global__ __launch_bounds__(kBlock) void combine_kernel(const uint16_t* __restrict__ y,
                                                          const float* __restrict__ w,
                                                          const int32_t* __restrict__ comb_row,
-                                                         uint16_t* __restrict__ out, int64_t NT,
+                                                         uint16_t* __restrict__ out, int NT,
                                                          int R, int H, int64_t rows_in) {
-  const int tok = wave_index();
+  const int wv = wave_index();
+  const int tok = wv / kCombWaves;
+  const int part = wv % kCombWaves;
   if (tok >= NT) return;
   const int32_t* rows = comb_row + (size_t)tok * R;
   const float* wt = w + (size_t)tok * R;
   const int n16 = H / 8;
   const u32x4* ybase = (const u32x4*)y;
   u32x4* o = (u32x4*)(out + (size_t)tok * H);
-  for (int base = 0; base < n16; base += kWave * kCombV) {
+  for (int base = part * kWave * kCombV; base < n16; base += kCombWaves * kWave * kCombV) {
     float acc[kCombV][8];
 #pragma unroll
     for (int i = 0; i < kCombV; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-    int k = 0;
-    for (; k + 1 < R; k += 2) {
+    for (int k0 = 0; k0 < R; k0 += kCombRows) {
       // rows outside [0, rows_in) (dropped slots) contribute nothing
-      const int r0 = rows[k] < rows_in ? rows[k] : -1;
-      const int r1 = rows[k + 1] < rows_in ? rows[k + 1] : -1;
-      RowRegs<kCombV> v0, v1;
-      if (r0 >= 0) load_row16(v0, ybase + (size_t)r0 * n16, base, n16);
-      if (r1 >= 0) load_row16(v1, ybase + (size_t)r1 * n16, base, n16);
-      if (r0 >= 0) fma_row(acc, v0, wt[k]);
-      if (r1 >= 0) fma_row(acc, v1, wt[k + 1]);
-    }
-    if (k < R) {
-      const int r0 = rows[k] < rows_in ? rows[k] : -1;
-      if (r0 >= 0) {
-        RowRegs<kCombV> v0;
-        load_row16(v0, ybase + (size_t)r0 * n16, base, n16);
-        fma_row(acc, v0, wt[k]);
+      int r[kCombRows];
+      RowRegs<kCombV> v[kCombRows];
+#pragma unroll
+      for (int b = 0; b < kCombRows; ++b) {
+        r[b] = k0 + b < R ? rows[k0 + b] : -1;
+        if (r[b] >= rows_in) r[b] = -1;
+        if (r[b] >= 0) load_row16(v[b], ybase + (size_t)r[b] * n16, base, n16);
       }
+#pragma unroll
+      for (int b = 0; b < kCombRows; ++b)
+        if (r[b] >= 0) fma_row(acc, v[b], wt[k0 + b]);
     }
     RowRegs<kCombV> res;
 #pragma unroll
-    for (int i = 0; i < kCombV; ++i) {
-      res.v[i].x = f32_to_bf16_bits(acc[i][0]) | (f32_to_bf16_bits(acc[i][1]) << 16);
-      res.v[i].y = f32_to_bf16_bits(acc[i][2]) | (f32_to_bf16_bits(acc[i][3]) << 16);
-      res.v[i].z = f32_to_bf16_bits(acc[i][4]) | (f32_to_bf16_bits(acc[i][5]) << 16);
-      res.v[i].w = f32_to_bf16_bits(acc[i][6]) | (f32_to_bf16_bits(acc[i][7]) << 16);
-    }
+    for (int i = 0; i < kCombV; ++i)
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        res.v[i][h] = f32_to_bf16_bits(acc[i][2 * h]) | (f32_to_bf16_bits(acc[i][2 * h + 1]) << 16);
     store_row16(res, o, base, n16);
   }
 }
@@ -153,8 +153,8 @@ unsigned blocks_for(int64_t waves) {
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* w, const PlanPtrs& p,
                           uint16_t* out, hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(d.NT)), dim3(kBlock), 0, stream, y, w,
-                     p.comb_row, out, d.NT, d.R, d.H, (int64_t)d.N * d.cap);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(d.NT * kCombWaves)), dim3(kBlock), 0,
+                     stream, y, w, p.comb_row, out, (int)d.NT, d.R, d.H, (int64_t)d.N * d.cap);
   return hipGetLastError();
 }
 
