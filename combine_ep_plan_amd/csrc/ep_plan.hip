@@ -143,6 +143,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
 
+  // This block's slots: expert ids and the ranks left by the count kernel,
+  // fetched first so that their latency overlaps the exchange below.
+  const int32_t* src = idx + (size_t)s * TR;
+  int e_of[kPlanSub], rank_of[kPlanSub];
+#pragma unroll
+  for (int sub = 0; sub < kPlanSub; ++sub) {
+    const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * kPlanThreads + tid;
+    e_of[sub] = -1;
+    rank_of[sub] = 0;
+    if (i < TR) {
+      e_of[sub] = src[i];
+      rank_of[sub] = p.send_pos[(size_t)s * TR + i];
+    }
+  }
+
   // The exchange: every block reads the counts of all sources. The column
   // sums over sources are split across G thread groups (sources s2 = g,
   // g + G, ...) so that all threads issue loads, then reduced through LDS.
@@ -219,19 +234,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
   }
 
   // Final positions of this block's slots.
-  const int32_t* src = idx + (size_t)s * TR;
+#pragma unroll
   for (int sub = 0; sub < kPlanSub; ++sub) {
     const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * kPlanThreads + tid;
     if (i >= TR) break;
     const size_t gi = (size_t)s * TR + i;
-    const int e = src[i];
+    const int e = e_of[sub];
     if (e < 0 || e >= E) {
       p.send_pos[gi] = -1;
       p.grp_pos[gi] = -1;
       p.comb_row[gi] = -1;
       continue;
     }
-    const int within = pre[e] + p.send_pos[gi];  // rank left by the count kernel
+    const int within = pre[e] + rank_of[sub];
     p.send_pos[gi] = soff[e] + within;
     const int d = e / L;
     const int64_t g = (int64_t)(gsc[e] - gsc[d * L]) + sro[e] + within;
