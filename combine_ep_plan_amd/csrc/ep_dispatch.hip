@@ -32,16 +32,30 @@ __device__ __forceinline__ int wave_index() {
   return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
 }
 
-// Copy one row of `row` bytes (multiple of 4) with the whole wave.
-__device__ __forceinline__ void wave_copy_row(const uint8_t* src,
-                                              uint8_t* dst, int64_t row) {
+// Copy one row of n16 16-byte chunks with the whole wave, V chunks per lane
+// per pass.
+template <int V>
+__device__ __forceinline__ void copy_row16(const uint8_t* src, uint8_t* dst, int n16) {
+  for (int base = 0; base < n16; base += kWave * V) {
+    RowRegs<V> r;
+    load_row16(r, (const u32x4*)src, base, n16);
+    store_row16(r, (u32x4*)dst, base, n16);
+  }
+}
+
+// Copy one row of `row` bytes (multiple of 4) with the whole wave. The
+// chunks per lane follow the row size (14 for a 14 KB bf16 row, 7 for a
+// 7 KB fp8 row, 1 for a scale row), so no wave issues store instructions
+// whose lanes would all be clamped duplicates.
+__device__ __forceinline__ void wave_copy_row(const uint8_t* src, uint8_t* dst, int64_t row) {
   if ((row & 15) == 0) {
     const int n16 = (int)(row >> 4);
-    for (int base = 0; base < n16; base += kWave * kRowV) {
-      RowRegs<kRowV> r;
-      load_row16(r, (const u32x4*)src, base, n16);
-      store_row16(r, (u32x4*)dst, base, n16);
-    }
+    if (n16 > kWave * 7)
+      copy_row16<kRowV>(src, dst, n16);
+    else if (n16 > kWave)
+      copy_row16<7>(src, dst, n16);
+    else
+      copy_row16<1>(src, dst, n16);
   } else {
     copy_row4((const uint32_t*)src, (uint32_t*)dst, row >> 2);
   }
@@ -51,13 +65,32 @@ __device__ __forceinline__ void wave_copy_row(const uint8_t* src,
 // flight per wave), then each is written to its R send slots. Two tokens
 // per wave measured faster than one (more loads in flight per wave at the
 // same occupancy). send rows of source s start at s * T * R.
-__device__ __forceinline__ void pack_stores(const RowRegs<kRowV>& r, uint8_t* dst0,
-                                            const int32_t* sp, int R, int64_t TR, int64_t row,
-                                            int base, int n16) {
+template <int V>
+__device__ __forceinline__ void pack_stores(const RowRegs<V>& r, uint8_t* dst0, const int32_t* sp,
+                                            int R, int64_t TR, int64_t row, int base, int n16) {
   for (int k = 0; k < R; ++k) {
     const int p = sp[k];
     if (p < 0 || p >= TR) continue;
     store_row16(r, (u32x4*)(dst0 + (size_t)p * row), base, n16);
+  }
+}
+
+// One plane of the token pair tok0, tok0 + 1 (the second may not exist).
+template <int V>
+__device__ __forceinline__ void pack_plane(const uint8_t* x, uint8_t* send,
+                                           const int32_t* __restrict__ send_pos, int tok0,
+                                           bool two, int T, int R, int64_t row) {
+  const int64_t TR = (int64_t)T * R;
+  const int n16 = (int)(row >> 4);
+  for (int base = 0; base < n16; base += kWave * V) {
+    RowRegs<V> r0, r1;
+    load_row16(r0, (const u32x4*)(x + (size_t)tok0 * row), base, n16);
+    if (two) load_row16(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), base, n16);
+    pack_stores(r0, send + (size_t)(tok0 / T) * TR * row, send_pos + (size_t)tok0 * R, R, TR,
+                row, base, n16);
+    if (two)
+      pack_stores(r1, send + (size_t)((tok0 + 1) / T) * TR * row,
+                  send_pos + (size_t)(tok0 + 1) * R, R, TR, row, base, n16);
   }
 }
 
@@ -71,16 +104,12 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(Planes pl, const int32_t* 
     const int64_t row = pl.row[q];
     if ((row & 15) == 0) {
       const int n16 = (int)(row >> 4);
-      for (int base = 0; base < n16; base += kWave * kRowV) {
-        RowRegs<kRowV> r0, r1;
-        load_row16(r0, (const u32x4*)(pl.src[q] + (size_t)tok0 * row), base, n16);
-        if (two) load_row16(r1, (const u32x4*)(pl.src[q] + (size_t)(tok0 + 1) * row), base, n16);
-        pack_stores(r0, pl.dst[q] + (size_t)(tok0 / T) * TR * row, send_pos + (size_t)tok0 * R,
-                    R, TR, row, base, n16);
-        if (two)
-          pack_stores(r1, pl.dst[q] + (size_t)((tok0 + 1) / T) * TR * row,
-                      send_pos + (size_t)(tok0 + 1) * R, R, TR, row, base, n16);
-      }
+      if (n16 > kWave * 7)
+        pack_plane<kRowV>(pl.src[q], pl.dst[q], send_pos, tok0, two, T, R, row);
+      else if (n16 > kWave)
+        pack_plane<7>(pl.src[q], pl.dst[q], send_pos, tok0, two, T, R, row);
+      else
+        pack_plane<1>(pl.src[q], pl.dst[q], send_pos, tok0, two, T, R, row);
     } else {
       for (int u = 0; u < (two ? 2 : 1); ++u) {
         const int tok = tok0 + u;
