@@ -82,6 +82,10 @@ int derive(const ep_desc* d, ep::Dims* o) {
   }
   const int64_t nch = (o->TR + ep::kPlanChunk - 1) / ep::kPlanChunk;
   o->nchunks = (int)(nch > 0 ? nch : 1);
+  // Copy kernels launch one wave per 7 KB row segment.
+  const int64_t segs = (o->row[0] + 7167) / 7168;
+  if (NTR * segs >= kMaxWaves)
+    return fail(EP_ERR_UNSUPPORTED, "rows x row segments must be < 2^26");
   return EP_OK;
 }
 
@@ -337,7 +341,7 @@ int ep_combine(const ep_desc* d, const uint16_t* expert_out, const float* weight
 
 int ep_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   if (bytes % 16 != 0) return fail(EP_ERR_INVALID_ARG, "bytes must be a multiple of 16");
-  if (bytes / 16 >= (size_t)kMaxWaves * 64 * 14)
+  if (bytes / 16 >= (size_t)kMaxWaves * 64 * 7)
     return fail(EP_ERR_UNSUPPORTED, "copy too large");
   DeviceScope scope(stream);
   if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");

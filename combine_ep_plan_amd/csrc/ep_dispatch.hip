@@ -7,10 +7,13 @@
 // receive buffer into the grouped-GEMM input; within a node, buffers mapped
 // into the peers let a rank pull tokens directly.
 //
-// All kernels move whole rows as opaque bytes. One wave owns one row: lane l
-// moves 16-byte chunks l, l+64, ..., and every chunk of the row is loaded
-// before the first store, so a 14 KB bf16 row (H = 7168) is one round trip.
-// Row indices are wave-uniform and live in scalar registers.
+// All kernels move rows as opaque bytes, in segments of 448 16-byte chunks
+// (7 KB): one wave owns one segment of a row (a 14 KB bf16 row at H = 7168 is
+// two waves), lane l moves chunks l, l+64, ... of the segment, and all of a
+// segment's chunks are loaded before the first store. Measured on gfx950, a
+// plain copy runs at 6.4 TB/s with 7 KB per wave against 5.8 TB/s with 14 KB
+// per wave (more waves resident at fewer registers each). Row indices are
+// wave-uniform and live in scalar registers.
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 
@@ -19,7 +22,8 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWavesPerBlock * kWave;
-constexpr int kRowV = 14;  // 16-byte chunks per lane per pass: 14 KB per wave
+constexpr int kSegV = 7;   // 16-byte chunks per lane in a row segment
+constexpr int kSeg = kWave * kSegV;  // 16-byte chunks per segment (7 KB)
 
 struct Planes {
   const uint8_t* src[2];
@@ -32,39 +36,38 @@ __device__ __forceinline__ int wave_index() {
   return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
 }
 
-// Copy one row of n16 16-byte chunks with the whole wave, V chunks per lane
-// per pass.
-template <int V>
-__device__ __forceinline__ void copy_row16(const uint8_t* src, uint8_t* dst, int n16) {
-  for (int base = 0; base < n16; base += kWave * V) {
-    RowRegs<V> r;
-    load_row16(r, (const u32x4*)src, base, n16);
-    store_row16(r, (u32x4*)dst, base, n16);
-  }
+// Segments a row of `row` bytes splits into (rows that are not a multiple
+// of 16 bytes are copied whole, 4 bytes per lane, by segment 0).
+__host__ __device__ __forceinline__ int row_segments(int64_t row) {
+  return (row & 15) == 0 ? (int)(((row >> 4) + kSeg - 1) / kSeg) : 1;
 }
 
-// Copy one row of `row` bytes (multiple of 4) with the whole wave. The
-// chunks per lane follow the row size (14 for a 14 KB bf16 row, 7 for a
-// 7 KB fp8 row, 1 for a scale row), so no wave issues store instructions
-// whose lanes would all be clamped duplicates.
-__device__ __forceinline__ void wave_copy_row(const uint8_t* src, uint8_t* dst, int64_t row) {
+// Copy segment `seg` of one row with the whole wave (7 chunks per lane, or 1
+// when the segment holds at most 64 chunks, so that no store instruction
+// carries only clamped duplicates).
+__device__ __forceinline__ void wave_copy_segment(const uint8_t* src, uint8_t* dst, int64_t row,
+                                                  int seg) {
   if ((row & 15) == 0) {
     const int n16 = (int)(row >> 4);
-    if (n16 > kWave * 7)
-      copy_row16<kRowV>(src, dst, n16);
-    else if (n16 > kWave)
-      copy_row16<7>(src, dst, n16);
-    else
-      copy_row16<1>(src, dst, n16);
-  } else {
+    const int base = seg * kSeg;
+    if (base >= n16) return;
+    if (n16 - base > kWave) {
+      RowRegs<kSegV> r;
+      load_row16(r, (const u32x4*)src, base, n16);
+      store_row16(r, (u32x4*)dst, base, n16);
+    } else {
+      RowRegs<1> r;
+      load_row16(r, (const u32x4*)src, base, n16);
+      store_row16(r, (u32x4*)dst, base, n16);
+    }
+  } else if (seg == 0) {
     copy_row4((const uint32_t*)src, (uint32_t*)dst, row >> 2);
   }
 }
 
-// Sender: one wave per pair of tokens. Both token rows are loaded (28 KB in
-// flight per wave), then each is written to its R send slots. Two tokens
-// per wave measured faster than one (more loads in flight per wave at the
-// same occupancy). send rows of source s start at s * T * R.
+// Sender: one wave per (pair of tokens, row segment). Both tokens' segments
+// are loaded (14 KB in flight per wave), then each is written to its R send
+// slots. send rows of source s start at s * T * R.
 template <int V>
 __device__ __forceinline__ void pack_stores(const RowRegs<V>& r, uint8_t* dst0, const int32_t* sp,
                                             int R, int64_t TR, int64_t row, int base, int n16) {
@@ -75,28 +78,27 @@ __device__ __forceinline__ void pack_stores(const RowRegs<V>& r, uint8_t* dst0, 
   }
 }
 
-// One plane of the token pair tok0, tok0 + 1 (the second may not exist).
 template <int V>
-__device__ __forceinline__ void pack_plane(const uint8_t* x, uint8_t* send,
-                                           const int32_t* __restrict__ send_pos, int tok0,
-                                           bool two, int T, int R, int64_t row) {
+__device__ __forceinline__ void pack_segment(const uint8_t* x, uint8_t* send,
+                                             const int32_t* __restrict__ send_pos, int tok0,
+                                             bool two, int T, int R, int64_t row, int base) {
   const int64_t TR = (int64_t)T * R;
   const int n16 = (int)(row >> 4);
-  for (int base = 0; base < n16; base += kWave * V) {
-    RowRegs<V> r0, r1;
-    load_row16(r0, (const u32x4*)(x + (size_t)tok0 * row), base, n16);
-    if (two) load_row16(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), base, n16);
-    pack_stores(r0, send + (size_t)(tok0 / T) * TR * row, send_pos + (size_t)tok0 * R, R, TR,
-                row, base, n16);
-    if (two)
-      pack_stores(r1, send + (size_t)((tok0 + 1) / T) * TR * row,
-                  send_pos + (size_t)(tok0 + 1) * R, R, TR, row, base, n16);
-  }
+  RowRegs<V> r0, r1;
+  load_row16(r0, (const u32x4*)(x + (size_t)tok0 * row), base, n16);
+  if (two) load_row16(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), base, n16);
+  pack_stores(r0, send + (size_t)(tok0 / T) * TR * row, send_pos + (size_t)tok0 * R, R, TR, row,
+              base, n16);
+  if (two)
+    pack_stores(r1, send + (size_t)((tok0 + 1) / T) * TR * row, send_pos + (size_t)(tok0 + 1) * R,
+                R, TR, row, base, n16);
 }
 
 __global__ __launch_bounds__(kBlock) void pack_kernel(Planes pl, const int32_t* __restrict__ send_pos,
-                                                      int NT, int T, int R) {
-  const int tok0 = 2 * wave_index();
+                                                      int NT, int T, int R, int wps) {
+  const int w = wave_index();
+  const int tok0 = 2 * (w / wps);
+  const int seg = w % wps;
   if (tok0 >= NT) return;
   const bool two = tok0 + 1 < NT;
   const int64_t TR = (int64_t)T * R;
@@ -104,13 +106,13 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(Planes pl, const int32_t* 
     const int64_t row = pl.row[q];
     if ((row & 15) == 0) {
       const int n16 = (int)(row >> 4);
-      if (n16 > kWave * 7)
-        pack_plane<kRowV>(pl.src[q], pl.dst[q], send_pos, tok0, two, T, R, row);
-      else if (n16 > kWave)
-        pack_plane<7>(pl.src[q], pl.dst[q], send_pos, tok0, two, T, R, row);
+      const int base = seg * kSeg;
+      if (base >= n16) continue;
+      if (n16 - base > kWave)
+        pack_segment<kSegV>(pl.src[q], pl.dst[q], send_pos, tok0, two, T, R, row, base);
       else
-        pack_plane<1>(pl.src[q], pl.dst[q], send_pos, tok0, two, T, R, row);
-    } else {
+        pack_segment<1>(pl.src[q], pl.dst[q], send_pos, tok0, two, T, R, row, base);
+    } else if (seg == 0) {
       for (int u = 0; u < (two ? 2 : 1); ++u) {
         const int tok = tok0 + u;
         const int32_t* sp = send_pos + (size_t)tok * R;
@@ -137,8 +139,10 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(Planes pl, const int32_t* 
 __global__ __launch_bounds__(kBlock) void recv_kernel(Planes pl, const int32_t* __restrict__ grp_slot,
                                                       const int32_t* __restrict__ send_pos,
                                                       const int32_t* __restrict__ comb_row,
-                                                      int NTR, int TR, int64_t rows_out) {
-  const int j = wave_index();
+                                                      int NTR, int TR, int64_t rows_out, int wps) {
+  const int w = wave_index();
+  const int j = w / wps;
+  const int seg = w % wps;
   if (j >= NTR) return;
   const int slot = grp_slot[j];
   if (slot < 0 || slot >= NTR) return;
@@ -148,7 +152,8 @@ __global__ __launch_bounds__(kBlock) void recv_kernel(Planes pl, const int32_t* 
   const int s = slot / TR;
   for (int q = 0; q < pl.planes; ++q) {
     const int64_t row = pl.row[q];
-    wave_copy_row(pl.src[q] + ((size_t)s * TR + p) * row, pl.dst[q] + (size_t)g * row, row);
+    wave_copy_segment(pl.src[q] + ((size_t)s * TR + p) * row, pl.dst[q] + (size_t)g * row, row,
+                      seg);
   }
 }
 
@@ -158,8 +163,10 @@ __global__ __launch_bounds__(kBlock) void recv_kernel(Planes pl, const int32_t* 
 __global__ __launch_bounds__(kBlock) void transfer_kernel(Planes pl, const int32_t* __restrict__ send_off,
                                                           const int32_t* __restrict__ recv_off,
                                                           int N, int E, int L, int64_t TR,
-                                                          int64_t cap) {
-  const int g = wave_index();
+                                                          int64_t cap, int wps) {
+  const int w = wave_index();
+  const int g = w / wps;
+  const int seg = w % wps;
   if (g >= (int64_t)N * TR) return;
   const int s = (int)(g / TR);
   const int i = (int)(g - (int64_t)s * TR);
@@ -175,8 +182,8 @@ __global__ __launch_bounds__(kBlock) void transfer_kernel(Planes pl, const int32
   if (r < 0 || r >= cap) return;
   for (int q = 0; q < pl.planes; ++q) {
     const int64_t row = pl.row[q];
-    wave_copy_row(pl.src[q] + ((size_t)s * TR + i) * row,
-                  pl.dst[q] + ((size_t)d * cap + r) * row, row);
+    wave_copy_segment(pl.src[q] + ((size_t)s * TR + i) * row,
+                      pl.dst[q] + ((size_t)d * cap + r) * row, row, seg);
   }
 }
 
@@ -188,9 +195,12 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(Planes pl, const int32_t
                                                         const int32_t* __restrict__ recv_off,
                                                         const int32_t* __restrict__ grp_off,
                                                         const int32_t* __restrict__ src_off,
-                                                        int N, int E, int L, int64_t cap) {
+                                                        int N, int E, int L, int64_t cap,
+                                                        int wps) {
   const int d = blockIdx.y;
-  const int r = wave_index();
+  const int w = wave_index();
+  const int r = w / wps;
+  const int seg = w % wps;
   const int32_t* ro = recv_off + (size_t)d * (N + 1);
   const int64_t lim = ro[N] < cap ? ro[N] : cap;
   if (r >= lim) return;
@@ -213,18 +223,19 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(Planes pl, const int32_t
   if (gpos < 0 || gpos >= cap) return;
   for (int q = 0; q < pl.planes; ++q) {
     const int64_t row = pl.row[q];
-    wave_copy_row(pl.src[q] + ((size_t)d * cap + r) * row,
-                  pl.dst[q] + ((size_t)d * cap + gpos) * row, row);
+    wave_copy_segment(pl.src[q] + ((size_t)d * cap + r) * row,
+                      pl.dst[q] + ((size_t)d * cap + gpos) * row, row, seg);
   }
 }
 
+// Plain copy with the same per-wave loop as the row copies (7 KB per wave).
 __global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4* src, u32x4* dst,
                                                             int64_t n16) {
-  const int64_t base = (int64_t)wave_index() * kWave * kRowV;
+  const int64_t base = (int64_t)wave_index() * kSeg;
   if (base >= n16) return;
   const int64_t left = n16 - base;
-  const int n = left < kWave * kRowV ? (int)left : kWave * kRowV;
-  RowRegs<kRowV> r;
+  const int n = left < kSeg ? (int)left : kSeg;
+  RowRegs<kSegV> r;
   load_row16(r, src + base, 0, n);
   store_row16(r, dst + base, 0, n);
 }
@@ -244,31 +255,41 @@ unsigned blocks_for(int64_t waves) {
   return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
+// Waves per row: enough segments for the largest plane.
+int waves_per_row(const Dims& d) {
+  int w = 1;
+  for (int q = 0; q < d.planes; ++q) w = row_segments(d.row[q]) > w ? row_segments(d.row[q]) : w;
+  return w;
+}
+
 }  // namespace
 
 hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
                        void* const send[2], hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_kernel, dim3(blocks_for((d.NT + 1) / 2)), dim3(kBlock), 0, stream,
-                     make_planes(d, x, send), p.send_pos, (int)d.NT, d.T, d.R);
+  const int wps = waves_per_row(d);
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks_for((d.NT + 1) / 2 * wps)), dim3(kBlock), 0, stream,
+                     make_planes(d, x, send), p.send_pos, (int)d.NT, d.T, d.R, wps);
   return hipGetLastError();
 }
 
 hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs& p,
                        void* const grouped[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
-  hipLaunchKernelGGL(recv_kernel, dim3(blocks_for(d.NTR)), dim3(kBlock), 0, stream,
+  const int wps = waves_per_row(d);
+  hipLaunchKernelGGL(recv_kernel, dim3(blocks_for(d.NTR * wps)), dim3(kBlock), 0, stream,
                      make_planes(d, send, grouped), p.grp_slot, p.send_pos, p.comb_row,
-                     (int)d.NTR, (int)d.TR, (int64_t)d.N * d.cap);
+                     (int)d.NTR, (int)d.TR, (int64_t)d.N * d.cap, wps);
   return hipGetLastError();
 }
 
 hipError_t launch_transfer(const Dims& d, const void* const send[2], const PlanPtrs& p,
                            void* const recv[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
-  hipLaunchKernelGGL(transfer_kernel, dim3(blocks_for(d.NTR)), dim3(kBlock), 0, stream,
+  const int wps = waves_per_row(d);
+  hipLaunchKernelGGL(transfer_kernel, dim3(blocks_for(d.NTR * wps)), dim3(kBlock), 0, stream,
                      make_planes(d, send, recv), p.send_off, p.recv_off, d.N, d.E, d.L, d.TR,
-                     d.cap);
+                     d.cap, wps);
   return hipGetLastError();
 }
 
@@ -276,16 +297,17 @@ hipError_t launch_unpack(const Dims& d, const void* const recv[2], const PlanPtr
                          void* const grouped[2], hipStream_t stream) {
   const int64_t rows = d.cap < d.NTR ? d.cap : d.NTR;  // no rank holds more
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(unpack_kernel, dim3(blocks_for(rows), d.N), dim3(kBlock), 0, stream,
+  const int wps = waves_per_row(d);
+  hipLaunchKernelGGL(unpack_kernel, dim3(blocks_for(rows * wps), d.N), dim3(kBlock), 0, stream,
                      make_planes(d, recv, grouped), p.send_off, p.recv_off, p.grp_off,
-                     p.src_off, d.N, d.E, d.L, d.cap);
+                     p.src_off, d.N, d.E, d.L, d.cap, wps);
   return hipGetLastError();
 }
 
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   const int64_t n16 = (int64_t)(bytes / 16);
   if (n16 == 0) return hipSuccess;
-  const int64_t waves = (n16 + kWave * kRowV - 1) / (kWave * kRowV);
+  const int64_t waves = (n16 + kSeg - 1) / kSeg;
   hipLaunchKernelGGL(probe_copy_kernel, dim3(blocks_for(waves)), dim3(kBlock), 0, stream,
                      (const u32x4*)src, (u32x4*)dst, n16);
   return hipGetLastError();
