@@ -7,7 +7,7 @@
 // ノード内の GPU 間通信: libfabric の shm と SAR" (sections 問題 and 直し方2),
 // a transfer thread that never selected its GPU silently fell back to a slow
 // path.
-#include "../../include/ep.h"
+#include "ep.h"
 
 #include <hip/hip_runtime.h>
 

@@ -42,11 +42,19 @@ __device__ __forceinline__ void fma_row(float (&acc)[V][8], const RowRegs<V>& r,
   }
 }
 
-__global__ __launch_bounds__(kBlock) void combine_kernel(const uint16_t* __restrict__ y,
-                                                         const float* __restrict__ w,
-                                                         const int32_t* __restrict__ comb_row,
-                                                         uint16_t* __restrict__ out, int NT,
-                                                         int R, int H, int64_t rows_in) {
+__device__ __forceinline__ void store_acc(float (&acc)[kCombV][8], u32x4* o, int base, int n16) {
+  RowRegs<kCombV> res;
+#pragma unroll
+  for (int i = 0; i < kCombV; ++i)
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      res.v[i][h] = f32_to_bf16_bits(acc[i][2 * h]) | (f32_to_bf16_bits(acc[i][2 * h + 1]) << 16);
+  store_row16(res, o, base, n16);
+}
+
+__global__ __launch_bounds__(kBlock) void combine_kernel(const uint16_t* y, const float* w,
+                                                         const int32_t* comb_row, uint16_t* out,
+                                                         int NT, int R, int H, int64_t rows_in) {
   const int wv = wave_index();
   const int tok = wv / kCombWaves;
   const int part = wv % kCombWaves;
@@ -63,26 +71,19 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint16_t* __restr
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
     for (int k0 = 0; k0 < R; k0 += kCombRows) {
-      // rows outside [0, rows_in) (dropped slots) contribute nothing
-      int r[kCombRows];
+      // Rows k0 .. k0 + kCombRows - 1: loads of all in flight, then the FMAs.
+      // Rows outside [0, rows_in) (dropped slots) contribute nothing.
       RowRegs<kCombV> v[kCombRows];
 #pragma unroll
-      for (int b = 0; b < kCombRows; ++b) {
-        r[b] = k0 + b < R ? rows[k0 + b] : -1;
-        if (r[b] >= rows_in) r[b] = -1;
-        if (r[b] >= 0) load_row16(v[b], ybase + (size_t)r[b] * n16, base, n16);
-      }
+      for (int b = 0; b < kCombRows; ++b)
+        if (k0 + b < R && rows[k0 + b] >= 0 && rows[k0 + b] < rows_in)
+          load_row16(v[b], ybase + (size_t)rows[k0 + b] * n16, base, n16);
 #pragma unroll
       for (int b = 0; b < kCombRows; ++b)
-        if (r[b] >= 0) fma_row(acc, v[b], wt[k0 + b]);
+        if (k0 + b < R && rows[k0 + b] >= 0 && rows[k0 + b] < rows_in)
+          fma_row(acc, v[b], wt[k0 + b]);
     }
-    RowRegs<kCombV> res;
-#pragma unroll
-    for (int i = 0; i < kCombV; ++i)
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        res.v[i][h] = f32_to_bf16_bits(acc[i][2 * h]) | (f32_to_bf16_bits(acc[i][2 * h + 1]) << 16);
-    store_row16(res, o, base, n16);
+    store_acc(acc, o, base, n16);
   }
 }
 
