@@ -61,6 +61,12 @@ def _declare(L: ctypes.CDLL) -> None:
     L.oracle_f32_to_bf16.restype = ctypes.c_uint16
     L.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
     L.oracle_e4m3_to_f32.restype = ctypes.c_float
+    L.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    L.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    L.oracle_quantize_b128.argtypes = [_I, _P, _P, _P]
+    L.oracle_quantize_b128.restype = None
+    L.oracle_dispatch_pack_quant.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
+    L.oracle_dispatch_pack_quant.restype = None
     L.oracle_recv_bound.argtypes = [_I, _I, _I, _I]
     L.oracle_recv_bound.restype = _I64
     L.oracle_plan.argtypes = [_I, _I, _I, _I, _I64] + [_P] * 8
@@ -110,6 +116,34 @@ def bf16_to_f32(b: int) -> float:
 
 def e4m3_to_f32(c: int) -> float:
     return float(lib().oracle_e4m3_to_f32(int(c)))
+
+
+def f32_to_e4m3(v: float) -> int:
+    return int(lib().oracle_f32_to_e4m3(float(v)))
+
+
+def quantize_b128(x_bf16: np.ndarray):
+    """bf16 rows [..., H] -> (e4m3 codes uint8 [..., H], scales fp32 [..., H/128])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    H = x.shape[-1]
+    rows = x.reshape(-1, H)
+    codes = np.zeros(rows.shape, np.uint8)
+    scales = np.zeros((rows.shape[0], H // 128), np.float32)
+    for i in range(rows.shape[0]):
+        lib().oracle_quantize_b128(H, _ptr(rows[i]), _ptr(codes[i]), _ptr(scales[i]))
+    return codes.reshape(x.shape), scales.reshape(*x.shape[:-1], H // 128)
+
+
+def dispatch_pack_quant(x_bf16: np.ndarray, p: dict):
+    """bf16 x [N, T, H] -> fp8 send planes (codes [N, T*R, H], scales [N, T*R, H/128])."""
+    N, T, H = x_bf16.shape
+    R = p["send_pos"].shape[2]
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    codes = np.zeros((N, T * R, H), np.uint8)
+    scales = np.zeros((N, T * R, H // 128), np.float32)
+    lib().oracle_dispatch_pack_quant(N, T, R, H, _ptr(x), _ptr(p["send_pos"]), _ptr(codes),
+                                     _ptr(scales))
+    return codes, scales
 
 
 def recv_bound(N: int, T: int, E: int, R: int) -> int:

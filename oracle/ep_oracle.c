@@ -116,6 +116,84 @@ float oracle_e4m3_to_f32(uint8_t c)
     return (float)(sign ? -v : v);
 }
 
+/* Nearest OCP e4m3fn value to v, ties to the even code; magnitudes beyond the
+ * largest finite value (448) saturate to it; NaN gives 0x7F. Written as a
+ * search over the 127 non-negative finite codes, which are ordered like
+ * their values. */
+uint8_t oracle_f32_to_e4m3(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    uint8_t best = 0;
+    double best_d = a;                 /* distance to code 0 (value 0) */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs((double)oracle_e4m3_to_f32((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) != 0)) {
+            best = (uint8_t)c;
+            best_d = d;
+        }
+    }
+    return sign | best;
+}
+
+/* Block-scaled fp8 ("Evaluation": block-scaled fp8 dispatch), for one row of
+ * H bf16 values: per block of 128, amax = max |x|, scale = amax / 448 in
+ * float (1 when amax is 0), code = e4m3(x / scale) with the quotient formed
+ * in float and clamped to +-448. codes: H bytes; scales: H/128 floats. */
+void oracle_quantize_b128(int H, const uint16_t *x, uint8_t *codes, float *scales)
+{
+    for (int b = 0; b < H / 128; ++b) {
+        float amax = 0.0f;
+        for (int i = 0; i < 128; ++i) {
+            float a = fabsf(oracle_bf16_to_f32(x[b * 128 + i]));
+            if (a > amax)
+                amax = a;
+        }
+        float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scales[b] = scale;
+        for (int i = 0; i < 128; ++i) {
+            float q = oracle_bf16_to_f32(x[b * 128 + i]) / scale;
+            if (q > 448.0f)
+                q = 448.0f;
+            if (q < -448.0f)
+                q = -448.0f;
+            codes[b * 128 + i] = oracle_f32_to_e4m3(q);
+        }
+    }
+}
+
+/* Sender with the quantisation fused: the fp8 planes of token (s, t) go to
+ * its R send slots. x: bf16 [N][T][H]; codes: [N][T*R][H];
+ * scales: [N][T*R][H/128]. */
+void oracle_dispatch_pack_quant(int N, int T, int R, int H, const uint16_t *x,
+                                const int32_t *send_pos, uint8_t *codes,
+                                float *scales)
+{
+    uint8_t *qc = (uint8_t *)malloc((size_t)H);
+    float *qs = (float *)malloc((size_t)(H / 128) * sizeof(float));
+    if (!qc || !qs) {
+        free(qc);
+        free(qs);
+        return;
+    }
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t) {
+            oracle_quantize_b128(H, x + ((size_t)s * T + t) * H, qc, qs);
+            for (int k = 0; k < R; ++k) {
+                int32_t p = send_pos[((size_t)s * T + t) * R + k];
+                if (p < 0)
+                    continue;
+                size_t row = (size_t)s * T * R + (size_t)p;
+                memcpy(codes + row * H, qc, (size_t)H);
+                memcpy(scales + row * (H / 128), qs, (size_t)(H / 128) * sizeof(float));
+            }
+        }
+    free(qc);
+    free(qs);
+}
+
 /* ---------------------------------------------------------------------- */
 /* Plan: counts, prefix sums, positions, exchange, receive offsets.         */
 /* ---------------------------------------------------------------------- */

@@ -24,6 +24,11 @@ float oracle_bf16_to_f32(uint16_t b);
 uint16_t oracle_f64_to_bf16(double v);
 uint16_t oracle_f32_to_bf16(float f);
 float oracle_e4m3_to_f32(uint8_t c);
+uint8_t oracle_f32_to_e4m3(float v);
+void oracle_quantize_b128(int H, const uint16_t *x, uint8_t *codes, float *scales);
+void oracle_dispatch_pack_quant(int N, int T, int R, int H, const uint16_t *x,
+                                const int32_t *send_pos, uint8_t *codes,
+                                float *scales);
 
 int64_t oracle_recv_bound(int N, int T, int E, int R);
 

@@ -52,6 +52,15 @@ MUTATIONS = {
     "dequant_block": ("float v = oracle_e4m3_to_f32(codes[h]) * scales[h / 128];",
                       "float v = oracle_e4m3_to_f32(codes[h]) * scales[h / 256];"),
     "bound_min": ("int64_t m = R > L ? R : L;", "int64_t m = R < L ? R : L;"),
+    "e4m3_ties_odd": ("(d == best_d && (c & 1) == 0 && (best & 1) != 0)",
+                      "(d == best_d && (c & 1) != 0 && (best & 1) == 0)"),
+    "e4m3_sign_dropped": ("    return sign | best;", "    return best;"),
+    "quant_scale_max": ("float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
+                        "float scale = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    "quant_zero_scale": ("float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
+                         "float scale = amax > 0.0f ? amax / 448.0f : 0.5f;"),
+    "quant_block_size": ("float a = fabsf(oracle_bf16_to_f32(x[b * 128 + i]));",
+                         "float a = fabsf(oracle_bf16_to_f32(x[b * 128 + (i & 63)]));"),
 }
 
 
@@ -75,6 +84,9 @@ def _pin_checks():
         pins.test_combine_exact_brute_force_scale_expert,
         pins.test_expert_dequant_matches_torch,
         pins.test_combine_token_rounds_once,
+        pins.test_f32_to_e4m3_matches_torch_including_ties,
+        pins.test_quantize_b128_matches_generator_quantiser,
+        pins.test_quantize_b128_roundtrip_error_bound,
     ]
 
 

@@ -424,3 +424,65 @@ def test_combine_skips_dropped_slots():
     x = W.bf16_bits_to_f32(wl.x_bf16[0, 0]).astype(np.float64)
     want = np.array([brute_bf16_round(Fraction(float(w)) * Fraction(float(v))) for v in x])
     np.testing.assert_array_equal(r["out"][0, 0], want)
+
+
+# ---------------------------------------------------------------------------
+# Block-fp8 quantisation (sender-side fp8 dispatch)
+# ---------------------------------------------------------------------------
+
+def _all_e4m3_values():
+    codes = np.arange(0x7F, dtype=np.uint8)                  # non-negative finite
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def test_f32_to_e4m3_matches_torch_including_ties():
+    vals = _all_e4m3_values().astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2                        # exact ties
+    eps = np.nextafter(mids.astype(np.float32), np.float32(np.inf)) - mids.astype(np.float32)
+    rng = np.random.default_rng(9)
+    probe = np.concatenate([
+        vals, mids, mids + 1e-7 * mids, mids - 1e-7 * mids,
+        rng.uniform(-448, 448, 20000), rng.uniform(-1, 1, 5000) * 2.0 ** -6,
+        [0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10],
+    ]).astype(np.float32)
+    probe = np.concatenate([probe, -probe])
+    want = torch.from_numpy(probe).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.f32_to_e4m3(float(v)) for v in probe], np.uint8)
+    np.testing.assert_array_equal(got, want)
+    assert oracle.f32_to_e4m3(1000.0) == 0x7E and oracle.f32_to_e4m3(-1e9) == 0xFE   # saturate
+    assert oracle.f32_to_e4m3(2.0 ** -10) == 0x00 and oracle.f32_to_e4m3(3 * 2.0 ** -10) == 0x02
+
+
+def test_quantize_b128_matches_generator_quantiser():
+    """The oracle's quantiser (search encoder) against the workload
+    generator's (torch cast), on random rows and hand-made edge blocks."""
+    rng = np.random.default_rng(10)
+    x = (rng.standard_normal((6, 512)) * rng.choice([1e-3, 1.0, 40.0], size=(6, 1))).astype(np.float32)
+    x[0, :128] = 0.0                                         # all-zero block: scale 1
+    x[1, 128:256] = 0.0
+    x[1, 200] = -3.0                                         # one non-zero value
+    x[2, 256:384] = -0.0                                     # negative zeros
+    xb = W.to_bf16_bits(x)
+    codes, scales = oracle.quantize_b128(xb)
+    gc, gs = W.quantize_fp8_b128(xb)
+    np.testing.assert_array_equal(scales, gs)
+    np.testing.assert_array_equal(codes, gc)
+    assert scales[0, 0] == 1.0 and (codes[0, :128] == 0).all()
+    assert codes[1, 200] == 0xFE                             # -448 after scaling by 3/448
+    assert (codes[2, 256:384] == 0x80).all()                 # -0 keeps its sign
+
+
+def test_quantize_b128_roundtrip_error_bound():
+    """Dequantised values stay within half an e4m3 ulp (2^-4 relative) of x
+    for normal codes, and within half the smallest subnormal step below."""
+    rng = np.random.default_rng(11)
+    xb = W.to_bf16_bits(rng.standard_normal((4, 1024)).astype(np.float32))
+    codes, scales = oracle.quantize_b128(xb)
+    x = W.bf16_bits_to_f32(xb).astype(np.float64)
+    deq = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    deq *= np.repeat(scales.astype(np.float64), 128, axis=-1)
+    q = np.abs(x) / np.repeat(scales.astype(np.float64), 128, axis=-1)
+    normal = q >= 2.0 ** -6
+    assert (np.abs(deq - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal] * (1 + 1e-6)).all()
+    sub = ~normal
+    assert (np.abs(deq - x)[sub] <= 2.0 ** -10 * np.repeat(scales, 128, axis=-1)[sub] * (1 + 1e-6)).all()
