@@ -26,18 +26,20 @@ METRIC = "µs per dispatch+combine and effective HBM GB/s (% of peak) on 1 MI355
 HBM_PEAK_GBPS = 8000.0
 
 
-def algorithmic_bytes(sh, row_d: int) -> dict:
+def algorithmic_bytes(sh, row_d: int, quant: bool) -> dict:
     """Bytes the method must move, per stage and per step.
 
     x read once, the send buffer written and read (the transfer is pulled by
     the receiver), the grouped layout written, the expert output read, the
-    combined tokens written, plus the routing ids and weights.
+    combined tokens written, plus the routing ids and weights. The
+    quantising sender reads the bf16 rows (2H bytes) instead of fp8 ones.
     """
     N, T, R, H = sh.n_ranks, sh.tokens, sh.topk, sh.hidden
     NT, NTR, row_c = N * T, N * T * R, 2 * H
+    row_x = 2 * H if quant else row_d
     stages = {
         "plan": 4 * NTR,                                  # routing ids
-        "pack": NT * row_d + NTR * row_d,                 # read x, write send
+        "pack": NT * row_x + NTR * row_d,                 # read x, write send
         "recv": 2 * NTR * row_d,                          # read send, write grouped
         "combine": NTR * row_c + NT * row_c + 4 * NTR,    # read y and weights, write out
     }
@@ -73,13 +75,20 @@ def recorded_traffic(workload: str, kernel: str):
     return None if k is None else k["traffic_bytes"]
 
 
-def cpu_baseline(sh, wl, budget_s: float) -> dict:
-    """The oracle as it stands, single thread, on the same workload."""
+def cpu_baseline(sh, wl, budget_s: float, quant: bool) -> dict:
+    """The oracle as it stands, single thread, on the same workload.
+
+    With the quantising sender the oracle's quantiser (an exhaustive nearest
+    code search per value) runs on the first `quant_ranks` source ranks only
+    and its time is scaled by N / quant_ranks; the rest of the step runs on
+    the whole workload.
+    """
     import numpy as np
     import oracle
 
     N, T, E, R, H = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk, sh.hidden
     cap = oracle.recv_bound(N, T, E, R)
+    quant_ranks = min(N, 2)
     times = []
     t_begin = time.perf_counter()
     while True:
@@ -87,19 +96,33 @@ def cpu_baseline(sh, wl, budget_s: float) -> dict:
         p = oracle.plan(N, T, E, R, cap, wl.idx)
         totals = p["recv_off"][:, N]
         rows = int(min(cap, int(totals.max())))
-        send = [oracle.dispatch_pack(pl, p) for pl in wl.planes]
+        t_plan = time.perf_counter() - t0
+        if quant:
+            tq0 = time.perf_counter()
+            oracle.dispatch_pack_quant(wl.x_bf16[:quant_ranks],
+                                       {"send_pos": p["send_pos"][:quant_ranks]})
+            t_pack = (time.perf_counter() - tq0) * N / quant_ranks
+            # the full-size send planes from the pre-quantised rows (the same
+            # bytes); this copy is not timed
+            send = [oracle.dispatch_pack(pl, p) for pl in wl.planes]
+        else:
+            tp0 = time.perf_counter()
+            send = [oracle.dispatch_pack(pl, p) for pl in wl.planes]
+            t_pack = time.perf_counter() - tp0
+        tr0 = time.perf_counter()
         recv = [oracle.transfer(s, p, rows) for s in send]
         grouped = [oracle.unpack(r, p, rows) for r in recv]
-        t1 = time.perf_counter()
+        t_recv = time.perf_counter() - tr0
         y = oracle.expert_op(grouped, p, H, sh.payload, wl.alpha)   # stand-in, not timed
-        t2 = time.perf_counter()
+        tc0 = time.perf_counter()
         out = oracle.combine(y, wl.weights, wl.idx, p)
-        t3 = time.perf_counter()
-        times.append((t1 - t0) + (t3 - t2))
+        t_comb = time.perf_counter() - tc0
+        times.append(t_plan + t_pack + t_recv + t_comb)
         del send, recv, grouped, y, out
         if time.perf_counter() - t_begin >= budget_s or len(times) >= 5:
             break
-    return {"seconds": times, "median_s": statistics.median(times), "runs": len(times)}
+    return {"seconds": times, "median_s": statistics.median(times), "runs": len(times),
+            "quant_ranks": quant_ranks if quant else None}
 
 
 def main() -> int:
@@ -110,6 +133,9 @@ def main() -> int:
     ap.add_argument("--config", default="decode")
     ap.add_argument("--sample-every", type=int, default=10,
                     help="record per-stage events on every n-th timed step")
+    ap.add_argument("--prequantized", action="store_true",
+                    help="fp8 payloads: send pre-quantised rows with the plain sender "
+                         "instead of quantising bf16 rows in the sender")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0 = skip)")
     args = ap.parse_args()
@@ -134,13 +160,21 @@ def main() -> int:
     for q, plane in enumerate(wl.planes):
         b.x[q].copy_(torch.from_numpy(plane))
     alpha = torch.from_numpy(wl.alpha).cuda() if wl.alpha is not None else None
+    quant = sh.payload == W.PAYLOAD_FP8_B128 and not args.prequantized
+    x_bf16 = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda() if quant else None
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     row_d = sum(ep.row_bytes(d, q) for q in range(ep.num_planes(d)))
 
+    def pack():
+        if quant:
+            ep.dispatch_pack_quant(d, x_bf16, b.plan_ws, b.send, sp)
+        else:
+            ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)
+
     # expert outputs once (outside timing)
     ep.plan(d, b.idx, b.plan_ws, b.status, sp)
-    ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)
+    pack()
     ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp)
     ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out, sp)
     torch.cuda.synchronize()
@@ -154,7 +188,7 @@ def main() -> int:
         ep.plan(d, b.idx, b.plan_ws, b.status, sp)
         if ev is not None:
             ev[1].record(stream)
-        ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)
+        pack()
         if ev is not None:
             ev[2].record(stream)
         ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp)
@@ -189,10 +223,10 @@ def main() -> int:
         steps_ms.append(ev[0].elapsed_time(ev[4]))
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    ab = algorithmic_bytes(sh, row_d)
+    ab = algorithmic_bytes(sh, row_d, quant)
     eff = ab["step"] / (ms_per_step * 1e-3) / 1e9
 
-    # the dominant kernel: the receiver (largest algorithmic bytes)
+    # the dominant kernel: the stage with the largest algorithmic bytes
     dom = max(ab["stages"], key=lambda k: ab["stages"][k])
     dom_ms = statistics.mean(per[dom])
     achieved = ab["stages"][dom] / (dom_ms * 1e-3) / 1e9
@@ -214,18 +248,28 @@ def main() -> int:
 
     cpu = None
     if args.cpu_budget > 0:
-        base = cpu_baseline(sh, wl, args.cpu_budget)
+        base = cpu_baseline(sh, wl, args.cpu_budget, quant)
+        sample = (f"the whole {sh.name} workload, {base['runs']} run(s) of the plain-C "
+                  f"oracle (plan, pack, per-pair transfer, unpack, combine; stand-in "
+                  f"expert not timed), median {base['median_s']:.3f} s")
+        if quant:
+            sample += (f"; the quantising sender timed on {base['quant_ranks']} of "
+                       f"{sh.n_ranks} source ranks and scaled")
         cpu = {
             "value": ab["step"] / base["median_s"] / 1e9,
             "unit": "GB/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": (f"the whole {sh.name} workload, {base['runs']} run(s) of the plain-C "
-                       f"oracle (plan, pack, per-pair transfer, unpack, combine; stand-in "
-                       f"expert not timed), median {base['median_s']:.3f} s"),
+            "sample": sample,
             "us_per_step": base["median_s"] * 1e6,
         }
 
+    if sh.payload == W.PAYLOAD_BF16:
+        payload_name = "bf16"
+    elif quant:
+        payload_name = "fp8 e4m3 + fp32 scale per 128 values, quantised in the sender"
+    else:
+        payload_name = "fp8 e4m3 + fp32 scale per 128 values, pre-quantised"
     res = {
         "metric": METRIC,
         "value": round(eff, 2),
@@ -242,8 +286,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": (f"{sh.name}: N={sh.n_ranks} virtual ranks, T={sh.tokens} tokens/rank, "
-                         f"H={sh.hidden} bf16, E={sh.n_experts} experts, top-{sh.topk} "
-                         f"{sh.routing} routing, softmax weights, expert = per-expert scale"),
+                         f"H={sh.hidden} bf16 tokens, dispatch payload {payload_name}, "
+                         f"E={sh.n_experts} experts, top-{sh.topk} {sh.routing} routing, "
+                         f"softmax weights, stand-in expert = {sh.expert}"),
             "parallelism": "ep (virtual ranks on one GPU)",
             "global_batch": sh.n_ranks * sh.tokens,
         },

@@ -30,7 +30,7 @@ EP_PAYLOAD_FP8_B128 = 1
 # Every entry point the C header declares (checked by the tests).
 EXPORTS = (
     "ep_recv_bound", "ep_capacity", "ep_num_planes", "ep_row_bytes",
-    "ep_plan_bytes", "ep_plan_views", "ep_plan", "ep_dispatch_pack",
+    "ep_plan_bytes", "ep_plan_views", "ep_plan", "ep_dispatch_pack", "ep_dispatch_pack_quant",
     "ep_dispatch_transfer", "ep_dispatch_unpack", "ep_dispatch_recv",
     "ep_expert_stub", "ep_combine", "ep_probe_copy", "ep_status_string",
     "ep_last_error",
@@ -79,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "ep_plan_views": (ctypes.c_int, [D, P, ctypes.POINTER(PlanView)]),
         "ep_plan": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_pack": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_dispatch_pack_quant": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_transfer": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_unpack": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_recv": (ctypes.c_int, [D, P, P, P, P]),
@@ -185,6 +186,11 @@ def plan(d: Desc, topk_idx, plan_ws, status, stream=None) -> None:
 def dispatch_pack(d: Desc, x: Sequence, plan_ws, send: Sequence, stream=None) -> None:
     _check(_lib.ep_dispatch_pack(ctypes.byref(d), _planes(x), _addr(plan_ws), _planes(send),
                                  _stream(stream)), "ep_dispatch_pack")
+
+
+def dispatch_pack_quant(d: Desc, x_bf16, plan_ws, send: Sequence, stream=None) -> None:
+    _check(_lib.ep_dispatch_pack_quant(ctypes.byref(d), _addr(x_bf16), _addr(plan_ws), _planes(send),
+                                       _stream(stream)), "ep_dispatch_pack_quant")
 
 
 def dispatch_transfer(d: Desc, send: Sequence, plan_ws, recv: Sequence, stream=None) -> None:

@@ -283,6 +283,18 @@ int ep_dispatch_pack(const ep_desc* d, const void* const x[2], const void* plan_
   return EP_OK;
 }
 
+int ep_dispatch_pack_quant(const ep_desc* d, const uint16_t* x, const void* plan_ws,
+                           void* const send[2], hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  if (dims.payload != EP_PAYLOAD_FP8_B128)
+    return fail(EP_ERR_INVALID_ARG, "ep_dispatch_pack_quant needs the fp8 payload descriptor");
+  EP_CHECK(check_ptr(x, scope.device(), "x", dims.NT * 2 * (int64_t)dims.H));
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  const hipError_t e = ep::launch_pack_quant(dims, x, pp, send, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_pack_quant");
+  return EP_OK;
+}
+
 int ep_dispatch_transfer(const ep_desc* d, const void* const send[2], const void* plan_ws,
                          void* const recv[2], hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);

@@ -34,6 +34,8 @@ hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                        int32_t* status, hipStream_t stream);
 hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
                        void* const send[2], hipStream_t stream);
+hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p,
+                             void* const send[2], hipStream_t stream);
 hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs& p,
                        void* const grouped[2], hipStream_t stream);
 hipError_t launch_transfer(const Dims& d, const void* const send[2], const PlanPtrs& p,

@@ -1,0 +1,132 @@
+// Dispatch sender with block-fp8 quantisation fused in.
+//
+// Method: "Enabling trillion-parameter models on AWS EFA", section
+// "Evaluation": dispatch moves block-scaled fp8 rows (the DeepSeek-V3 /
+// Kimi-K2 setting), combine moves bf16. Here the sender reads each bf16 token
+// row once, quantises it per block of 128 values (scale = amax / 448, codes =
+// OCP e4m3fn of x / scale, nearest even, clamped to +-448) and writes the code
+// and scale rows to the token's R send slots, so the send buffer holds half
+// the bytes of a bf16 dispatch.
+//
+// One wave per token. Lane l holds 16-byte chunks l, l+64, ... (8 bf16 each);
+// the 16 lanes l = 16g .. 16g+15 of one pass step hold one 128-value block,
+// so the block's amax is a 16-lane xor-shuffle reduction. Scale and quotient
+// are IEEE fp32 divisions (the same operations a CPU reference performs), so
+// the integer codes are decided in the same precision everywhere.
+#include "ep_device.hpp"
+#include "ep_kernels.hpp"
+
+namespace ep {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWavesPerBlock * kWave;
+constexpr int kQV = 14;                  // chunks of 8 bf16 per lane per pass
+constexpr int kQPass = kWave * kQV;      // 896 chunks = 7168 values per pass
+constexpr int kQBlocks = kQPass / 16;    // 56 scale blocks per pass
+
+__device__ __forceinline__ int wave_index() {
+  return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+}
+
+// OCP e4m3fn code of q (|q| <= 448), round to nearest, ties to even. For
+// |q| >= 2^-6 with 2^E <= |q| < 2^(E+1): N = rne(|q| * 2^(3-E)) in [8, 16],
+// code = (E + 6) * 8 + N (N = 16 carries into the next exponent). Below 2^-6
+// (subnormals): code = rne(|q| * 2^9) in [0, 8]. Both scalings are by powers
+// of two, so exact.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
+  const uint32_t bits = __float_as_uint(q);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = __uint_as_float(bits & 0x7fffffffu);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const int E = (int)((bits >> 23) & 0xffu) - 127;
+    const float scaled = a * __uint_as_float((uint32_t)(127 + 3 - E) << 23);
+    code = (uint32_t)((E + 6) * 8) + (uint32_t)__builtin_rintf(scaled);
+  }
+  return sign | code;
+}
+
+__global__ __launch_bounds__(kBlock) void pack_quant_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
+    const int32_t* __restrict__ send_pos, int NT, int T, int R, int H) {
+  const int tok = wave_index();
+  if (tok >= NT) return;
+  const int lane = lane_id();
+  const int n16 = H / 8;
+  const int nblk = H / 128;
+  const int TR = T * R;
+  const int s = tok / T;
+  const u32x4* src = (const u32x4*)(x + (size_t)tok * H);
+  for (int base = 0; base < n16; base += kQPass) {
+    RowRegs<kQV> r;
+    load_row16(r, src, base, n16);
+    uint32_t packed[kQV][2];
+    float sc[kQV];
+#pragma unroll
+    for (int i = 0; i < kQV; ++i) {
+      float v[8];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v[2 * h] = bf16_lo(r.v[i][h]);
+        v[2 * h + 1] = bf16_hi(r.v[i][h]);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+      const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+      sc[i] = scale;
+      uint32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float q = v[j] / scale;
+        q = fminf(fmaxf(q, -448.0f), 448.0f);
+        c[j] = f32_to_e4m3(q);
+      }
+      packed[i][0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      packed[i][1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    }
+    // Lane b < 56 collects the scale of block b of this pass: block b was
+    // computed in step b / 4 by lane group b % 4.
+    float my_scale = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kQV; ++i) {
+      const float t = __shfl(sc[i], 16 * (lane % 4));
+      if (lane / 4 == i) my_scale = t;
+    }
+    const int blk0 = base / 16;
+    const int pass_blocks = nblk - blk0 < kQBlocks ? nblk - blk0 : kQBlocks;
+    for (int k = 0; k < R; ++k) {
+      const int p = send_pos[(size_t)tok * R + k];
+      if (p < 0 || p >= TR) continue;
+      const size_t row = (size_t)s * TR + p;
+      uint64_t* crow = (uint64_t*)(codes + row * H);  // 8 codes per chunk
+#pragma unroll
+      for (int i = 0; i < kQV; ++i) {
+        const int c = base + lane + kWave * i;
+        if (c < n16)
+          __builtin_nontemporal_store((uint64_t)packed[i][0] | ((uint64_t)packed[i][1] << 32),
+                                      &crow[c]);
+      }
+      if (lane < pass_blocks)
+        __builtin_nontemporal_store(my_scale, &scales[row * nblk + blk0 + lane]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p,
+                             void* const send[2], hipStream_t stream) {
+  if (d.NT == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_quant_kernel, dim3((unsigned)((d.NT + kWavesPerBlock - 1) / kWavesPerBlock)),
+                     dim3(kBlock), 0, stream, x, (uint8_t*)send[0], (float*)send[1], p.send_pos,
+                     (int)d.NT, d.T, d.R, d.H);
+  return hipGetLastError();
+}
+
+}  // namespace ep

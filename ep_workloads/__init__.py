@@ -63,6 +63,10 @@ CONFIGS = {
     # as "decode shapes" rather than "tiny shapes".
     "decode_zipf": Shape("decode_zipf", 32, 128, 7168, 256, 8,
                          routing="zipf", expert="scale"),
+    # Decode shapes with the block-scaled fp8 dispatch of the evaluation
+    # setting (quantised by the sender, dequantised by the stand-in expert).
+    "decode_fp8": Shape("decode_fp8", 32, 128, 7168, 256, 8,
+                        payload=PAYLOAD_FP8_B128, expert="dequant"),
 }
 
 

@@ -164,6 +164,19 @@ EP_API int ep_dispatch_pack(const ep_desc *d, const void *const x[2],
                      const void *plan_ws, void *const send[2],
                      hipStream_t stream);
 
+/* Dispatch sender with block-fp8 quantisation fused in ("Evaluation":
+ * block-scaled fp8 dispatch, bf16 combine). x: bf16 [N][T][H]; the
+ * descriptor's payload must be EP_PAYLOAD_FP8_B128. Each token row is read
+ * once and quantised per block of 128 values: scale = amax / 448 as a float
+ * division (1 when amax is 0), code = OCP e4m3fn of x / scale (float
+ * division), nearest even, clamped to +-448. send[0] (codes, [N][T*R][H])
+ * and send[1] (fp32 scales, [N][T*R][H/128]) receive the token's planes at
+ * each of its R send positions, exactly as ep_dispatch_pack would place a
+ * pre-quantised row. */
+EP_API int ep_dispatch_pack_quant(const ep_desc *d, const uint16_t *x,
+                                  const void *plan_ws, void *const send[2],
+                                  hipStream_t stream);
+
 /* The network write, materialised: for every pair (s, d) one bulk copy of
  * s's segment for d into d's receive buffer at recv_off[d][s].
  * recv[p] is [N][cap][row_p]; rows at or beyond cap are dropped. */

@@ -1,0 +1,143 @@
+"""Sender with fused block-fp8 quantisation, against the CPU oracle.
+
+Codes and scales are integers and fp32 values decided by IEEE fp32
+divisions on both sides, so the send planes must match bit for bit; the
+rest of the fp8 path (receive, dequantising expert, combine) follows the
+parity bar of the bf16 path.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_plan_amd as ep
+import ep_workloads as W
+import oracle
+from gpu_util import bf16_close, desc_of, note, plan_arrays, rows_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu_memory():
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _run_quant_path(sh, wl, cap=0):
+    d = desc_of(sh, cap)
+    b = ep.Buffers(d)
+    b.idx.copy_(torch.from_numpy(wl.idx))
+    b.weights.copy_(torch.from_numpy(wl.weights))
+    x = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda()
+    b.status.zero_()
+    ep.plan(d, b.idx, b.plan_ws, b.status)
+    ep.dispatch_pack_quant(d, x, b.plan_ws, b.send)
+    ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped)
+    ep.expert_stub(d, b.grouped, None, b.plan_ws, b.expert_out)
+    ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out)
+    torch.cuda.synchronize()
+    return d, b, x
+
+
+QUANT_SHAPES = [
+    W.Shape("q_tiny", 4, 16, 256, 16, 2, payload=W.PAYLOAD_FP8_B128, expert="dequant"),
+    W.Shape("q_ragged_pass", 3, 9, 7296, 6, 2, payload=W.PAYLOAD_FP8_B128, expert="dequant", seed=4),
+    W.Shape("q_zipf", 8, 24, 1024, 32, 4, routing="zipf", payload=W.PAYLOAD_FP8_B128,
+            expert="dequant", seed=5),
+    W.Shape("q_rank0", 8, 8, 512, 32, 8, routing="rank0", payload=W.PAYLOAD_FP8_B128,
+            expert="dequant", seed=6),
+]
+
+
+@pytest.mark.parametrize("sh", QUANT_SHAPES, ids=[s.name for s in QUANT_SHAPES])
+def test_pack_quant_and_fp8_path_full(sh):
+    wl = W.make_workload(sh)
+    # planes the oracle's own quantiser produces from the bf16 rows
+    codes, scales = oracle.quantize_b128(wl.x_bf16)
+    wl.planes = [codes, scales.view(np.uint8)]
+    note(f"quant full {sh.name} N={sh.n_ranks} T={sh.tokens} H={sh.hidden} R={sh.topk}")
+    d, b, _ = _run_quant_path(sh, wl)
+    ref = oracle.run(wl, cap=ep.capacity(d))
+    p = ref["plan"]
+    assert int(b.status.item()) == p["status"] == 0
+    oc, osc = oracle.dispatch_pack_quant(wl.x_bf16, p)
+    np.testing.assert_array_equal(b.send[0].cpu().numpy(), oc)
+    np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.float32), osc)
+    np.testing.assert_array_equal(oc, ref["send"][0])     # fused == quantise, then pack
+    N = sh.n_ranks
+    totals = p["recv_off"][:, N]
+    y = b.expert_out.cpu().numpy().view(np.uint16)
+    for dd in range(N):
+        n = int(totals[dd])
+        np.testing.assert_array_equal(y[dd, :n], ref["y"][dd, :n])
+    out = b.out.cpu().numpy().view(np.uint16)
+    assert bf16_close(out, ref["out"]).all()
+
+
+def test_pack_quant_zero_and_signed_blocks():
+    sh = W.Shape("q_edges", 2, 4, 384, 4, 2, payload=W.PAYLOAD_FP8_B128, expert="dequant", seed=7)
+    wl = W.make_workload(sh)
+    x = W.bf16_bits_to_f32(wl.x_bf16).copy()
+    x[0, 0, :128] = 0.0                  # all-zero block: scale 1, codes 0
+    x[0, 1, 128:256] = -0.0              # negative zeros keep their sign
+    x[1, 2, 256:384] = 0.0
+    x[1, 2, 300] = 1e-30                 # one tiny value: the whole block scales to it
+    x[1, 3, :128] = 448.0                # saturating magnitudes
+    x[0, 2, 128:256] *= 1e-37            # subnormal fp32 scale (amax / 448 < 2^-126)
+    wl.x_bf16 = W.to_bf16_bits(x)
+    codes, scales = oracle.quantize_b128(wl.x_bf16)
+    wl.planes = [codes, scales.view(np.uint8)]
+    d, b, _ = _run_quant_path(sh, wl)
+    p = oracle.plan(2, 4, 4, 2, ep.capacity(d), wl.idx)
+    oc, osc = oracle.dispatch_pack_quant(wl.x_bf16, p)
+    np.testing.assert_array_equal(b.send[0].cpu().numpy(), oc)
+    np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.float32), osc)
+
+
+def test_pack_quant_rejects_bf16_descriptor():
+    sh = W.CONFIGS["tiny"]
+    d = desc_of(sh)
+    b = ep.Buffers(d)
+    x = torch.zeros((4, 16, 256), dtype=torch.int16, device="cuda")
+    with pytest.raises(ep.EPError) as e:
+        ep.dispatch_pack_quant(d, x, b.plan_ws, b.send)
+    assert e.value.code == ep.EP_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["decode_fp8", "prefill"])
+def test_pack_quant_full_size(name):
+    """Every send row of the fused sender equals the plain sender's row for
+    the pre-quantised planes (whole tensors, on the device); sampled rows
+    equal the oracle's quantiser; sampled tokens combine like the oracle."""
+    sh = W.CONFIGS[name]
+    wl = W.make_workload(sh)
+    N, T, H, R = sh.n_ranks, sh.tokens, sh.hidden, sh.topk
+    note(f"quant full-size {name}")
+    d, b, x = _run_quant_path(sh, wl)
+    assert int(b.status.item()) == 0
+    q_codes = b.send[0].clone()
+    q_scales = b.send[1].clone()
+    for q, plane in enumerate(wl.planes):
+        b.x[q].copy_(torch.from_numpy(plane))
+    ep.dispatch_pack(d, b.x, b.plan_ws, b.send)
+    torch.cuda.synchronize()
+    assert torch.equal(q_codes, b.send[0])
+    assert torch.equal(q_scales, b.send[1])
+    p = plan_arrays(d, b)
+    rng = np.random.default_rng(3)
+    toks = rng.choice(N * T, size=64, replace=False)
+    s, t = np.unravel_index(toks, (N, T))
+    oc, osc = oracle.quantize_b128(wl.x_bf16[s, t])
+    k = rng.integers(0, R, size=len(toks))
+    sp = p["send_pos"][s, t, k]
+    np.testing.assert_array_equal(rows_of(q_codes, s, sp), oc)
+    np.testing.assert_array_equal(rows_of(q_scales, s, sp).view(np.float32), osc)
+    out = rows_of(b.out, s, t).view(np.uint16)
+    for i in range(len(toks)):
+        row = [oc[i], osc[i].view(np.uint8)]
+        ys = [oracle.expert_row(row, int(e), 1, H, None) for e in wl.idx[s[i], t[i]]]
+        want = oracle.combine_token(wl.weights[s[i], t[i]], ys)
+        assert bf16_close(out[i], want).all()
