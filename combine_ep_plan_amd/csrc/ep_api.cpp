@@ -288,6 +288,9 @@ int ep_dispatch_pack_quant(const ep_desc* d, const uint16_t* x, const void* plan
   EP_PROLOGUE(d, stream, plan_ws);
   if (dims.payload != EP_PAYLOAD_FP8_B128)
     return fail(EP_ERR_INVALID_ARG, "ep_dispatch_pack_quant needs the fp8 payload descriptor");
+  // one wave per 1024-value segment of a token row
+  if (dims.NT * (((int64_t)dims.H + 1023) / 1024) >= kMaxWaves)
+    return fail(EP_ERR_UNSUPPORTED, "tokens x 1024-value row segments must be < 2^26");
   EP_CHECK(check_ptr(x, scope.device(), "x", dims.NT * 2 * (int64_t)dims.H));
   EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
   const hipError_t e = ep::launch_pack_quant(dims, x, pp, send, stream);

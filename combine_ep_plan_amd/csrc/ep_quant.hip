@@ -8,9 +8,10 @@
 // and scale rows to the token's R send slots, so the send buffer holds half
 // the bytes of a bf16 dispatch.
 //
-// One wave per token. Lane l holds 16-byte chunks l, l+64, ... (8 bf16 each);
-// the 16 lanes l = 16g .. 16g+15 of one pass step hold one 128-value block,
-// so the block's amax is a 16-lane xor-shuffle reduction. Scale and quotient
+// One wave per 1024-value segment of a token row. Lane l holds 16-byte chunks
+// l and l+64 of the segment (8 bf16 each); the 16 lanes 16g .. 16g+15 of one
+// step hold one 128-value block, so the block's amax is a 16-lane
+// xor-shuffle reduction. Scale and quotient
 // are IEEE fp32 divisions (the same operations a CPU reference performs), so
 // the integer codes are decided in the same precision everywhere.
 #include "ep_device.hpp"
@@ -21,9 +22,13 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWavesPerBlock * kWave;
-constexpr int kQV = 14;                  // chunks of 8 bf16 per lane per pass
-constexpr int kQPass = kWave * kQV;      // 896 chunks = 7168 values per pass
-constexpr int kQBlocks = kQPass / 16;    // 56 scale blocks per pass
+// Segment per wave: 2 chunks of 8 bf16 per lane, 128 chunks = 1024 values =
+// 8 scale blocks. Small segments keep the kernel at ~40 VGPRs, so 8 waves per
+// SIMD overlap one wave's loads with another's R-fold stores; one wave per
+// whole 7168-value token (256 VGPRs, one wave per SIMD) ran 1.5x slower.
+constexpr int kQV = 2;
+constexpr int kQSeg = kWave * kQV;
+constexpr int kQBlocks = kQSeg / 16;
 
 __device__ __forceinline__ int wave_index() {
   return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
@@ -51,70 +56,70 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
 
 __global__ __launch_bounds__(kBlock) void pack_quant_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
-    const int32_t* __restrict__ send_pos, int NT, int T, int R, int H) {
-  const int tok = wave_index();
+    const int32_t* __restrict__ send_pos, int NT, int T, int R, int H, int nseg) {
+  const int w = wave_index();
+  const int tok = w / nseg;
   if (tok >= NT) return;
   const int lane = lane_id();
   const int n16 = H / 8;
   const int nblk = H / 128;
   const int TR = T * R;
   const int s = tok / T;
+  const int base = (w - tok * nseg) * kQSeg;
   const u32x4* src = (const u32x4*)(x + (size_t)tok * H);
-  for (int base = 0; base < n16; base += kQPass) {
-    RowRegs<kQV> r;
-    load_row16(r, src, base, n16);
-    uint32_t packed[kQV][2];
-    float sc[kQV];
+  RowRegs<kQV> r;
+  load_row16(r, src, base, n16);
+  uint32_t packed[kQV][2];
+  float sc[kQV];
+#pragma unroll
+  for (int i = 0; i < kQV; ++i) {
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[2 * h] = bf16_lo(r.v[i][h]);
+      v[2 * h + 1] = bf16_hi(r.v[i][h]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    sc[i] = scale;
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float q = v[j] / scale;
+      q = fminf(fmaxf(q, -448.0f), 448.0f);
+      c[j] = f32_to_e4m3(q);
+    }
+    packed[i][0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    packed[i][1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  }
+  // Lane b < kQBlocks collects the scale of block b of this segment: block b
+  // was computed in step b / 4 by lane group b % 4.
+  float my_scale = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kQV; ++i) {
+    const float t = __shfl(sc[i], 16 * (lane % 4));
+    if (lane / 4 == i) my_scale = t;
+  }
+  const int blk0 = base / 16;
+  const int seg_blocks = nblk - blk0 < kQBlocks ? nblk - blk0 : kQBlocks;
+  for (int k = 0; k < R; ++k) {
+    const int p = send_pos[(size_t)tok * R + k];
+    if (p < 0 || p >= TR) continue;
+    const size_t row = (size_t)s * TR + p;
+    uint64_t* crow = (uint64_t*)(codes + row * H);  // 8 codes per chunk
 #pragma unroll
     for (int i = 0; i < kQV; ++i) {
-      float v[8];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        v[2 * h] = bf16_lo(r.v[i][h]);
-        v[2 * h + 1] = bf16_hi(r.v[i][h]);
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-      const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-      sc[i] = scale;
-      uint32_t c[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float q = v[j] / scale;
-        q = fminf(fmaxf(q, -448.0f), 448.0f);
-        c[j] = f32_to_e4m3(q);
-      }
-      packed[i][0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      packed[i][1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      const int c = base + lane + kWave * i;
+      if (c < n16)
+        __builtin_nontemporal_store((uint64_t)packed[i][0] | ((uint64_t)packed[i][1] << 32),
+                                    &crow[c]);
     }
-    // Lane b < 56 collects the scale of block b of this pass: block b was
-    // computed in step b / 4 by lane group b % 4.
-    float my_scale = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kQV; ++i) {
-      const float t = __shfl(sc[i], 16 * (lane % 4));
-      if (lane / 4 == i) my_scale = t;
-    }
-    const int blk0 = base / 16;
-    const int pass_blocks = nblk - blk0 < kQBlocks ? nblk - blk0 : kQBlocks;
-    for (int k = 0; k < R; ++k) {
-      const int p = send_pos[(size_t)tok * R + k];
-      if (p < 0 || p >= TR) continue;
-      const size_t row = (size_t)s * TR + p;
-      uint64_t* crow = (uint64_t*)(codes + row * H);  // 8 codes per chunk
-#pragma unroll
-      for (int i = 0; i < kQV; ++i) {
-        const int c = base + lane + kWave * i;
-        if (c < n16)
-          __builtin_nontemporal_store((uint64_t)packed[i][0] | ((uint64_t)packed[i][1] << 32),
-                                      &crow[c]);
-      }
-      if (lane < pass_blocks)
-        __builtin_nontemporal_store(my_scale, &scales[row * nblk + blk0 + lane]);
-    }
+    if (lane < seg_blocks)
+      __builtin_nontemporal_store(my_scale, &scales[row * nblk + blk0 + lane]);
   }
 }
 
@@ -123,9 +128,11 @@ __global__ __launch_bounds__(kBlock) void pack_quant_kernel(
 hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p,
                              void* const send[2], hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_quant_kernel, dim3((unsigned)((d.NT + kWavesPerBlock - 1) / kWavesPerBlock)),
+  const int nseg = (d.H / 8 + kQSeg - 1) / kQSeg;
+  const int64_t waves = d.NT * nseg;
+  hipLaunchKernelGGL(pack_quant_kernel, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                      dim3(kBlock), 0, stream, x, (uint8_t*)send[0], (float*)send[1], p.send_pos,
-                     (int)d.NT, d.T, d.R, d.H);
+                     (int)d.NT, d.T, d.R, d.H, nseg);
   return hipGetLastError();
 }
 
