@@ -125,6 +125,109 @@ def cpu_baseline(sh, wl, budget_s: float, quant: bool) -> dict:
             "quant_ranks": quant_ranks if quant else None}
 
 
+def measure_split(ep, torch, d, b, sh, P: int, steps: int, warmup: int) -> dict:
+    """The split dispatch (sender half, receiver half with private regions of
+    P rows) + combine, and its overlap with independent work: a stand-in for
+    a shared expert (two bf16 GEMMs, H -> 2048 -> H, over all N*T tokens,
+    random weights) on a second stream."""
+    import statistics as st
+
+    priv = ep.priv_buffers(d, P) if P > 0 else []
+    sa = torch.cuda.current_stream()
+    sb = torch.cuda.Stream()
+    spa = sa.cuda_stream
+
+    def send():
+        ep.dispatch_send(d, b.idx, b.x, b.plan_ws, b.send, priv, P, b.status, spa)
+
+    def recv():
+        ep.dispatch_recv_split(d, b.send, priv, P, b.plan_ws, b.grouped, b.status, spa)
+
+    def comb():
+        ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, spa)
+
+    NT, H = sh.n_ranks * sh.tokens, sh.hidden
+    g = torch.Generator(device="cuda").manual_seed(1)
+    xs = torch.randn(NT, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    w1 = torch.randn(H, 2048, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02
+    w2 = torch.randn(2048, H, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02
+
+    def gemm():
+        return torch.mm(torch.mm(xs, w1), w2)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        out = []
+        for _ in range(reps):
+            e0.record(sa)
+            fn()
+            e1.record(sa)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3)
+        return st.median(out)
+
+    def split_step():
+        send()
+        recv()
+        comb()
+
+    def sequential():
+        send()
+        gemm()
+        recv()
+        comb()
+
+    def overlapped():
+        # the GEMM starts with the sender half on the second stream; the
+        # step ends when both streams are done
+        start = torch.cuda.Event()
+        start.record(sa)
+        sb.wait_event(start)
+        with torch.cuda.stream(sb):
+            gemm()
+        split_step()
+        done = torch.cuda.Event()
+        done.record(sb)
+        sa.wait_event(done)
+
+    for fn in (split_step, gemm, sequential, overlapped):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stages = {"send": [], "recv": [], "combine": []}
+    for _ in range(max(steps // 10, 3)):
+        ev[0].record(sa)
+        send()
+        ev[1].record(sa)
+        recv()
+        ev[2].record(sa)
+        comb()
+        ev[3].record(sa)
+        torch.cuda.synchronize()
+        for j, n in enumerate(stages):
+            stages[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(sa)
+    for _ in range(steps):
+        split_step()
+    e1.record(sa)
+    torch.cuda.synchronize()
+    reps = max(steps // 5, 5)
+    t_gemm = timed(gemm, reps)
+    t_seq = timed(sequential, reps)
+    t_ovl = timed(overlapped, reps)
+    return {
+        "priv_rows": P,
+        "us_per_dispatch_combine": round(e0.elapsed_time(e1) / steps * 1e3, 2),
+        "stages_us": {n: round(st.mean(v), 2) for n, v in stages.items()},
+        "shared_expert_stand_in": f"bf16 GEMMs [{NT},{H}]x[{H},2048] then x[2048,{H}]",
+        "shared_expert_us": round(t_gemm, 2),
+        "sequential_us": round(t_seq, 2),
+        "overlapped_us": round(t_ovl, 2),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +239,10 @@ def main() -> int:
     ap.add_argument("--prequantized", action="store_true",
                     help="fp8 payloads: send pre-quantised rows with the plain sender "
                          "instead of quantising bf16 rows in the sender")
+    ap.add_argument("--split", type=int, default=-1, metavar="P",
+                    help="also measure the split dispatch with P private rows per "
+                         "(destination, source) pair, alone and overlapped with a "
+                         "shared-expert stand-in on a second stream")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0 = skip)")
     args = ap.parse_args()
@@ -246,6 +353,10 @@ def main() -> int:
     copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    split = None
+    if args.split >= 0:
+        split = measure_split(ep, torch, d, b, sh, args.split, args.steps, args.warmup)
+
     cpu = None
     if args.cpu_budget > 0:
         base = cpu_baseline(sh, wl, args.cpu_budget, quant)
@@ -315,6 +426,8 @@ def main() -> int:
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }
+    if split is not None:
+        res["split"] = split
     print(json.dumps(res), flush=True)
     return 0
 

@@ -32,7 +32,7 @@ EXPORTS = (
     "ep_recv_bound", "ep_capacity", "ep_num_planes", "ep_row_bytes",
     "ep_plan_bytes", "ep_plan_views", "ep_plan", "ep_dispatch_pack", "ep_dispatch_pack_quant",
     "ep_dispatch_transfer", "ep_dispatch_unpack", "ep_dispatch_recv",
-    "ep_expert_stub", "ep_combine", "ep_probe_copy", "ep_status_string",
+    "ep_dispatch_send", "ep_dispatch_recv_split", "ep_expert_stub", "ep_combine", "ep_probe_copy", "ep_status_string",
     "ep_last_error",
 )
 
@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
         "ep_dispatch_transfer": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_unpack": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_recv": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_dispatch_send": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_int32, P, P]),
+        "ep_dispatch_recv_split": (ctypes.c_int, [D, P, P, ctypes.c_int32, P, P, P, P]),
         "ep_expert_stub": (ctypes.c_int, [D, P, P, P, P, P]),
         "ep_combine": (ctypes.c_int, [D, P, P, P, P, P]),
         "ep_probe_copy": (ctypes.c_int, [P, P, ctypes.c_size_t, P]),
@@ -206,6 +208,28 @@ def dispatch_unpack(d: Desc, recv: Sequence, plan_ws, grouped: Sequence, stream=
 def dispatch_recv(d: Desc, send: Sequence, plan_ws, grouped: Sequence, stream=None) -> None:
     _check(_lib.ep_dispatch_recv(ctypes.byref(d), _planes(send), _addr(plan_ws),
                                  _planes(grouped), _stream(stream)), "ep_dispatch_recv")
+
+
+def dispatch_send(d: Desc, topk_idx, x: Sequence, plan_ws, send: Sequence, priv: Sequence,
+                  priv_rows: int, status, stream=None) -> None:
+    _check(_lib.ep_dispatch_send(ctypes.byref(d), _addr(topk_idx), _planes(x), _addr(plan_ws),
+                                 _planes(send), _planes(priv), int(priv_rows), _addr(status),
+                                 _stream(stream)), "ep_dispatch_send")
+
+
+def dispatch_recv_split(d: Desc, send: Sequence, priv: Sequence, priv_rows: int, plan_ws,
+                        grouped: Sequence, status, stream=None) -> None:
+    _check(_lib.ep_dispatch_recv_split(ctypes.byref(d), _planes(send), _planes(priv),
+                                       int(priv_rows), _addr(plan_ws), _planes(grouped),
+                                       _addr(status), _stream(stream)), "ep_dispatch_recv_split")
+
+
+def priv_buffers(d: Desc, priv_rows: int, device="cuda") -> list:
+    """Private regions of a split dispatch: per plane [N][N][P][row_p] bytes."""
+    import torch
+    N = d.n_ranks
+    return [torch.empty((N, N, priv_rows, row_bytes(d, p)), dtype=torch.uint8, device=device)
+            for p in range(num_planes(d))]
 
 
 def expert_stub(d: Desc, grouped: Sequence, alpha, plan_ws, expert_out, stream=None) -> None:

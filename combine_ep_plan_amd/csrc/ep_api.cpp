@@ -328,6 +328,43 @@ int ep_dispatch_recv(const ep_desc* d, const void* const send[2], const void* pl
   return EP_OK;
 }
 
+// Private regions: P rows per (destination, source) pair, P in [0, T R].
+int check_priv(const ep::Dims& d, void* const priv[2], int32_t P, int dev) {
+  if (P < 0 || P > d.TR) return fail(EP_ERR_INVALID_ARG, "priv_rows must be in [0, tokens * topk]");
+  if (P == 0) return EP_OK;
+  return check_planes(d, (const void* const*)priv, dev, "priv", (int64_t)d.N * d.N * P);
+}
+
+int ep_dispatch_send(const ep_desc* d, const int32_t* topk_idx, const void* const x[2],
+                     void* plan_ws, void* const send[2], void* const priv[2], int32_t priv_rows,
+                     int32_t* status, hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_ptr(status, scope.device(), "status"));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  EP_CHECK(check_planes(dims, (const void* const*)x, scope.device(), "x", dims.NT));
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
+  hipError_t e = ep::launch_plan_local(dims, topk_idx, pp, status, stream);
+  if (e == hipSuccess)
+    e = ep::launch_pack_split(dims, topk_idx, x, pp, send, priv, priv_rows, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_send");
+  return EP_OK;
+}
+
+int ep_dispatch_recv_split(const ep_desc* d, const void* const send[2], void* const priv[2],
+                           int32_t priv_rows, void* plan_ws, void* const grouped[2],
+                           int32_t* status, hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_ptr(status, scope.device(), "status"));
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
+  EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
+  hipError_t e = ep::launch_plan_exchange(dims, pp, status, stream);
+  if (e == hipSuccess) e = ep::launch_recv_split(dims, send, priv, priv_rows, pp, grouped, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_recv_split");
+  return EP_OK;
+}
+
 int ep_expert_stub(const ep_desc* d, const void* const grouped[2], const float* alpha,
                    const void* plan_ws, uint16_t* expert_out, hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);

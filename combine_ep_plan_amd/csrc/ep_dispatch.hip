@@ -189,6 +189,112 @@ int pass_v(int64_t row) {
   return 0;
 }
 
+// Split dispatch. Rows of the segment s -> d (the rows source s sends to the
+// experts of rank d) with index i < P inside the segment live in d's
+// private region for s, priv[(d * N + s) * P + i]; the others in the send
+// buffer. Source s's segment for d starts at send_off[s][d L].
+struct Split {
+  uint8_t* priv[2];
+  const int32_t* send_off;
+  int N, E, L, P;
+};
+
+__device__ __forceinline__ uint8_t* split_row(const Split& sp, int q, uint8_t* send, int s, int d,
+                                              int p, int TR, size_t row) {
+  const int i = p - sp.send_off[(size_t)s * (sp.E + 1) + d * sp.L];
+  if (i >= 0 && i < sp.P) return sp.priv[q] + (((size_t)d * sp.N + s) * sp.P + i) * row;
+  return send + ((size_t)s * TR + p) * row;
+}
+
+// Sender half of a split dispatch: as pack_kernel, with each slot's row
+// sent to the private region of its destination when it is among the
+// first P rows of its segment.
+template <int V>
+__device__ __forceinline__ void pack_split_plane(const uint8_t* x, uint8_t* send, const Split& sp,
+                                                 int q, const int32_t* __restrict__ idx,
+                                                 const int32_t* __restrict__ send_pos, int tok0,
+                                                 bool two, int T, int R, size_t row) {
+  const int TR = T * R;
+  const int n16 = (int)(row >> 4);
+  for (int base = 0; base < n16; base += kWave * V) {
+    RowRegs<V> r0, r1;
+    load_row16(r0, (const u32x4*)(x + (size_t)tok0 * row), base, n16);
+    if (two) load_row16(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), base, n16);
+    for (int u = 0; u < (two ? 2 : 1); ++u) {
+      const int tok = tok0 + u;
+      const int s = tok / T;
+      for (int k = 0; k < R; ++k) {
+        const int p = send_pos[(size_t)tok * R + k];
+        const int e = idx[(size_t)tok * R + k];
+        if (p < 0 || p >= TR || e < 0 || e >= sp.E) continue;
+        store_row16(u ? r1 : r0, (u32x4*)split_row(sp, q, send, s, e / sp.L, p, TR, row), base,
+                    n16);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void pack_split_kernel(Planes pl, Split sp,
+                                                            const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ send_pos,
+                                                            int NT, int T, int R) {
+  const int tok0 = 2 * wave_index();
+  if (tok0 >= NT) return;
+  const bool two = tok0 + 1 < NT;
+  const int TR = T * R;
+  for (int q = 0; q < pl.planes; ++q) {
+    const size_t row = (size_t)pl.row[q];
+    if ((row & 15) == 0) {
+      const int n16 = (int)(row >> 4);
+      if (n16 > kSeg)
+        pack_split_plane<2 * kSegV>(pl.src[q], pl.dst[q], sp, q, idx, send_pos, tok0, two, T, R,
+                                    row);
+      else if (n16 > kWave)
+        pack_split_plane<kSegV>(pl.src[q], pl.dst[q], sp, q, idx, send_pos, tok0, two, T, R, row);
+      else
+        pack_split_plane<1>(pl.src[q], pl.dst[q], sp, q, idx, send_pos, tok0, two, T, R, row);
+    } else {
+      for (int u = 0; u < (two ? 2 : 1); ++u) {
+        const int tok = tok0 + u;
+        for (int k = 0; k < R; ++k) {
+          const int p = send_pos[(size_t)tok * R + k];
+          const int e = idx[(size_t)tok * R + k];
+          if (p < 0 || p >= TR || e < 0 || e >= sp.E) continue;
+          copy_row4((const uint32_t*)(pl.src[q] + (size_t)tok * row),
+                    (uint32_t*)split_row(sp, q, pl.dst[q], tok / T, e / sp.L, p, TR, row),
+                    (int64_t)(row >> 2));
+        }
+      }
+    }
+  }
+}
+
+// Receiver half of a split dispatch: recv_kernel, reading each row from
+// the private region or the send buffer, wherever the sender put it.
+__global__ __launch_bounds__(kBlock) void recv_split_kernel(Planes pl, Split sp,
+                                                            const int32_t* __restrict__ grp_slot,
+                                                            const int32_t* __restrict__ send_pos,
+                                                            const int32_t* __restrict__ comb_row,
+                                                            int NTR, int TR, int64_t cap,
+                                                            int wps) {
+  const int w = wave_index();
+  const int j = w / wps;
+  const int seg = w % wps;
+  if (j >= NTR) return;
+  const int slot = grp_slot[j];
+  if (slot < 0 || slot >= NTR) return;
+  const int p = send_pos[slot];
+  const int g = comb_row[slot];
+  if (p < 0 || p >= TR || g < 0 || g >= (int64_t)sp.N * cap) return;
+  const int s = slot / TR;
+  const int d = (int)(g / cap);
+  for (int q = 0; q < pl.planes; ++q) {
+    const int64_t row = pl.row[q];
+    wave_copy_segment(split_row(sp, q, (uint8_t*)pl.src[q], s, d, p, TR, (size_t)row),
+                      pl.dst[q] + (size_t)g * row, row, seg);
+  }
+}
+
 // Receiver with the transfer fused in: wave j pulls the j-th row of the
 // receive order (grp_slot: each rank's grouped rows in turn) from its
 // source's send buffer into the grouped layout on its expert's rank
@@ -358,6 +464,37 @@ hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs&
   hipLaunchKernelGGL(recv_kernel, dim3(blocks_for(d.NTR * wps)), dim3(kBlock), 0, stream,
                      make_planes(d, send, grouped), p.grp_slot, p.send_pos, p.comb_row,
                      (int)d.NTR, (int)d.TR, (int64_t)d.N * d.cap, wps);
+  return hipGetLastError();
+}
+
+Split make_split(const Dims& d, void* const priv[2], int P, const PlanPtrs& p) {
+  Split sp{};
+  for (int q = 0; q < 2; ++q) sp.priv[q] = (P > 0 && q < d.planes) ? (uint8_t*)priv[q] : nullptr;
+  sp.send_off = p.send_off;
+  sp.N = d.N;
+  sp.E = d.E;
+  sp.L = d.L;
+  sp.P = P;
+  return sp;
+}
+
+hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* const x[2],
+                             const PlanPtrs& p, void* const send[2], void* const priv[2], int P,
+                             hipStream_t stream) {
+  if (d.NT == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_split_kernel, dim3(blocks_for((d.NT + 1) / 2)), dim3(kBlock), 0, stream,
+                     make_planes(d, x, send), make_split(d, priv, P, p), idx, p.send_pos,
+                     (int)d.NT, d.T, d.R);
+  return hipGetLastError();
+}
+
+hipError_t launch_recv_split(const Dims& d, const void* const send[2], void* const priv[2], int P,
+                             const PlanPtrs& p, void* const grouped[2], hipStream_t stream) {
+  if (d.NTR == 0) return hipSuccess;
+  const int wps = waves_per_row(d);
+  hipLaunchKernelGGL(recv_split_kernel, dim3(blocks_for(d.NTR * wps)), dim3(kBlock), 0, stream,
+                     make_planes(d, send, grouped), make_split(d, priv, P, p), p.grp_slot,
+                     p.send_pos, p.comb_row, (int)d.NTR, (int)d.TR, d.cap, wps);
   return hipGetLastError();
 }
 

@@ -32,6 +32,18 @@ constexpr int kPlanChunk = kPlanThreads * kPlanSub;      // slots per block
 
 hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                        int32_t* status, hipStream_t stream);
+// Split dispatch: the sender half's plan (no data of other ranks), the
+// receiver half's exchange, and the two data movers with private regions of
+// P rows per (destination, source) pair.
+hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
+                             int32_t* status, hipStream_t stream);
+hipError_t launch_plan_exchange(const Dims& d, const PlanPtrs& p, int32_t* status,
+                                hipStream_t stream);
+hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* const x[2],
+                             const PlanPtrs& p, void* const send[2], void* const priv[2], int P,
+                             hipStream_t stream);
+hipError_t launch_recv_split(const Dims& d, const void* const send[2], void* const priv[2], int P,
+                             const PlanPtrs& p, void* const grouped[2], hipStream_t stream);
 hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
                        void* const send[2], hipStream_t stream);
 hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p,

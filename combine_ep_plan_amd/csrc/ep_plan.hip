@@ -128,60 +128,44 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(
   if (bad) atomicOr(status, kStatusBadExpert);
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
-    const int32_t* __restrict__ idx, int N, int E, int L, int64_t TR, int nchunks,
-    int64_t cap, PlanPtrs p, int32_t* __restrict__ status) {
-  extern __shared__ int32_t lds[];
-  int32_t* soff = lds;               // [E+1] counts of s -> send offsets
-  int32_t* pre = soff + (E + 1);     // [E]   rows of s in earlier chunks
-  int32_t* sro = pre + E;            // [E]   rows earlier sources send to e
-  int32_t* sros = sro + E;           // [E+1] prefix of sro over experts
-  int32_t* gsc = sros + (E + 1);     // [E+1] prefix of column totals
-  int32_t* dstart = gsc + (E + 1);   // [N+1] first receive-order row of rank d
-  int32_t* scratch = dstart + (N + 1);  // [kPlanThreads / 64], then partial sums
-  const int s = blockIdx.y;
-  const int c = blockIdx.x;
+// Fetch this block's slots: expert ids and the per-slot value the previous
+// launch left in send_pos (a rank inside the chunk, or a final position).
+__device__ __forceinline__ void fetch_slots(const int32_t* __restrict__ idx,
+                                            const int32_t* __restrict__ send_pos, int s, int c,
+                                            int64_t TR, int* e_of, int* v_of) {
   const int tid = threadIdx.x;
-
-  // This block's slots: expert ids and the ranks left by the count kernel,
-  // fetched first so that their latency overlaps the exchange below.
-  const int32_t* src = idx + (size_t)s * TR;
-  int e_of[kPlanSub], rank_of[kPlanSub];
 #pragma unroll
   for (int sub = 0; sub < kPlanSub; ++sub) {
     const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * kPlanThreads + tid;
     e_of[sub] = -1;
-    rank_of[sub] = 0;
+    v_of[sub] = -1;
     if (i < TR) {
-      e_of[sub] = src[i];
-      rank_of[sub] = p.send_pos[(size_t)s * TR + i];
+      e_of[sub] = idx != nullptr ? idx[(size_t)s * TR + i] : 0;
+      v_of[sub] = send_pos[(size_t)s * TR + i];
     }
   }
+}
 
-  // The exchange: every block reads the counts of all sources. The column
-  // sums over sources are split across G thread groups (sources s2 = g,
-  // g + G, ...) so that all threads issue loads, then reduced through LDS.
+// The exchange: column sums over all sources of the per-expert counts. The
+// sources are split across G thread groups (s2 = g, g + G, ...) so that all
+// threads issue loads, then reduced through LDS. `count(s2, e)` is the
+// count of expert e at source s2. On return (synced): gsc[e] = rows all
+// sources send to e and sro[e], sros[e] = rows sources before s send to e.
+template <typename Count>
+__device__ __forceinline__ void column_sums(Count count, int N, int E, int s, int32_t* sro,
+                                            int32_t* sros, int32_t* gsc, int32_t* part) {
+  const int tid = threadIdx.x;
   const int G = E >= kPlanThreads ? 1 : kPlanThreads / E;
-  int32_t* part_total = scratch + kPlanThreads / kWave;  // [G][E]
-  int32_t* part_before = part_total + G * E;             // [G][E]
+  int32_t* part_total = part;            // [G][E]
+  int32_t* part_before = part + G * E;   // [G][E]
   for (int q = tid; q < G * E; q += kPlanThreads) {
     const int g = q / E, e = q % E;
     int total = 0, before = 0;
 #pragma unroll 4
     for (int s2 = g; s2 < N; s2 += G) {
-      const int32_t* cc = p.chunk_cnt + (size_t)s2 * nchunks * E + e;
-      int sum = 0, part = 0;
-      for (int c2 = 0; c2 < nchunks; ++c2) {
-        const int v = cc[(size_t)c2 * E];
-        sum += v;
-        if (c2 < c) part += v;
-      }
-      total += sum;
-      if (s2 < s) before += sum;
-      if (s2 == s) {
-        soff[e] = sum;
-        pre[e] = part;
-      }
+      const int v = count(s2, e);
+      total += v;
+      if (s2 < s) before += v;
     }
     part_total[q] = total;
     part_before[q] = before;
@@ -198,13 +182,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
     gsc[e] = total;
   }
   __syncthreads();
-  if (c == 0) {
-    for (int e = tid; e < E; e += kPlanThreads) {
-      p.cnt[(size_t)s * E + e] = soff[e];
-      p.src_off[(size_t)s * E + e] = sro[e];
-    }
-  }
-  block_exclusive_scan(soff, E, scratch, &soff[E]);
+}
+
+// Receive side of the plan for the slots of block (c, s), from the sums of
+// column_sums. within_of[sub] is the slot's index among the rows that s
+// sends to its expert (negative: dropped slot). Writes src_off[s] and
+// recv_off[.][s] (block c == 0), grp_off, the receive totals and the
+// capacity flag (block (0, 0)), and grp_pos, comb_row and grp_slot of the
+// block's slots; then clears the receive-order entries past the last
+// delivered row (shared by all blocks).
+__device__ void receive_tables(const int* e_of, const int* within_of, int s, int c, int N, int E,
+                               int L, int64_t TR, int64_t cap, const PlanPtrs& p,
+                               int32_t* status, int32_t* sro, int32_t* sros, int32_t* gsc,
+                               int32_t* dstart, int32_t* scratch) {
+  const int tid = threadIdx.x;
+  if (c == 0)
+    for (int e = tid; e < E; e += kPlanThreads) p.src_off[(size_t)s * E + e] = sro[e];
   block_exclusive_scan(sros, E, scratch, &sros[E]);
   block_exclusive_scan(gsc, E, scratch, &gsc[E]);
   // Receive order: the delivered rows of rank 0, then rank 1, ...
@@ -216,7 +209,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
   block_exclusive_scan(dstart, N, scratch, &dstart[N]);
 
   if (c == 0) {
-    for (int e = tid; e <= E; e += kPlanThreads) p.send_off[(size_t)s * (E + 1) + e] = soff[e];
     // Rank d receives source s after the rows of sources 0..s-1.
     for (int d = tid; d < N; d += kPlanThreads)
       p.recv_off[(size_t)d * (N + 1) + s] = sros[(d + 1) * L] - sros[d * L];
@@ -233,21 +225,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
     }
   }
 
-  // Final positions of this block's slots.
 #pragma unroll
   for (int sub = 0; sub < kPlanSub; ++sub) {
     const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * kPlanThreads + tid;
     if (i >= TR) break;
     const size_t gi = (size_t)s * TR + i;
     const int e = e_of[sub];
-    if (e < 0 || e >= E) {
-      p.send_pos[gi] = -1;
+    const int within = within_of[sub];
+    if (e < 0 || e >= E || within < 0) {
       p.grp_pos[gi] = -1;
       p.comb_row[gi] = -1;
       continue;
     }
-    const int within = pre[e] + rank_of[sub];
-    p.send_pos[gi] = soff[e] + within;
     const int d = e / L;
     const int64_t g = (int64_t)(gsc[e] - gsc[d * L]) + sro[e] + within;
     if (g < cap) {
@@ -259,7 +248,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
       p.comb_row[gi] = -1;
     }
   }
-  // Receive-order entries past the last delivered row, shared by all blocks.
   const int64_t nblocks = (int64_t)gridDim.x * gridDim.y;
   const int64_t bl = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
   for (int64_t j = dstart[N] + bl * kPlanThreads + tid; j < (int64_t)N * TR;
@@ -267,33 +255,209 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
     p.grp_slot[j] = -1;
 }
 
+// Per-source sums of the chunk counts: soff[e] = rows of s to e, pre[e] =
+// rows of s to e in chunks before c.
+__device__ __forceinline__ void source_sums(const int32_t* __restrict__ chunk_cnt, int s, int c,
+                                            int E, int nchunks, int32_t* soff, int32_t* pre) {
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
+    const int32_t* cc = chunk_cnt + (size_t)s * nchunks * E + e;
+    int sum = 0, part = 0;
+    for (int c2 = 0; c2 < nchunks; ++c2) {
+      const int v = cc[(size_t)c2 * E];
+      sum += v;
+      if (c2 < c) part += v;
+    }
+    soff[e] = sum;
+    pre[e] = part;
+  }
+}
+
+// Send side of the plan for the slots of block (c, s): cnt[s] and
+// send_off[s] (block c == 0) and the final send positions. Returns each
+// slot's index among the rows s sends to its expert (-1 for a bad id).
+__device__ __forceinline__ void send_tables(const int* e_of, const int* rank_of, int s, int c,
+                                            int E, int64_t TR, const PlanPtrs& p, int32_t* soff,
+                                            const int32_t* pre, int32_t* scratch,
+                                            int* within_of) {
+  const int tid = threadIdx.x;
+  if (c == 0)
+    for (int e = tid; e < E; e += kPlanThreads) p.cnt[(size_t)s * E + e] = soff[e];
+  block_exclusive_scan(soff, E, scratch, &soff[E]);
+  if (c == 0)
+    for (int e = tid; e <= E; e += kPlanThreads) p.send_off[(size_t)s * (E + 1) + e] = soff[e];
+#pragma unroll
+  for (int sub = 0; sub < kPlanSub; ++sub) {
+    const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * kPlanThreads + tid;
+    within_of[sub] = -1;
+    if (i >= TR) continue;
+    const int e = e_of[sub];
+    if (e < 0 || e >= E) {
+      p.send_pos[(size_t)s * TR + i] = -1;
+      continue;
+    }
+    within_of[sub] = pre[e] + rank_of[sub];
+    p.send_pos[(size_t)s * TR + i] = soff[e] + within_of[sub];
+  }
+}
+
+// The whole plan after the count launch: every block does the exchange (a
+// redundant read of all sources' chunk counts), then both sides' tables.
+__global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
+    const int32_t* __restrict__ idx, int N, int E, int L, int64_t TR, int nchunks,
+    int64_t cap, PlanPtrs p, int32_t* __restrict__ status) {
+  extern __shared__ int32_t lds[];
+  int32_t* soff = lds;               // [E+1] counts of s -> send offsets
+  int32_t* pre = soff + (E + 1);     // [E]   rows of s in earlier chunks
+  int32_t* sro = pre + E;            // [E]   rows earlier sources send to e
+  int32_t* sros = sro + E;           // [E+1] prefix of sro over experts
+  int32_t* gsc = sros + (E + 1);     // [E+1] prefix of column totals
+  int32_t* dstart = gsc + (E + 1);   // [N+1] first receive-order row of rank d
+  int32_t* scratch = dstart + (N + 1);  // [kPlanThreads / 64], then partial sums
+  const int s = blockIdx.y;
+  const int c = blockIdx.x;
+
+  // Slots first, so that their latency overlaps the exchange.
+  int e_of[kPlanSub], rank_of[kPlanSub], within_of[kPlanSub];
+  fetch_slots(idx, p.send_pos, s, c, TR, e_of, rank_of);
+  const int32_t* cc = p.chunk_cnt;
+  column_sums(
+      [=](int s2, int e) {
+        int sum = 0;
+        for (int c2 = 0; c2 < nchunks; ++c2) sum += cc[((size_t)s2 * nchunks + c2) * E + e];
+        return sum;
+      },
+      N, E, s, sro, sros, gsc, scratch + kPlanThreads / kWave);
+  source_sums(p.chunk_cnt, s, c, E, nchunks, soff, pre);
+  __syncthreads();
+  send_tables(e_of, rank_of, s, c, E, TR, p, soff, pre, scratch, within_of);
+  receive_tables(e_of, within_of, s, c, N, E, L, TR, cap, p, status, sro, sros, gsc, dstart,
+                 scratch);
+}
+
+// Sender half of a split dispatch: the send side of the plan from the
+// source's own chunk counts only (no data of any other rank).
+__global__ __launch_bounds__(kPlanThreads) void plan_local_kernel(
+    const int32_t* __restrict__ idx, int E, int64_t TR, int nchunks, PlanPtrs p) {
+  extern __shared__ int32_t lds[];
+  int32_t* soff = lds;               // [E+1]
+  int32_t* pre = soff + (E + 1);     // [E]
+  int32_t* scratch = pre + E;        // [kPlanThreads / 64]
+  const int s = blockIdx.y;
+  const int c = blockIdx.x;
+  int e_of[kPlanSub], rank_of[kPlanSub], within_of[kPlanSub];
+  fetch_slots(idx, p.send_pos, s, c, TR, e_of, rank_of);
+  source_sums(p.chunk_cnt, s, c, E, nchunks, soff, pre);
+  __syncthreads();
+  send_tables(e_of, rank_of, s, c, E, TR, p, soff, pre, scratch, within_of);
+}
+
+// Receiver half of a split dispatch: the exchange reads the counts every
+// sender published (cnt rows) and the senders' own send offsets and
+// positions; each slot's expert is the segment of send_off[s] its position
+// falls in, so no routing ids are needed here.
+__global__ __launch_bounds__(kPlanThreads) void plan_exchange_kernel(
+    int N, int E, int L, int64_t TR, int64_t cap, PlanPtrs p, int32_t* __restrict__ status) {
+  extern __shared__ int32_t lds[];
+  int32_t* so = lds;                 // [E+1] send_off row of s
+  int32_t* sro = so + (E + 1);       // [E]
+  int32_t* sros = sro + E;           // [E+1]
+  int32_t* gsc = sros + (E + 1);     // [E+1]
+  int32_t* dstart = gsc + (E + 1);   // [N+1]
+  int32_t* scratch = dstart + (N + 1);
+  const int s = blockIdx.y;
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
+  int e_of[kPlanSub], pos_of[kPlanSub], within_of[kPlanSub];
+  fetch_slots(nullptr, p.send_pos, s, c, TR, e_of, pos_of);
+  for (int e = tid; e <= E; e += kPlanThreads) so[e] = p.send_off[(size_t)s * (E + 1) + e];
+  const int32_t* cnt = p.cnt;
+  column_sums([=](int s2, int e) { return cnt[(size_t)s2 * E + e]; }, N, E, s, sro, sros, gsc,
+              scratch + kPlanThreads / kWave);
+#pragma unroll
+  for (int sub = 0; sub < kPlanSub; ++sub) {
+    const int pos = pos_of[sub];
+    e_of[sub] = -1;
+    within_of[sub] = -1;
+    if (pos < 0 || pos >= so[E]) continue;
+    int lo = 0, hi = E - 1;  // largest e with so[e] <= pos
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (so[mid] <= pos) lo = mid; else hi = mid - 1;
+    }
+    e_of[sub] = lo;
+    within_of[sub] = pos - so[lo];
+  }
+  receive_tables(e_of, within_of, s, c, N, E, L, TR, cap, p, status, sro, sros, gsc, dstart,
+                 scratch);
+}
+
+// LDS bytes of the finalize and exchange launches (the larger of the two
+// layouts) and of the count launch.
+size_t lds_count_bytes(const Dims& d) {
+  constexpr int kWaves = kPlanThreads / kWave;
+  return sizeof(int32_t) * (size_t)(kWaves + 1) * (d.E + 1);
+}
+size_t lds_final_bytes(const Dims& d) {
+  constexpr int kWaves = kPlanThreads / kWave;
+  const int groups = d.E >= kPlanThreads ? 1 : kPlanThreads / d.E;
+  return sizeof(int32_t) * ((size_t)5 * (d.E + 1) + (d.N + 1) + kWaves + (size_t)2 * groups * d.E);
+}
+
+// Kernels using more than 64 KB of LDS must opt in, once per device.
+hipError_t allow_large_lds() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static bool done[64] = {};
+  if (dev >= 0 && dev < 64 && done[dev]) return hipSuccess;
+  for (const void* f : {(const void*)plan_count_kernel, (const void*)plan_finalize_kernel,
+                        (const void*)plan_local_kernel, (const void*)plan_exchange_kernel}) {
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+  }
+  if (dev >= 0 && dev < 64) done[dev] = true;
+  return hipSuccess;
+}
+
+hipError_t launch_count(const Dims& d, const int32_t* idx, const PlanPtrs& p, int32_t* status,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(plan_count_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
+                     lds_count_bytes(d), stream, idx, d.E, d.TR, d.nchunks, p.send_pos,
+                     p.chunk_cnt, status);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                        int32_t* status, hipStream_t stream) {
-  constexpr int kWaves = kPlanThreads / kWave;
-  const size_t lds_count = sizeof(int32_t) * (size_t)(kWaves + 1) * (d.E + 1);
-  const int groups = d.E >= kPlanThreads ? 1 : kPlanThreads / d.E;
-  const size_t lds_final = sizeof(int32_t) * ((size_t)5 * (d.E + 1) + (d.N + 1) + kWaves +
-                                              (size_t)2 * groups * d.E);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)plan_count_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)plan_finalize_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const dim3 grid(d.nchunks, d.N);
-  hipLaunchKernelGGL(plan_count_kernel, grid, dim3(kPlanThreads), lds_count, stream, idx, d.E,
-                     d.TR, d.nchunks, p.send_pos, p.chunk_cnt, status);
-  hipError_t e = hipGetLastError();
+  hipError_t e = allow_large_lds();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_finalize_kernel, grid, dim3(kPlanThreads), lds_final, stream, idx, d.N,
-                     d.E, d.L, d.TR, d.nchunks, d.cap, p, status);
+  e = launch_count(d, idx, p, status, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_finalize_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
+                     lds_final_bytes(d), stream, idx, d.N, d.E, d.L, d.TR, d.nchunks, d.cap, p,
+                     status);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
+                             int32_t* status, hipStream_t stream) {
+  hipError_t e = allow_large_lds();
+  if (e != hipSuccess) return e;
+  e = launch_count(d, idx, p, status, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_local_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
+                     lds_final_bytes(d), stream, idx, d.E, d.TR, d.nchunks, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_exchange(const Dims& d, const PlanPtrs& p, int32_t* status,
+                                hipStream_t stream) {
+  hipError_t e = allow_large_lds();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_exchange_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
+                     lds_final_bytes(d), stream, d.N, d.E, d.L, d.TR, d.cap, p, status);
   return hipGetLastError();
 }
 

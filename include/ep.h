@@ -201,6 +201,40 @@ EP_API int ep_dispatch_recv(const ep_desc *d, const void *const send[2],
                      const void *plan_ws, void *const grouped[2],
                      hipStream_t stream);
 
+/* Split dispatch ("Dispatch and combine": dispatch is split into a sender
+ * half and a receiver half so that other work can run between them; "Send
+ * and receive buffers": each receiver keeps a small private region per
+ * sender, which takes the first tokens together with the routing
+ * information, before the counts have been exchanged).
+ *
+ * Sender half. Uses only each source rank's own data: the send side of the
+ * plan (cnt[s], send_off[s], send_pos[s], as ep_plan writes them; these
+ * rows are the routing information the source publishes) and the pack, with
+ * one change of destination: row i of the segment s -> d (the rows s sends
+ * to the experts of rank d, which start at send_off[s][d L]) goes to
+ * priv[p][(d N + s) P + i] when i < P = priv_rows, and to the send buffer
+ * otherwise (those send rows are left unwritten).
+ * priv: per plane [N][N][P][row_p] bytes; may be NULL when P == 0. P must be
+ * in [0, T R]. status: as for ep_plan (bad expert ids). The receive-side
+ * tables of plan_ws are not written. */
+EP_API int ep_dispatch_send(const ep_desc *d, const int32_t *topk_idx,
+                            const void *const x[2], void *plan_ws,
+                            void *const send[2], void *const priv[2],
+                            int32_t priv_rows, int32_t *status,
+                            hipStream_t stream);
+
+/* Receiver half, after ep_dispatch_send on the same plan_ws (stream order
+ * or an event). The exchange reads every source's published cnt row and
+ * computes the receive side of the plan (src_off, recv_off, grp_off,
+ * grp_pos, comb_row, grp_slot, capacity bit in status), then every
+ * delivered row is moved into the grouped layout from wherever the sender
+ * put it (private region or send buffer). Afterwards plan_ws and grouped
+ * are identical to those of ep_plan, ep_dispatch_pack, ep_dispatch_recv. */
+EP_API int ep_dispatch_recv_split(const ep_desc *d, const void *const send[2],
+                                  void *const priv[2], int32_t priv_rows,
+                                  void *plan_ws, void *const grouped[2],
+                                  int32_t *status, hipStream_t stream);
+
 /* Stand-in for the grouped GEMM (outside the method; used by tests and the
  * benchmark to produce expert outputs). expert_out is bf16 [N][cap][H].
  * bf16 payload: y = x when alpha == NULL, else y = bf16(x * alpha[e]) with a
