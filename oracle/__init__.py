@@ -87,6 +87,10 @@ def _declare(L: ctypes.CDLL) -> None:
     L.oracle_combine_token.restype = None
     L.oracle_combine.argtypes = [_I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P]
     L.oracle_combine.restype = None
+    L.oracle_combine_presum_token.argtypes = [_I, _I, _P, _P, _P, _P, _P]
+    L.oracle_combine_presum_token.restype = None
+    L.oracle_combine_presum.argtypes = [_I, _I, _I, _I, _I, _I64] + [_P] * 6
+    L.oracle_combine_presum.restype = None
     L.oracle_rounding_mode_is_nearest.argtypes = []
     L.oracle_rounding_mode_is_nearest.restype = _I
 
@@ -250,6 +254,38 @@ def combine_token(w: np.ndarray, rows: list) -> np.ndarray:
     out = np.zeros(H, np.uint16)
     w = np.ascontiguousarray(w, dtype=np.float32)
     lib().oracle_combine_token(H, R, _ptr(w), ctypes.cast(arr, ctypes.c_void_p), _ptr(out))
+    return out
+
+
+def combine_presum(y: np.ndarray, weights: np.ndarray, idx: np.ndarray, p: dict):
+    """Partial sums on the expert side, then on the source side.
+    Returns (partial bf16 [N, T*R, H] with leader rows set (others 0),
+    out bf16 [N, T, H])."""
+    N, rows, H = y.shape
+    T, R = idx.shape[1:]
+    E = p["cnt"].shape[1]
+    partial = np.zeros((N, T * R, H), np.uint16)
+    out = np.zeros((N, T, H), np.uint16)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    lib().oracle_combine_presum(N, T, E, R, H, rows, _ptr(idx), _ptr(p["grp_pos"]),
+                                _ptr(np.ascontiguousarray(y)), _ptr(w), _ptr(partial), _ptr(out))
+    return partial, out
+
+
+def combine_presum_token(w: np.ndarray, rows: list, ranks: list) -> np.ndarray:
+    """One token of the partial-sum combine from explicit expert rows and the
+    ranks hosting them (None = dropped slot)."""
+    R = len(rows)
+    H = next(r.shape[0] for r in rows if r is not None) if any(r is not None for r in rows) else 0
+    keep = [np.ascontiguousarray(r, dtype=np.uint16) if r is not None else None for r in rows]
+    arr = (ctypes.c_void_p * R)(*[(r.ctypes.data if r is not None else None) for r in keep])
+    rk = np.array([-1 if r is None else int(r) for r in ranks], np.int32)
+    partial = np.zeros((max(R, 1), max(H, 1)), np.uint16)
+    out = np.zeros(H, np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    lib().oracle_combine_presum_token(H, R, _ptr(w), ctypes.cast(arr, ctypes.c_void_p), _ptr(rk),
+                                      _ptr(partial), _ptr(out))
     return out
 
 

@@ -510,6 +510,90 @@ void oracle_combine(int N, int T, int E, int R, int H, int64_t cap,
     free(rows);
 }
 
+/* Combine with partial sums on the expert side (the sender-side
+ * accumulation the "Evaluation" section contrasts with receiver-only
+ * accumulation). Reading adopted: for one token, the slots whose experts sit
+ * on the same rank d form a group; the expert rank sums its group in float
+ * (fused multiply-add, slot order k ascending, from 0) and rounds the sum
+ * once to bf16, which is what travels back; the group's row is kept at the
+ * slot of its first member (its leader). The source rank then adds the
+ * partial rows in float in leader order (k ascending, from 0) and rounds
+ * once to bf16. Dropped slots (grp_pos < 0 or a bad id) belong to no group.
+ * rows[k], rank[k]: the slot's expert-output row and hosting rank (rows[k]
+ * NULL for a dropped slot). partial: R rows of H (leader rows written, the
+ * others untouched). */
+void oracle_combine_presum_token(int H, int R, const float *w,
+                                 const uint16_t *const *rows, const int *rank,
+                                 uint16_t *partial, uint16_t *out)
+{
+    for (int k = 0; k < R; ++k) {
+        if (!rows[k])
+            continue;
+        int leader = 1;
+        for (int k2 = 0; k2 < k; ++k2)
+            if (rows[k2] && rank[k2] == rank[k])
+                leader = 0;
+        if (!leader)
+            continue;
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int k2 = k; k2 < R; ++k2)
+                if (rows[k2] && rank[k2] == rank[k])
+                    acc = fmaf(w[k2], oracle_bf16_to_f32(rows[k2][h]), acc);
+            partial[(size_t)k * H + h] = oracle_f32_to_bf16(acc);
+        }
+    }
+    for (int h = 0; h < H; ++h) {
+        float acc = 0.0f;
+        for (int k = 0; k < R; ++k) {
+            if (!rows[k])
+                continue;
+            int leader = 1;
+            for (int k2 = 0; k2 < k; ++k2)
+                if (rows[k2] && rank[k2] == rank[k])
+                    leader = 0;
+            if (leader)
+                acc = acc + oracle_bf16_to_f32(partial[(size_t)k * H + h]);
+        }
+        out[h] = oracle_f32_to_bf16(acc);
+    }
+}
+
+/* The whole partial-sum combine. y: bf16 [N][cap][H]; w: fp32 [N][T][R];
+ * partial: bf16 [N][T*R][H] (leader rows written); out: bf16 [N][T][H]. */
+void oracle_combine_presum(int N, int T, int E, int R, int H, int64_t cap,
+                           const int32_t *idx, const int32_t *grp_pos,
+                           const uint16_t *y, const float *w, uint16_t *partial,
+                           uint16_t *out)
+{
+    const int L = E / N;
+    const uint16_t **rows = (const uint16_t **)malloc((size_t)R * sizeof *rows);
+    int *rank = (int *)malloc((size_t)R * sizeof *rank);
+    if (!rows || !rank) {
+        free(rows);
+        free(rank);
+        return;
+    }
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t) {
+            size_t tok = (size_t)s * T + t;
+            for (int k = 0; k < R; ++k) {
+                int32_t e = idx[tok * R + k];
+                int32_t g = grp_pos[tok * R + k];
+                rank[k] = -1;
+                rows[k] = NULL;
+                if (e < 0 || e >= E || g < 0)
+                    continue;
+                rank[k] = e / L;
+                rows[k] = y + ((size_t)(e / L) * cap + g) * H;
+            }
+            oracle_combine_presum_token(H, R, w + tok * R, rows, rank,
+                                        partial + tok * R * (size_t)H, out + tok * H);
+        }
+    free(rows);
+    free(rank);
+}
+
 int oracle_rounding_mode_is_nearest(void)
 {
     return fegetround() == FE_TONEAREST;

@@ -65,6 +65,14 @@ void oracle_combine(int N, int T, int E, int R, int H, int64_t cap,
                     const int32_t *idx, const int32_t *grp_pos,
                     const uint16_t *y, const float *w, uint16_t *out);
 
+void oracle_combine_presum_token(int H, int R, const float *w,
+                                 const uint16_t *const *rows, const int *rank,
+                                 uint16_t *partial, uint16_t *out);
+void oracle_combine_presum(int N, int T, int E, int R, int H, int64_t cap,
+                           const int32_t *idx, const int32_t *grp_pos,
+                           const uint16_t *y, const float *w, uint16_t *partial,
+                           uint16_t *out);
+
 int oracle_rounding_mode_is_nearest(void);
 
 #ifdef __cplusplus

@@ -59,6 +59,13 @@ MUTATIONS = {
                         "float scale = amax > 0.0f ? amax / 240.0f : 1.0f;"),
     "quant_zero_scale": ("float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
                          "float scale = amax > 0.0f ? amax / 448.0f : 0.5f;"),
+    "presum_rank_ignored": ("for (int k2 = k; k2 < R; ++k2)\n                if (rows[k2] && rank[k2] == rank[k])",
+                            "for (int k2 = k; k2 < R; ++k2)\n                if (rows[k2])"),
+    "presum_leader_weight": ("acc = fmaf(w[k2], oracle_bf16_to_f32(rows[k2][h]), acc);",
+                             "acc = fmaf(w[k], oracle_bf16_to_f32(rows[k2][h]), acc);"),
+    "presum_leader_is_last": ("        int leader = 1;\n        for (int k2 = 0; k2 < k; ++k2)",
+                              "        int leader = 1;\n        for (int k2 = k + 1; k2 < R; ++k2)"),
+    "presum_groups_by_expert": ("rank[k] = e / L;", "rank[k] = e;"),
     "quant_block_size": ("float a = fabsf(oracle_bf16_to_f32(x[b * 128 + i]));",
                          "float a = fabsf(oracle_bf16_to_f32(x[b * 128 + (i & 63)]));"),
 }
@@ -87,6 +94,11 @@ def _pin_checks():
         pins.test_f32_to_e4m3_matches_torch_including_ties,
         pins.test_quantize_b128_matches_generator_quantiser,
         pins.test_quantize_b128_roundtrip_error_bound,
+        pins.test_presum_groups_by_rank_and_rounds_each_partial,
+        pins.test_presum_adds_partials_in_slot_order,
+        pins.test_presum_single_choice_is_the_rounded_product,
+        pins.test_presum_one_rank_exact_sums_equal_the_plain_combine,
+        pins.test_presum_partial_rows_sit_at_group_leaders,
     ]
 
 

@@ -486,3 +486,98 @@ def test_quantize_b128_roundtrip_error_bound():
     assert (np.abs(deq - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal] * (1 + 1e-6)).all()
     sub = ~normal
     assert (np.abs(deq - x)[sub] <= 2.0 ** -10 * np.repeat(scales, 128, axis=-1)[sub] * (1 + 1e-6)).all()
+
+
+# ---------------------------------------------------------------------------
+# Combine with partial sums on the expert side ("Evaluation": the sender-side
+# accumulation that receiver-only accumulation is contrasted with)
+# ---------------------------------------------------------------------------
+
+def _one(v: int) -> np.ndarray:
+    return np.array([v], np.uint16)
+
+
+BF16_ONE, BF16_2M8, BF16_2M25 = 0x3F80, 0x3B80, 0x3300      # 1, 2^-8, 2^-25
+
+
+def test_presum_groups_by_rank_and_rounds_each_partial():
+    """Weights 1; slot 0 (2^-8) on rank 0, slots 1 (1) and 2 (2^-8) on rank 1.
+    Rank 1's partial 1 + 2^-8 is a bf16 tie and rounds to 1; the final
+    2^-8 + 1 is a tie again: 1 (0x3F80). Receiver-only accumulation gives
+    1 + 2^-7 (0x3F81), and so do three separate ranks (exact partials)."""
+    w = np.ones(3, np.float32)
+    rows = [_one(BF16_2M8), _one(BF16_ONE), _one(BF16_2M8)]
+    assert oracle.combine_presum_token(w, rows, [0, 1, 1])[0] == 0x3F80
+    assert oracle.combine_token(w, rows)[0] == 0x3F81
+    assert oracle.combine_presum_token(w, rows, [0, 1, 2])[0] == 0x3F81
+    assert oracle.combine_presum_token(np.array([0.25, 0.75], np.float32),
+                                       [None, _one(BF16_ONE)], [None, 0])[0] == 0x3F40
+
+
+def test_presum_adds_partials_in_slot_order():
+    """Partials 1, 2^-8, 2^-25 x 3 on five ranks. Added from slot 0 upward,
+    each 2^-25 is a quarter ulp of 1 + 2^-8 in float and is lost, leaving a
+    bf16 tie that rounds to 1. In the opposite order the small ones add up
+    to 3 * 2^-25 first and the float sum 1 + 2^-8 + 2^-23 rounds to 1 + 2^-7.
+    The ranks run 4..0, so rank order would be the opposite order."""
+    w = np.ones(5, np.float32)
+    rows = [_one(BF16_ONE), _one(BF16_2M8)] + [_one(BF16_2M25)] * 3
+    assert oracle.combine_presum_token(w, rows, [4, 3, 2, 1, 0])[0] == 0x3F80
+    assert oracle.combine_presum_token(w, rows[::-1], [0, 1, 2, 3, 4])[0] == 0x3F81
+
+
+def test_presum_single_choice_is_the_rounded_product():
+    """R = 1: every group is one slot, the partial is bf16(float(w * y)) (a
+    correctly rounded float product, here from numpy, then torch's bf16
+    cast), and the final sum returns it unchanged; the partial sits in the
+    token's only slot row."""
+    sh = W.Shape("r1", 4, 16, 64, 8, 1, expert="scale", seed=3)
+    wl = W.make_workload(sh)
+    r = oracle.run(wl)
+    p = r["plan"]
+    partial, out = oracle.combine_presum(r["y"], wl.weights, wl.idx, p)
+    L = sh.n_experts // sh.n_ranks
+    y = r["y"][wl.idx[..., 0] // L, p["grp_pos"][..., 0]]          # [N, T, H]
+    prod = wl.weights[..., 0:1].astype(np.float32) * W.bf16_bits_to_f32(y)
+    want = W.to_bf16_bits(prod.astype(np.float32))
+    np.testing.assert_array_equal(out, want)
+    np.testing.assert_array_equal(partial, out)
+
+
+def test_presum_one_rank_exact_sums_equal_the_plain_combine():
+    """N = 1: all of a token's slots form one group. With power-of-two
+    weights and values of magnitude in [2^-4, 2) every product and float sum
+    is exact, so the result is the correctly rounded exact sum: the plain
+    combine's value (double accumulation, one rounding)."""
+    sh = W.Shape("one_rank", 1, 64, 96, 6, 4, seed=5)
+    wl = W.make_workload(sh)
+    rng = np.random.default_rng(5)
+    mag = rng.uniform(2.0 ** -4, 2.0, size=wl.x_bf16.shape)
+    sign = rng.choice([-1.0, 1.0], size=wl.x_bf16.shape)
+    wl.x_bf16 = W.to_bf16_bits((mag * sign).astype(np.float32))
+    wl.planes = [wl.x_bf16.view(np.uint8).reshape(1, 64, 2 * 96)]
+    wl.weights = rng.choice([0.5, 0.25, 0.125, 0.0625], size=wl.weights.shape).astype(np.float32)
+    r = oracle.run(wl)
+    partial, out = oracle.combine_presum(r["y"], wl.weights, wl.idx, r["plan"])
+    np.testing.assert_array_equal(out, r["out"])
+    np.testing.assert_array_equal(partial[0, ::4], out[0])        # leader = slot 0
+
+
+def test_presum_partial_rows_sit_at_group_leaders():
+    """Hand layout: N = 2, E = 4 (experts 0, 1 on rank 0; 2, 3 on rank 1),
+    one token of rank 0 routed to experts (0, 2, 3) with weights 1 and expert
+    rows 2^-8, 1, 2^-8: rank 1 holds slots 1 and 2 (different experts), so
+    its partial (1 + 2^-8 rounded to 1) sits in slot 1's row, slot 2's row is
+    left untouched, and the token combines to 1 (0x3F80)."""
+    N, T, E, R, H = 2, 1, 4, 3, 1
+    idx = np.array([[[0, 2, 3]], [[1, 0, 1]]], np.int32)
+    p = oracle.plan(N, T, E, R, oracle.recv_bound(N, T, E, R), idx)
+    cap = oracle.recv_bound(N, T, E, R)
+    y = np.zeros((N, cap, H), np.uint16)
+    vals = [BF16_2M8, BF16_ONE, BF16_2M8]
+    for k in range(R):
+        y[idx[0, 0, k] // 2, p["grp_pos"][0, 0, k], 0] = vals[k]
+    w = np.ones((N, T, R), np.float32)
+    partial, out = oracle.combine_presum(y, w, idx, p)
+    assert out[0, 0, 0] == 0x3F80
+    assert list(partial[0, :, 0]) == [BF16_2M8, BF16_ONE, 0]
