@@ -228,6 +228,52 @@ def measure_split(ep, torch, d, b, sh, P: int, steps: int, warmup: int) -> dict:
     }
 
 
+def measure_presum(ep, torch, np, d, b, sh, wl, steps: int, warmup: int) -> dict:
+    """Combine with partial sums on the expert side next to the plain
+    combine: time, and the rows a multi-GPU combine would move back (one per
+    (token, rank) pair instead of one per slot)."""
+    import statistics as st
+
+    N, T, R, H, E = sh.n_ranks, sh.tokens, sh.topk, sh.hidden, sh.n_experts
+    L = E // N
+    ranks = wl.idx // L
+    pairs = sum(len(set(row)) for row in ranks.reshape(-1, R).tolist())
+    partial = torch.empty((N, T * R, H), dtype=torch.int16, device="cuda")
+    out = torch.empty((N, T, H), dtype=torch.int16, device="cuda")
+    s = torch.cuda.current_stream()
+    sp = s.cuda_stream
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        res = []
+        for _ in range(5):
+            e0.record(s)
+            for _ in range(max(steps // 5, 1)):
+                fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / max(steps // 5, 1) * 1e3)
+        return st.median(res)
+
+    t_plain = timed(lambda: ep.combine(d, b.expert_out, b.weights, b.plan_ws, out, sp))
+    t_pre = timed(lambda: ep.combine_presum(d, b.expert_out, b.weights, b.plan_ws, partial,
+                                            out, sp))
+    row = 2 * H
+    NT, NTR = N * T, N * T * R
+    one_gpu = NTR * row + 2 * pairs * row + NT * row + 4 * NTR
+    return {
+        "combine_us": round(t_plain, 2),
+        "presum_combine_us": round(t_pre, 2),
+        "rows_returned": pairs,
+        "rows_returned_plain": NTR,
+        "returned_fraction": round(pairs / NTR, 4),
+        "presum_bytes_one_gpu": one_gpu,
+        "presum_GBps_one_gpu": round(one_gpu / t_pre / 1e3, 1),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +289,8 @@ def main() -> int:
                     help="also measure the split dispatch with P private rows per "
                          "(destination, source) pair, alone and overlapped with a "
                          "shared-expert stand-in on a second stream")
+    ap.add_argument("--presum", action="store_true",
+                    help="also measure the combine with partial sums on the expert side")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0 = skip)")
     args = ap.parse_args()
@@ -357,6 +405,10 @@ def main() -> int:
     if args.split >= 0:
         split = measure_split(ep, torch, d, b, sh, args.split, args.steps, args.warmup)
 
+    presum = None
+    if args.presum:
+        presum = measure_presum(ep, torch, np, d, b, sh, wl, args.steps, args.warmup)
+
     cpu = None
     if args.cpu_budget > 0:
         base = cpu_baseline(sh, wl, args.cpu_budget, quant)
@@ -428,6 +480,8 @@ def main() -> int:
     }
     if split is not None:
         res["split"] = split
+    if presum is not None:
+        res["presum"] = presum
     print(json.dumps(res), flush=True)
     return 0
 

@@ -32,7 +32,8 @@ EXPORTS = (
     "ep_recv_bound", "ep_capacity", "ep_num_planes", "ep_row_bytes",
     "ep_plan_bytes", "ep_plan_views", "ep_plan", "ep_dispatch_pack", "ep_dispatch_pack_quant",
     "ep_dispatch_transfer", "ep_dispatch_unpack", "ep_dispatch_recv",
-    "ep_dispatch_send", "ep_dispatch_recv_split", "ep_expert_stub", "ep_combine", "ep_probe_copy", "ep_status_string",
+    "ep_dispatch_send", "ep_dispatch_recv_split", "ep_expert_stub", "ep_combine",
+    "ep_combine_presum", "ep_probe_copy", "ep_status_string",
     "ep_last_error",
 )
 
@@ -87,6 +88,7 @@ def _load() -> ctypes.CDLL:
         "ep_dispatch_recv_split": (ctypes.c_int, [D, P, P, ctypes.c_int32, P, P, P, P]),
         "ep_expert_stub": (ctypes.c_int, [D, P, P, P, P, P]),
         "ep_combine": (ctypes.c_int, [D, P, P, P, P, P]),
+        "ep_combine_presum": (ctypes.c_int, [D, P, P, P, P, P, P]),
         "ep_probe_copy": (ctypes.c_int, [P, P, ctypes.c_size_t, P]),
         "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "ep_last_error": (ctypes.c_char_p, []),
@@ -240,6 +242,12 @@ def expert_stub(d: Desc, grouped: Sequence, alpha, plan_ws, expert_out, stream=N
 def combine(d: Desc, expert_out, weights, plan_ws, out, stream=None) -> None:
     _check(_lib.ep_combine(ctypes.byref(d), _addr(expert_out), _addr(weights), _addr(plan_ws),
                            _addr(out), _stream(stream)), "ep_combine")
+
+
+def combine_presum(d: Desc, expert_out, weights, plan_ws, partial, out, stream=None) -> None:
+    _check(_lib.ep_combine_presum(ctypes.byref(d), _addr(expert_out), _addr(weights),
+                                  _addr(plan_ws), _addr(partial), _addr(out), _stream(stream)),
+           "ep_combine_presum")
 
 
 def probe_copy(dst, src, nbytes: int, stream=None) -> None:

@@ -391,6 +391,18 @@ int ep_combine(const ep_desc* d, const uint16_t* expert_out, const float* weight
   return EP_OK;
 }
 
+int ep_combine_presum(const ep_desc* d, const uint16_t* expert_out, const float* weights,
+                      const void* plan_ws, uint16_t* partial, uint16_t* out, hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap));
+  EP_CHECK(check_ptr(partial, scope.device(), "partial", dims.NTR));
+  EP_CHECK(check_ptr(out, scope.device(), "out", dims.NT));
+  EP_CHECK(check_ptr(weights, scope.device(), "weights", dims.NTR));
+  const hipError_t e = ep::launch_combine_presum(dims, expert_out, weights, pp, partial, out, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_combine_presum");
+  return EP_OK;
+}
+
 int ep_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   if (bytes % 16 != 0) return fail(EP_ERR_INVALID_ARG, "bytes must be a multiple of 16");
   if (bytes / 16 >= (size_t)kMaxWaves * 64 * 7)

@@ -87,6 +87,103 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const uint16_t* y, cons
   }
 }
 
+// Combine with partial sums on the expert side ("Evaluation": sender-side
+// accumulation moves fewer bytes than accumulating on the receiver only).
+// A token's slots whose expert rows live on the same rank form a group;
+// rows[k] = rank * cap + grouped position, so the rank is rows[k] / cap.
+// The group's first slot is its leader.
+__device__ __forceinline__ bool slot_ok(int r, int64_t rows_in) { return r >= 0 && r < rows_in; }
+
+__device__ __forceinline__ bool is_leader(const int32_t* rows, int k, int cap, int64_t rows_in) {
+  const int rk = rows[k];
+  if (!slot_ok(rk, rows_in)) return false;
+  const int d = rk / cap;
+  for (int k2 = 0; k2 < k; ++k2) {
+    const int r2 = rows[k2];
+    if (slot_ok(r2, rows_in) && r2 / cap == d) return false;
+  }
+  return true;
+}
+
+// Expert side: for each group, sum w_k * y_k over its slots in k order
+// (fused multiply-adds from 0, fp32), round once to bf16 and store the row
+// at the leader's slot of `partial` ([N][T R][H]). Two waves per token as
+// in combine_kernel; one expert row in flight per lane set.
+__global__ __launch_bounds__(kBlock) void presum_kernel(const uint16_t* y, const float* w,
+                                                        const int32_t* comb_row,
+                                                        uint16_t* partial, int NT, int R, int H,
+                                                        int cap, int64_t rows_in) {
+  const int wv = wave_index();
+  const int tok = wv / kCombWaves;
+  const int part = wv % kCombWaves;
+  if (tok >= NT) return;
+  const int32_t* rows = comb_row + (size_t)tok * R;
+  const float* wt = w + (size_t)tok * R;
+  const int n16 = H / 8;
+  const u32x4* ybase = (const u32x4*)y;
+  for (int k0 = 0; k0 < R; ++k0) {
+    if (!is_leader(rows, k0, cap, rows_in)) continue;
+    const int d = rows[k0] / cap;
+    u32x4* o = (u32x4*)(partial + ((size_t)tok * R + k0) * H);
+    for (int base = part * kWave * kCombV; base < n16; base += kCombWaves * kWave * kCombV) {
+      float acc[kCombV][8];
+#pragma unroll
+      for (int i = 0; i < kCombV; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+      for (int k = k0; k < R; ++k) {
+        const int rk = rows[k];
+        if (!slot_ok(rk, rows_in) || rk / cap != d) continue;
+        RowRegs<kCombV> v;
+        load_row16(v, ybase + (size_t)rk * n16, base, n16);
+        fma_row(acc, v, wt[k]);
+      }
+      store_acc(acc, o, base, n16);
+    }
+  }
+}
+
+// Source side: out = bf16( sum over leaders, k order, of float(partial) ),
+// from 0 (a fused multiply-add by 1 is an exact add). Two rows in flight.
+__global__ __launch_bounds__(kBlock) void presum_final_kernel(const uint16_t* partial,
+                                                              const int32_t* comb_row,
+                                                              uint16_t* out, int NT, int R, int H,
+                                                              int cap, int64_t rows_in) {
+  const int wv = wave_index();
+  const int tok = wv / kCombWaves;
+  const int part = wv % kCombWaves;
+  if (tok >= NT) return;
+  const int32_t* rows = comb_row + (size_t)tok * R;
+  const int n16 = H / 8;
+  const u32x4* pbase = (const u32x4*)(partial + (size_t)tok * R * H);
+  u32x4* o = (u32x4*)(out + (size_t)tok * H);
+  uint64_t leaders = 0;
+  for (int k = 0; k < R; ++k)
+    if (is_leader(rows, k, cap, rows_in)) leaders |= 1ull << k;
+  for (int base = part * kWave * kCombV; base < n16; base += kCombWaves * kWave * kCombV) {
+    float acc[kCombV][8];
+#pragma unroll
+    for (int i = 0; i < kCombV; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    uint64_t left = leaders;
+    while (left) {
+      const int ka = __builtin_ctzll(left);
+      left &= left - 1;
+      RowRegs<kCombV> va, vb;
+      load_row16(va, pbase + (size_t)ka * n16, base, n16);
+      const int kb = left ? __builtin_ctzll(left) : -1;
+      if (kb >= 0) {
+        left &= left - 1;
+        load_row16(vb, pbase + (size_t)kb * n16, base, n16);
+      }
+      fma_row(acc, va, 1.0f);
+      if (kb >= 0) fma_row(acc, vb, 1.0f);
+    }
+    store_acc(acc, o, base, n16);
+  }
+}
+
 // Stand-in expert: one wave per delivered grouped row r of rank d; its local
 // expert j is the one with grp_off[d][j] <= r < grp_off[d][j+1].
 __global__ __launch_bounds__(kBlock) void expert_stub_kernel(
@@ -156,6 +253,21 @@ hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* w, cons
   if (d.NT == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(d.NT * kCombWaves)), dim3(kBlock), 0,
                      stream, y, w, p.comb_row, out, (int)d.NT, d.R, d.H, (int64_t)d.N * d.cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_presum(const Dims& d, const uint16_t* y, const float* w,
+                                 const PlanPtrs& p, uint16_t* partial, uint16_t* out,
+                                 hipStream_t stream) {
+  if (d.NT == 0) return hipSuccess;
+  const dim3 grid(blocks_for(d.NT * kCombWaves));
+  const int64_t rows_in = (int64_t)d.N * d.cap;
+  hipLaunchKernelGGL(presum_kernel, grid, dim3(kBlock), 0, stream, y, w, p.comb_row, partial,
+                     (int)d.NT, d.R, d.H, (int)d.cap, rows_in);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(presum_final_kernel, grid, dim3(kBlock), 0, stream, partial, p.comb_row, out,
+                     (int)d.NT, d.R, d.H, (int)d.cap, rows_in);
   return hipGetLastError();
 }
 

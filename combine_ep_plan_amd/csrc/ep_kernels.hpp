@@ -59,6 +59,9 @@ hipError_t launch_expert_stub(const Dims& d, const void* const grouped[2],
                               hipStream_t stream);
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* w,
                           const PlanPtrs& p, uint16_t* out, hipStream_t stream);
+hipError_t launch_combine_presum(const Dims& d, const uint16_t* y, const float* w,
+                                 const PlanPtrs& p, uint16_t* partial, uint16_t* out,
+                                 hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes,
                              hipStream_t stream);
 

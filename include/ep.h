@@ -254,6 +254,24 @@ EP_API int ep_combine(const ep_desc *d, const uint16_t *expert_out,
                const float *weights, const void *plan_ws, uint16_t *out,
                hipStream_t stream);
 
+/* Combine with partial sums on the expert side ("Evaluation": accumulating
+ * on the sender side of combine moves fewer bytes than accumulating on the
+ * receiver only, at some cost in accuracy). For one token, the slots whose
+ * experts sit on the same rank form a group; the first slot of a group is
+ * its leader. Expert side: partial[s][t R + leader] = bf16( sum over the
+ * group's slots, k order, of w_k * y_k ) in fp32 with fused multiply-adds
+ * from 0, rounded once (nearest even); one row per (token, rank) pair is
+ * what would travel back. Source side: out[s][t] = bf16( sum over the
+ * token's leaders, k order, of partial ) in fp32 from 0, rounded once.
+ * Dropped slots belong to no group; a token with none writes zeros.
+ * partial: bf16 [N][T R][H], caller-owned scratch; only leader rows are
+ * written. Results differ from ep_combine by the rounding of each partial
+ * (one bf16 rounding per group). */
+EP_API int ep_combine_presum(const ep_desc *d, const uint16_t *expert_out,
+                             const float *weights, const void *plan_ws,
+                             uint16_t *partial, uint16_t *out,
+                             hipStream_t stream);
+
 /* Copy `bytes` (a multiple of 16) from src to dst with the library's row
  * copy loop: a bandwidth reference for measurements, not part of the
  * method. */
