@@ -91,6 +91,10 @@ def _declare(L: ctypes.CDLL) -> None:
     L.oracle_combine_presum_token.restype = None
     L.oracle_combine_presum.argtypes = [_I, _I, _I, _I, _I, _I64] + [_P] * 6
     L.oracle_combine_presum.restype = None
+    L.oracle_kv_regions.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _P, _P, _P]
+    L.oracle_kv_regions.restype = _I64
+    L.oracle_kv_copy.argtypes = [_I, _I64, _P, _P, _P, _P, _I64, _P, _I64]
+    L.oracle_kv_copy.restype = None
     L.oracle_rounding_mode_is_nearest.argtypes = []
     L.oracle_rounding_mode_is_nearest.restype = _I
 
@@ -286,6 +290,31 @@ def combine_presum_token(w: np.ndarray, rows: list, ranks: list) -> np.ndarray:
     w = np.ascontiguousarray(w, dtype=np.float32)
     lib().oracle_combine_presum_token(H, R, _ptr(w), ctypes.cast(arr, ctypes.c_void_p), _ptr(rk),
                                       _ptr(partial), _ptr(out))
+    return out
+
+
+def kv_regions(n: int, tok: int, bs_src: int, src_blocks: np.ndarray, bs_dst: int,
+               dst_blocks: np.ndarray) -> np.ndarray:
+    """Transfer regions of one request: int64 [m, 3] rows (src_off, dst_off, bytes)."""
+    sb = np.ascontiguousarray(src_blocks, dtype=np.int32)
+    db = np.ascontiguousarray(dst_blocks, dtype=np.int32)
+    so = np.zeros(max(n, 1), np.int64)
+    do = np.zeros(max(n, 1), np.int64)
+    by = np.zeros(max(n, 1), np.int64)
+    m = lib().oracle_kv_regions(n, tok, bs_src, _ptr(sb), bs_dst, _ptr(db), _ptr(so), _ptr(do),
+                                _ptr(by))
+    return np.stack([so[:m], do[:m], by[:m]], axis=1)
+
+
+def kv_copy(regions: np.ndarray, src: np.ndarray, dst: np.ndarray) -> np.ndarray:
+    """Apply regions to every rank: src uint8 [ranks, src_bytes], dst uint8
+    [ranks, dst_bytes] (a copy of dst is returned)."""
+    out = np.ascontiguousarray(dst).copy()
+    src = np.ascontiguousarray(src)
+    reg = np.ascontiguousarray(regions, dtype=np.int64)
+    so, do, by = (np.ascontiguousarray(reg[:, c]) for c in range(3))
+    lib().oracle_kv_copy(src.shape[0], reg.shape[0], _ptr(so), _ptr(do), _ptr(by), _ptr(src),
+                         src.shape[1], _ptr(out), out.shape[1])
     return out
 
 

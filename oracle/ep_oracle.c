@@ -594,6 +594,58 @@ void oracle_combine_presum(int N, int T, int E, int R, int H, int64_t cap,
     free(rank);
 }
 
+/* ---------------------------------------------------------------------- */
+/* KV-block push (the prefill-to-decode KV transfer of the pages: block ids  */
+/* are mapped to memory descriptors and contiguous blocks are merged into    */
+/* larger transfer regions before one write per region).                    */
+/* ---------------------------------------------------------------------- */
+
+/* Byte offset of token i of a request in a pool of blocks of `bs` tokens of
+ * `tok` bytes each, given the request's block table. */
+static int64_t kv_addr(int64_t i, int64_t tok, int64_t bs, const int32_t *blocks)
+{
+    return ((int64_t)blocks[i / bs] * bs + i % bs) * tok;
+}
+
+/* Regions of a request of n tokens: maximal runs of consecutive tokens
+ * whose source and destination bytes both continue where the previous
+ * token's ended. Writes up to n regions (src_off, dst_off, bytes) and
+ * returns their number. */
+int64_t oracle_kv_regions(int64_t n, int64_t tok, int64_t bs_src,
+                          const int32_t *src_blocks, int64_t bs_dst,
+                          const int32_t *dst_blocks, int64_t *src_off,
+                          int64_t *dst_off, int64_t *bytes)
+{
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t a = kv_addr(i, tok, bs_src, src_blocks);
+        int64_t b = kv_addr(i, tok, bs_dst, dst_blocks);
+        if (m > 0 && src_off[m - 1] + bytes[m - 1] == a &&
+            dst_off[m - 1] + bytes[m - 1] == b) {
+            bytes[m - 1] += tok;
+        } else {
+            src_off[m] = a;
+            dst_off[m] = b;
+            bytes[m] = tok;
+            ++m;
+        }
+    }
+    return m;
+}
+
+/* Apply the regions for every tensor-parallel rank r: rank r's pools start
+ * at r * src_rank_bytes and r * dst_rank_bytes. */
+void oracle_kv_copy(int ranks, int64_t m, const int64_t *src_off,
+                    const int64_t *dst_off, const int64_t *bytes,
+                    const uint8_t *src, int64_t src_rank_bytes, uint8_t *dst,
+                    int64_t dst_rank_bytes)
+{
+    for (int r = 0; r < ranks; ++r)
+        for (int64_t j = 0; j < m; ++j)
+            memcpy(dst + r * dst_rank_bytes + dst_off[j],
+                   src + r * src_rank_bytes + src_off[j], (size_t)bytes[j]);
+}
+
 int oracle_rounding_mode_is_nearest(void)
 {
     return fegetround() == FE_TONEAREST;

@@ -73,6 +73,15 @@ void oracle_combine_presum(int N, int T, int E, int R, int H, int64_t cap,
                            const uint16_t *y, const float *w, uint16_t *partial,
                            uint16_t *out);
 
+int64_t oracle_kv_regions(int64_t n, int64_t tok, int64_t bs_src,
+                          const int32_t *src_blocks, int64_t bs_dst,
+                          const int32_t *dst_blocks, int64_t *src_off,
+                          int64_t *dst_off, int64_t *bytes);
+void oracle_kv_copy(int ranks, int64_t m, const int64_t *src_off,
+                    const int64_t *dst_off, const int64_t *bytes,
+                    const uint8_t *src, int64_t src_rank_bytes, uint8_t *dst,
+                    int64_t dst_rank_bytes);
+
 int oracle_rounding_mode_is_nearest(void);
 
 #ifdef __cplusplus

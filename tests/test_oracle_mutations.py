@@ -66,6 +66,12 @@ MUTATIONS = {
     "presum_leader_is_last": ("        int leader = 1;\n        for (int k2 = 0; k2 < k; ++k2)",
                               "        int leader = 1;\n        for (int k2 = k + 1; k2 < R; ++k2)"),
     "presum_groups_by_expert": ("rank[k] = e / L;", "rank[k] = e;"),
+    "kv_src_only_contiguity": ("if (m > 0 && src_off[m - 1] + bytes[m - 1] == a &&\n            dst_off[m - 1] + bytes[m - 1] == b)",
+                               "if (m > 0 && src_off[m - 1] + bytes[m - 1] == a)"),
+    "kv_block_slot_dropped": ("return ((int64_t)blocks[i / bs] * bs + i % bs) * tok;",
+                              "return ((int64_t)blocks[i / bs] * bs) * tok;"),
+    "kv_copy_rank_stride": ("memcpy(dst + r * dst_rank_bytes + dst_off[j],",
+                            "memcpy(dst + dst_off[j],"),
     "quant_block_size": ("float a = fabsf(oracle_bf16_to_f32(x[b * 128 + i]));",
                          "float a = fabsf(oracle_bf16_to_f32(x[b * 128 + (i & 63)]));"),
 }
@@ -99,6 +105,10 @@ def _pin_checks():
         pins.test_presum_single_choice_is_the_rounded_product,
         pins.test_presum_one_rank_exact_sums_equal_the_plain_combine,
         pins.test_presum_partial_rows_sit_at_group_leaders,
+        pins.test_kv_regions_hand_worked_example,
+        lambda: pins.test_kv_regions_equal_block_sizes_count_block_runs(0),
+        pins.test_kv_regions_identity_tables_are_one_region,
+        lambda: pins.test_kv_copy_puts_each_token_where_the_tables_say(4, 16),
     ]
 
 

@@ -581,3 +581,78 @@ def test_presum_partial_rows_sit_at_group_leaders():
     partial, out = oracle.combine_presum(y, w, idx, p)
     assert out[0, 0, 0] == 0x3F80
     assert list(partial[0, :, 0]) == [BF16_2M8, BF16_ONE, 0]
+
+
+# ---------------------------------------------------------------------------
+# KV-block push: regions and the copy
+# ---------------------------------------------------------------------------
+
+def _read_kv_golden():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "kv_regions.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    n, tok, bs_src, bs_dst = map(int, rows[0])
+    src = np.array(rows[1], np.int32)
+    dst = np.array(rows[2], np.int32)
+    regions = np.array([list(map(int, r)) for r in rows[3:]], np.int64)
+    return n, tok, bs_src, src, bs_dst, dst, regions
+
+
+def test_kv_regions_hand_worked_example():
+    n, tok, bs_src, src, bs_dst, dst, want = _read_kv_golden()
+    np.testing.assert_array_equal(oracle.kv_regions(n, tok, bs_src, src, bs_dst, dst), want)
+
+
+def _block_runs(src, dst):
+    """Maximal runs of block indices where both tables step by one."""
+    breaks = (np.diff(src) != 1) | (np.diff(dst) != 1)
+    return 1 + int(breaks.sum())
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_kv_regions_equal_block_sizes_count_block_runs(seed):
+    """Same block size on both sides: a region can only break at a block
+    boundary, and does exactly where either table stops stepping by one."""
+    rng = np.random.default_rng(seed)
+    bs, tok = 4, 32
+    nb = 50
+    src = rng.permutation(200)[:nb].astype(np.int32)
+    src[10:20] = np.arange(70, 80)                     # a long adjacent stretch
+    dst = rng.permutation(300)[:nb].astype(np.int32)
+    dst[10:20] = np.arange(7, 17)
+    n = nb * bs - 3                                    # last block partly used
+    reg = oracle.kv_regions(n, tok, bs, src, bs, dst)
+    assert reg.shape[0] == _block_runs(src, dst)
+    assert reg[:, 2].sum() == n * tok
+
+
+def test_kv_regions_identity_tables_are_one_region():
+    n, tok = 1000, 48
+    reg = oracle.kv_regions(n, tok, 16, np.arange(63, dtype=np.int32), 1,
+                            np.arange(1000, dtype=np.int32))
+    np.testing.assert_array_equal(reg, [[0, 0, n * tok]])
+
+
+@pytest.mark.parametrize("bs_src,bs_dst", [(1, 1), (4, 16), (16, 4), (3, 5)])
+def test_kv_copy_puts_each_token_where_the_tables_say(bs_src, bs_dst):
+    """Pools as arrays [blocks, block_tokens, token_bytes]: after the copy,
+    destination token i (block dst[i / bs], slot i % bs) holds source token
+    i's bytes, on every rank; nothing else changes. Regions tile the tokens
+    in order and no two neighbours could be merged."""
+    rng = np.random.default_rng(bs_src * 31 + bs_dst)
+    ranks, tok, n = 3, 16, 97
+    nsb, ndb = 200 // bs_src + 40, 200 // bs_dst + 40
+    sblocks = rng.permutation(nsb)[: -(-n // bs_src)].astype(np.int32)
+    dblocks = rng.permutation(ndb)[: -(-n // bs_dst)].astype(np.int32)
+    sblocks[2:6] = np.arange(4) + nsb - 8 if len(sblocks) > 6 else sblocks[2:6]
+    src = rng.integers(0, 256, size=(ranks, nsb * bs_src * tok), dtype=np.uint8)
+    dst = rng.integers(0, 256, size=(ranks, ndb * bs_dst * tok), dtype=np.uint8)
+    reg = oracle.kv_regions(n, tok, bs_src, sblocks, bs_dst, dblocks)
+    got = oracle.kv_copy(reg, src, dst)
+    sv = src.reshape(ranks, nsb, bs_src, tok)
+    want = dst.copy().reshape(ranks, ndb, bs_dst, tok)
+    for i in range(n):
+        want[:, dblocks[i // bs_dst], i % bs_dst] = sv[:, sblocks[i // bs_src], i % bs_src]
+    np.testing.assert_array_equal(got, want.reshape(ranks, -1))
+    assert reg[:, 2].sum() == n * tok
+    ends = reg[:-1, :2] + reg[:-1, 2:3]
+    assert not ((ends[:, 0] == reg[1:, 0]) & (ends[:, 1] == reg[1:, 1])).any()
