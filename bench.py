@@ -274,6 +274,62 @@ def measure_presum(ep, torch, np, d, b, sh, wl, steps: int, warmup: int) -> dict
     }
 
 
+def measure_kv(ep, torch, np, W, reps: int = 10) -> dict:
+    """KV-block push of one 4096-token request to 8 tensor-parallel ranks:
+    merged regions, per-block descriptors, and the staged relay through
+    32 KiB x 64 bounce slots in device memory and in pinned host memory."""
+    import statistics as st
+
+    sh = W.KV_CONFIGS["kv_prompt4k"]
+    src_t, dst_t = W.make_kv_tables(sh)
+    tok = sh.token_bytes
+    src = torch.randint(0, 256, (sh.ranks, sh.src_pool_blocks * tok), dtype=torch.uint8,
+                        device="cuda")
+    dst = torch.zeros((sh.ranks, sh.dst_pool_blocks * tok), dtype=torch.uint8, device="cuda")
+    notify = torch.zeros(1, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    sp = s.cuda_stream
+    total = sh.tokens * tok
+    moved = 2 * total * sh.ranks            # read + write, all ranks
+    res = {"workload": (f"{sh.name}: {sh.tokens} tokens x {tok} B per rank, {sh.ranks} ranks, "
+                        f"page size 1, free-list runs of mean {sh.src_mean_run:g} (source) and "
+                        f"{sh.dst_mean_run:g} (destination) blocks"),
+           "bytes_per_push": moved}
+    bounce_dev = torch.empty(64 * 32768, dtype=torch.uint8, device="cuda")
+    bounce_host = torch.empty(64 * 32768, dtype=torch.uint8, pin_memory=True)
+    for name, merge, fn in (
+            ("merged", True, lambda r, m: ep.kv_push(sh.ranks, r, m, total, src, src.shape[1],
+                                                     dst, dst.shape[1], notify, status, sp)),
+            ("per_block", False, lambda r, m: ep.kv_push(sh.ranks, r, m, total, src, src.shape[1],
+                                                         dst, dst.shape[1], notify, status,
+                                                         sp)),
+            ("staged_device", True, lambda r, m: ep.kv_push_staged(
+                sh.ranks, r, m, total, src, src.shape[1], dst, dst.shape[1], bounce_dev, 64,
+                notify, status, sp)),
+            ("staged_pinned_host", True, lambda r, m: ep.kv_push_staged(
+                sh.ranks, r, m, total, src, src.shape[1], dst, dst.shape[1], bounce_host, 64,
+                notify, status, sp))):
+        reg = ep.kv_plan(sh.tokens, tok, 1, src_t, 1, dst_t, merge=merge)
+        reg_dev = torch.from_numpy(reg).cuda()
+        n = 2 if name == "staged_pinned_host" else reps
+        fn(reg_dev, len(reg))
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn(reg_dev, len(reg))
+            e1.record(s)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        t = st.median(ts)
+        res[name] = {"regions": int(len(reg)), "us": round(t, 1),
+                     "GBps": round(moved / t / 1e3, 1)}
+    res["notify_ok"] = int(notify.item()) == sh.ranks * (3 * reps + 4 + 2) and int(status.item()) == 0
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,6 +347,8 @@ def main() -> int:
                          "shared-expert stand-in on a second stream")
     ap.add_argument("--presum", action="store_true",
                     help="also measure the combine with partial sums on the expert side")
+    ap.add_argument("--kv", action="store_true",
+                    help="also measure the KV-block push (merged, per-block, staged)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0 = skip)")
     args = ap.parse_args()
@@ -409,6 +467,10 @@ def main() -> int:
     if args.presum:
         presum = measure_presum(ep, torch, np, d, b, sh, wl, args.steps, args.warmup)
 
+    kv = None
+    if args.kv:
+        kv = measure_kv(ep, torch, np, W)
+
     cpu = None
     if args.cpu_budget > 0:
         base = cpu_baseline(sh, wl, args.cpu_budget, quant)
@@ -482,6 +544,8 @@ def main() -> int:
         res["split"] = split
     if presum is not None:
         res["presum"] = presum
+    if kv is not None:
+        res["kv_push"] = kv
     print(json.dumps(res), flush=True)
     return 0
 

@@ -24,6 +24,7 @@ EP_ERR_DEVICE_MISMATCH = -3
 EP_ERR_HIP = -4
 EP_STATUS_BAD_EXPERT = 1
 EP_STATUS_CAPACITY = 2
+EP_STATUS_BAD_REGION = 4
 EP_PAYLOAD_BF16 = 0
 EP_PAYLOAD_FP8_B128 = 1
 
@@ -33,7 +34,8 @@ EXPORTS = (
     "ep_plan_bytes", "ep_plan_views", "ep_plan", "ep_dispatch_pack", "ep_dispatch_pack_quant",
     "ep_dispatch_transfer", "ep_dispatch_unpack", "ep_dispatch_recv",
     "ep_dispatch_send", "ep_dispatch_recv_split", "ep_expert_stub", "ep_combine",
-    "ep_combine_presum", "ep_probe_copy", "ep_status_string",
+    "ep_combine_presum", "ep_kv_plan", "ep_kv_push", "ep_kv_push_staged",
+    "ep_probe_copy", "ep_status_string",
     "ep_last_error",
 )
 
@@ -70,7 +72,7 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(LIB_PATH)
-    P, D = ctypes.c_void_p, ctypes.POINTER(Desc)
+    P, D, I64 = ctypes.c_void_p, ctypes.POINTER(Desc), ctypes.c_int64
     sig = {
         "ep_recv_bound": (ctypes.c_int64, [D]),
         "ep_capacity": (ctypes.c_int64, [D]),
@@ -89,6 +91,10 @@ def _load() -> ctypes.CDLL:
         "ep_expert_stub": (ctypes.c_int, [D, P, P, P, P, P]),
         "ep_combine": (ctypes.c_int, [D, P, P, P, P, P]),
         "ep_combine_presum": (ctypes.c_int, [D, P, P, P, P, P, P]),
+        "ep_kv_plan": (ctypes.c_int64, [I64, I64, I64, P, I64, P, ctypes.c_int32, P, I64]),
+        "ep_kv_push": (ctypes.c_int, [ctypes.c_int32, P, I64, I64, P, I64, P, I64, P, P, P]),
+        "ep_kv_push_staged": (ctypes.c_int, [ctypes.c_int32, P, I64, I64, P, I64, P, I64, P,
+                                             ctypes.c_int32, P, P, P]),
         "ep_probe_copy": (ctypes.c_int, [P, P, ctypes.c_size_t, P]),
         "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "ep_last_error": (ctypes.c_char_p, []),
@@ -248,6 +254,47 @@ def combine_presum(d: Desc, expert_out, weights, plan_ws, partial, out, stream=N
     _check(_lib.ep_combine_presum(ctypes.byref(d), _addr(expert_out), _addr(weights),
                                   _addr(plan_ws), _addr(partial), _addr(out), _stream(stream)),
            "ep_combine_presum")
+
+
+class KvRegion(ctypes.Structure):
+    """ep_kv_region: src_off, dst_off, bytes, first (int64 each)."""
+    _fields_ = [("src_off", ctypes.c_int64), ("dst_off", ctypes.c_int64),
+                ("bytes", ctypes.c_int64), ("first", ctypes.c_int64)]
+
+
+def kv_plan(n_tokens: int, token_bytes: int, src_block_tokens: int, src_blocks,
+            dst_block_tokens: int, dst_blocks, merge: bool = True):
+    """Host-only region planner; returns an int64 numpy array [m, 4] of
+    (src_off, dst_off, bytes, first)."""
+    import numpy as np
+    sb = np.ascontiguousarray(src_blocks, dtype=np.int32)
+    db = np.ascontiguousarray(dst_blocks, dtype=np.int32)
+    cap = max(int(n_tokens), 1)
+    out = np.zeros((cap, 4), np.int64)
+    m = _lib.ep_kv_plan(int(n_tokens), int(token_bytes), int(src_block_tokens),
+                        sb.ctypes.data, int(dst_block_tokens), db.ctypes.data, int(bool(merge)),
+                        out.ctypes.data, cap)
+    if m < 0:
+        raise EPError(int(m), "ep_kv_plan", _lib.ep_last_error().decode())
+    return out[:m].copy()
+
+
+def kv_push(ranks: int, regions, n_regions: int, total_bytes: int, src_pool, src_rank_bytes: int,
+            dst_pool, dst_rank_bytes: int, notify, status, stream=None) -> None:
+    _check(_lib.ep_kv_push(int(ranks), _addr(regions), int(n_regions), int(total_bytes),
+                           _addr(src_pool), int(src_rank_bytes), _addr(dst_pool),
+                           int(dst_rank_bytes), _addr(notify), _addr(status),
+                           _stream(stream)), "ep_kv_push")
+
+
+def kv_push_staged(ranks: int, regions, n_regions: int, total_bytes: int, src_pool,
+                   src_rank_bytes: int, dst_pool, dst_rank_bytes: int, bounce, bounce_slots: int,
+                   notify, status, stream=None) -> None:
+    _check(_lib.ep_kv_push_staged(int(ranks), _addr(regions), int(n_regions), int(total_bytes),
+                                  _addr(src_pool), int(src_rank_bytes), _addr(dst_pool),
+                                  int(dst_rank_bytes), _addr(bounce), int(bounce_slots),
+                                  _addr(notify), _addr(status), _stream(stream)),
+           "ep_kv_push_staged")
 
 
 def probe_copy(dst, src, nbytes: int, stream=None) -> None:

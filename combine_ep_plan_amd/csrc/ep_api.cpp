@@ -403,6 +403,110 @@ int ep_combine_presum(const ep_desc* d, const uint16_t* expert_out, const float*
   return EP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// KV-block push
+// ---------------------------------------------------------------------------
+
+int64_t ep_kv_plan(int64_t n, int64_t tok, int64_t bs_src, const int32_t* src_blocks,
+                   int64_t bs_dst, const int32_t* dst_blocks, int32_t merge,
+                   ep_kv_region* regions, int64_t max_regions) {
+  if (n < 0 || tok <= 0 || tok % 16 != 0 || bs_src <= 0 || bs_dst <= 0)
+    return fail(EP_ERR_INVALID_ARG, "ep_kv_plan: bad sizes (token_bytes must be a positive multiple of 16)");
+  if (n > 0 && (!src_blocks || !dst_blocks || !regions))
+    return fail(EP_ERR_INVALID_ARG, "ep_kv_plan: null table or output");
+  int64_t m = 0;
+  // Walk the request in spans that stay inside one source block and one
+  // destination block (contiguous on both sides by construction); a span
+  // extends the previous region when both its addresses continue it.
+  for (int64_t i = 0; i < n;) {
+    const int64_t sb = i / bs_src, so = i % bs_src, db = i / bs_dst, dof = i % bs_dst;
+    const int32_t bsrc = src_blocks[sb], bdst = dst_blocks[db];
+    if (bsrc < 0 || bdst < 0) return fail(EP_ERR_INVALID_ARG, "ep_kv_plan: negative block id");
+    int64_t span = bs_src - so;
+    if (bs_dst - dof < span) span = bs_dst - dof;
+    if (n - i < span) span = n - i;
+    const int64_t src_off = ((int64_t)bsrc * bs_src + so) * tok;
+    const int64_t dst_off = ((int64_t)bdst * bs_dst + dof) * tok;
+    ep_kv_region* prev = m > 0 ? &regions[m - 1] : nullptr;
+    if (merge && prev && prev->src_off + prev->bytes == src_off &&
+        prev->dst_off + prev->bytes == dst_off) {
+      prev->bytes += span * tok;
+    } else {
+      if (m >= max_regions) return fail(EP_ERR_INVALID_ARG, "ep_kv_plan: max_regions too small");
+      regions[m] = ep_kv_region{src_off, dst_off, span * tok, i * tok};
+      ++m;
+    }
+    i += span;
+  }
+  return m;
+}
+
+namespace {
+
+int kv_checks(int32_t ranks, const ep_kv_region* regions, int64_t m, int64_t total,
+              const void* src, int64_t src_rank_bytes, void* dst, int64_t dst_rank_bytes,
+              int32_t* notify, int32_t* status, int dev) {
+  if (ranks < 1 || m < 0 || total < 0 || total % 16 != 0 || src_rank_bytes < 0 ||
+      dst_rank_bytes < 0 || src_rank_bytes % 16 != 0 || dst_rank_bytes % 16 != 0)
+    return fail(EP_ERR_INVALID_ARG, "ep_kv_push: bad sizes (bytes must be multiples of 16)");
+  if (((uintptr_t)src | (uintptr_t)dst) & 15)
+    return fail(EP_ERR_INVALID_ARG, "ep_kv_push: pools must be 16-byte aligned");
+  const int64_t pieces = (total + ep::kv_piece_bytes() - 1) / ep::kv_piece_bytes();
+  if (pieces >= kMaxWaves / ranks) return fail(EP_ERR_UNSUPPORTED, "ep_kv_push: request too large");
+  EP_CHECK(check_ptr(regions, dev, "regions", m));
+  EP_CHECK(check_ptr(src, dev, "src_pool", src_rank_bytes * ranks));
+  EP_CHECK(check_ptr(dst, dev, "dst_pool", dst_rank_bytes * ranks));
+  EP_CHECK(check_ptr(notify, dev, "notify"));
+  EP_CHECK(check_ptr(status, dev, "status"));
+  return EP_OK;
+}
+
+// Device memory of `dev`, or pinned host memory.
+int check_bounce(const void* p, int dev) {
+  if (!p) return fail(EP_ERR_INVALID_ARG, "null pointer: bounce");
+  if (((uintptr_t)p) & 15) return fail(EP_ERR_INVALID_ARG, "bounce must be 16-byte aligned");
+  hipPointerAttribute_t a;
+  std::memset(&a, 0, sizeof a);
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(EP_ERR_INVALID_ARG, "bounce is neither device nor pinned host memory");
+  }
+  if (a.type == hipMemoryTypeHost) return EP_OK;
+  return check_ptr(p, dev, "bounce");
+}
+
+}  // namespace
+
+int ep_kv_push(int32_t ranks, const ep_kv_region* regions, int64_t m, int64_t total,
+               const void* src, int64_t src_rank_bytes, void* dst, int64_t dst_rank_bytes,
+               int32_t* notify, int32_t* status, hipStream_t stream) {
+  DeviceScope scope(stream);
+  if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");
+  EP_CHECK(kv_checks(ranks, regions, m, total, src, src_rank_bytes, dst, dst_rank_bytes, notify,
+                     status, scope.device()));
+  const hipError_t e = ep::launch_kv_push(ranks, regions, m, total, src, src_rank_bytes, dst,
+                                          dst_rank_bytes, notify, status, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_kv_push");
+  return EP_OK;
+}
+
+int ep_kv_push_staged(int32_t ranks, const ep_kv_region* regions, int64_t m, int64_t total,
+                      const void* src, int64_t src_rank_bytes, void* dst, int64_t dst_rank_bytes,
+                      void* bounce, int32_t slots, int32_t* notify, int32_t* status,
+                      hipStream_t stream) {
+  DeviceScope scope(stream);
+  if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");
+  EP_CHECK(kv_checks(ranks, regions, m, total, src, src_rank_bytes, dst, dst_rank_bytes, notify,
+                     status, scope.device()));
+  if (slots < 1 || slots > 64) return fail(EP_ERR_INVALID_ARG, "bounce_slots must be in [1, 64]");
+  EP_CHECK(check_bounce(bounce, scope.device()));
+  const hipError_t e = ep::launch_kv_push_staged(ranks, regions, m, total, src, src_rank_bytes,
+                                                 dst, dst_rank_bytes, bounce,
+                                                 (int64_t)slots * 32768, notify, status, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_kv_push_staged");
+  return EP_OK;
+}
+
 int ep_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   if (bytes % 16 != 0) return fail(EP_ERR_INVALID_ARG, "bytes must be a multiple of 16");
   if (bytes / 16 >= (size_t)kMaxWaves * 64 * 7)
@@ -427,6 +531,7 @@ const char* ep_status_string(int code) {
     case EP_STATUS_CAPACITY: return "receive capacity exceeded (rows dropped)";
     case EP_STATUS_BAD_EXPERT | EP_STATUS_CAPACITY:
       return "expert id out of range and receive capacity exceeded";
+    case EP_STATUS_BAD_REGION: return "KV region outside its pools (skipped)";
     default: return "unknown code";
   }
 }

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ep.h"
+
 namespace ep {
 
 // Sizes derived from a validated descriptor.
@@ -62,6 +64,16 @@ hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* w,
 hipError_t launch_combine_presum(const Dims& d, const uint16_t* y, const float* w,
                                  const PlanPtrs& p, uint16_t* partial, uint16_t* out,
                                  hipStream_t stream);
+// KV-block push (regions: device array of ep_kv_region).
+int64_t kv_piece_bytes();
+hipError_t launch_kv_push(int ranks, const ep_kv_region* reg, int64_t m, int64_t total,
+                          const void* src, int64_t src_rank_bytes, void* dst,
+                          int64_t dst_rank_bytes, int32_t* notify, int32_t* status,
+                          hipStream_t stream);
+hipError_t launch_kv_push_staged(int ranks, const ep_kv_region* reg, int64_t m, int64_t total,
+                                 const void* src, int64_t src_rank_bytes, void* dst,
+                                 int64_t dst_rank_bytes, void* bounce, int64_t round_bytes,
+                                 int32_t* notify, int32_t* status, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes,
                              hipStream_t stream);
 

@@ -1,0 +1,167 @@
+// KV-block push: the device side of the prefill-to-decode KV transfer.
+//
+// Method: "Disaggregated prefill/decode push connector" page, sections
+// "Protocol" and "Thread model": the producer maps a request's KV block ids
+// to memory descriptors, merges contiguous blocks into larger regions and
+// writes them to each destination tensor-parallel rank; every producer rank's
+// write carries a completion notification and the consumer counts them.
+// And "libfabric shm and SAR" (EFA intra-node page, section "SAR"): the
+// fallback path relays a message through 32 KiB bounce buffers, at most 64
+// per message round, with two copies per chunk.
+//
+// A request's regions, concatenated in token order, form a byte stream;
+// region j covers stream bytes [first_j, first_j + bytes_j). One wave moves
+// one 7 KB piece of the stream for one rank, walking the (few) regions that
+// overlap the piece. Every region is checked against the pools before any
+// byte moves; a bad one is skipped and flagged.
+#include "ep_device.hpp"
+#include "ep_kernels.hpp"
+
+namespace ep {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWavesPerBlock * kWave;
+constexpr int kKvV = 7;
+constexpr int64_t kPiece = (int64_t)kWave * kKvV * 16;  // 7 KB
+
+__device__ __forceinline__ int64_t wave_index64() {
+  return (int64_t)__builtin_amdgcn_readfirstlane(blockIdx.x) * kWavesPerBlock +
+         __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+__device__ __forceinline__ bool region_ok(const ep_kv_region& g, int64_t src_bytes,
+                                          int64_t dst_bytes) {
+  return g.bytes >= 0 && g.src_off >= 0 && g.dst_off >= 0 && g.first >= 0 &&
+         ((g.bytes | g.src_off | g.dst_off | g.first) & 15) == 0 &&
+         g.src_off <= src_bytes - g.bytes && g.dst_off <= dst_bytes - g.bytes;
+}
+
+// Copy n16 (<= 448) 16-byte chunks with the wave.
+__device__ __forceinline__ void wave_copy(const uint8_t* src, uint8_t* dst, int n16) {
+  if (n16 <= 0) return;
+  if (n16 > kWave) {
+    RowRegs<kKvV> r;
+    load_row16(r, (const u32x4*)src, 0, n16);
+    store_row16(r, (u32x4*)dst, 0, n16);
+  } else {
+    RowRegs<1> r;
+    load_row16(r, (const u32x4*)src, 0, n16);
+    store_row16(r, (u32x4*)dst, 0, n16);
+  }
+}
+
+// Where the stream goes to or comes from: the region mapping into a pool,
+// or a plain linear buffer (the bounce slots) starting at stream byte `lin0`.
+struct KvSide {
+  uint8_t* base;      // pool (rank 0) or linear buffer
+  int64_t rank_bytes; // pool bytes per rank (0 for a linear buffer)
+  bool linear;
+};
+
+// Moves stream bytes [lo, hi) of rank r from `from` to `to` (one of them
+// mapped by the regions, possibly both). Regions are in stream order.
+__global__ __launch_bounds__(kBlock) void kv_copy_kernel(
+    const ep_kv_region* __restrict__ reg, int64_t m, int64_t lo, int64_t hi, int ranks,
+    KvSide from, KvSide to, int64_t src_pool_bytes, int64_t dst_pool_bytes, int32_t* status) {
+  const int64_t pieces = (hi - lo + kPiece - 1) / kPiece;
+  const int64_t w = wave_index64();
+  if (w >= pieces * ranks) return;
+  const int r = (int)(w / pieces);
+  const int64_t p0 = lo + (w - (int64_t)r * pieces) * kPiece;
+  const int64_t p1 = p0 + kPiece < hi ? p0 + kPiece : hi;
+  // first region ending after p0
+  int64_t a = 0, b = m;
+  while (a < b) {
+    const int64_t mid = (a + b) >> 1;
+    if (reg[mid].first + reg[mid].bytes <= p0) a = mid + 1; else b = mid;
+  }
+  bool bad = false;
+  for (int64_t j = a; j < m; ++j) {
+    const ep_kv_region g = reg[j];
+    if (g.first >= p1) break;
+    if (!region_ok(g, src_pool_bytes, dst_pool_bytes)) {
+      bad = true;
+      continue;
+    }
+    const int64_t s = g.first > p0 ? g.first : p0;
+    const int64_t e = g.first + g.bytes < p1 ? g.first + g.bytes : p1;
+    if (e <= s) continue;
+    const int64_t in_reg = s - g.first;
+    const uint8_t* src = from.linear
+                             ? from.base + (s - lo)
+                             : from.base + r * from.rank_bytes + g.src_off + in_reg;
+    uint8_t* dst = to.linear ? to.base + (s - lo) : to.base + r * to.rank_bytes + g.dst_off + in_reg;
+    wave_copy(src, dst, (int)((e - s) >> 4));
+  }
+  if (bad && lane_id() == 0) atomicOr(status, EP_STATUS_BAD_REGION);
+}
+
+// Completion: one notification per producer rank, enqueued after the
+// rank's copies (stream order makes its bytes visible first). A fence and a
+// counter per copying wave instead would write back the L2 of the wave's
+// XCD once per wave, which measured 25x slower than the copy itself.
+__global__ void kv_notify_kernel(int32_t* notify, int ranks) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < ranks) atomicAdd(notify, 1);
+}
+
+unsigned blocks_for(int64_t waves) {
+  return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+
+hipError_t notify_ranks(int ranks, int32_t* notify, hipStream_t stream) {
+  hipLaunchKernelGGL(kv_notify_kernel, dim3((ranks + 255) / 256), dim3(256), 0, stream, notify,
+                     ranks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t kv_piece_bytes() { return kPiece; }
+
+hipError_t launch_kv_push(int ranks, const ep_kv_region* reg, int64_t m, int64_t total,
+                          const void* src, int64_t src_rank_bytes, void* dst,
+                          int64_t dst_rank_bytes, int32_t* notify, int32_t* status,
+                          hipStream_t stream) {
+  if (total > 0) {
+    const int64_t pieces = (total + kPiece - 1) / kPiece;
+    const KvSide from{(uint8_t*)src, src_rank_bytes, false};
+    const KvSide to{(uint8_t*)dst, dst_rank_bytes, false};
+    hipLaunchKernelGGL(kv_copy_kernel, dim3(blocks_for(pieces * ranks)), dim3(kBlock), 0, stream,
+                       reg, m, (int64_t)0, total, ranks, from, to, src_rank_bytes,
+                       dst_rank_bytes, status);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return notify_ranks(ranks, notify, stream);
+}
+
+hipError_t launch_kv_push_staged(int ranks, const ep_kv_region* reg, int64_t m, int64_t total,
+                                 const void* src, int64_t src_rank_bytes, void* dst,
+                                 int64_t dst_rank_bytes, void* bounce, int64_t round_bytes,
+                                 int32_t* notify, int32_t* status, hipStream_t stream) {
+  const KvSide lin{(uint8_t*)bounce, 0, true};
+  // One message per rank, relayed round by round: sender copy into the
+  // bounce slots, then receiver copy out of them (stream order stands in
+  // for the FULL / EMPTY flags of the slots).
+  for (int r = 0; r < ranks && total > 0; ++r) {
+    const KvSide s{(uint8_t*)src + r * src_rank_bytes, src_rank_bytes, false};
+    const KvSide d{(uint8_t*)dst + r * dst_rank_bytes, dst_rank_bytes, false};
+    for (int64_t lo = 0; lo < total; lo += round_bytes) {
+      const int64_t hi = lo + round_bytes < total ? lo + round_bytes : total;
+      const unsigned grid = blocks_for((hi - lo + kPiece - 1) / kPiece);
+      hipLaunchKernelGGL(kv_copy_kernel, dim3(grid), dim3(kBlock), 0, stream, reg, m, lo, hi, 1,
+                         s, lin, src_rank_bytes, dst_rank_bytes, status);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kv_copy_kernel, dim3(grid), dim3(kBlock), 0, stream, reg, m, lo, hi, 1,
+                         lin, d, src_rank_bytes, dst_rank_bytes, status);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return notify_ranks(ranks, notify, stream);
+}
+
+}  // namespace ep

@@ -176,3 +176,58 @@ def make_workload(sh: Shape, idx: Optional[np.ndarray] = None) -> Workload:
     else:
         raise ValueError(sh.payload)
     return Workload(sh, idx, weights, x_bf16, planes, alpha)
+
+
+# ---------------------------------------------------------------------------
+# KV-block push workloads (the prefill-to-decode KV transfer)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class KvShape:
+    """One request's KV moved to `ranks` tensor-parallel ranks. Each side
+    keeps a pool of `*_pool_blocks` blocks of `*_block_tokens` tokens of
+    `token_bytes` bytes (all layers of a token together); its free list is
+    fragmented into runs of consecutive blocks with the given mean length."""
+    name: str
+    ranks: int
+    tokens: int
+    token_bytes: int
+    src_block_tokens: int
+    dst_block_tokens: int
+    src_pool_blocks: int
+    dst_pool_blocks: int
+    src_mean_run: float = 256.0
+    dst_mean_run: float = 32.0
+    seed: int = 0
+
+
+KV_CONFIGS = {
+    "kv_tiny": KvShape("kv_tiny", 2, 37, 64, 4, 1, 40, 120, 3.0, 2.0),
+    # page size 1 on both sides (the measured serving setting of the pages),
+    # a 4096-token prompt, 40 KiB per token per rank (80 layers x 8 KV heads x
+    # 128 x K,V x bf16 over 8 tensor-parallel ranks), 8 ranks
+    "kv_prompt4k": KvShape("kv_prompt4k", 8, 4096, 40960, 1, 1, 16384, 16384, 256.0, 32.0),
+}
+
+
+def _free_list(rng: np.random.Generator, blocks: int, mean_run: float) -> np.ndarray:
+    """Pool block ids cut into runs of consecutive ids (geometric lengths of
+    the given mean), runs in random order."""
+    cuts, pos = [], 0
+    while pos < blocks:
+        n = int(rng.geometric(1.0 / max(mean_run, 1.0)))
+        cuts.append((pos, min(blocks, pos + n)))
+        pos += n
+    order = rng.permutation(len(cuts))
+    return np.concatenate([np.arange(*cuts[i]) for i in order]).astype(np.int32)
+
+
+def make_kv_tables(sh: KvShape):
+    """Block tables (source, destination) of the request."""
+    rng = np.random.default_rng(sh.seed)
+    ns = -(-sh.tokens // sh.src_block_tokens)
+    nd = -(-sh.tokens // sh.dst_block_tokens)
+    src = _free_list(rng, sh.src_pool_blocks, sh.src_mean_run)[:ns]
+    dst = _free_list(rng, sh.dst_pool_blocks, sh.dst_mean_run)[:nd]
+    assert len(src) == ns and len(dst) == nd, "pool too small for the request"
+    return src, dst

@@ -67,6 +67,7 @@ extern "C" {
 /* Device status bits, OR-ed into *status by ep_plan. */
 #define EP_STATUS_BAD_EXPERT 1 /* an expert id outside [0, E): slot dropped */
 #define EP_STATUS_CAPACITY 2   /* a rank would receive more than cap rows */
+#define EP_STATUS_BAD_REGION 4 /* a KV region outside its pools: skipped */
 
 /* Payload formats of the dispatched rows. */
 #define EP_PAYLOAD_BF16 0     /* one plane: H bf16 values, 2H bytes per row */
@@ -234,6 +235,69 @@ EP_API int ep_dispatch_recv_split(const ep_desc *d, const void *const send[2],
                                   void *const priv[2], int32_t priv_rows,
                                   void *plan_ws, void *const grouped[2],
                                   int32_t *status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * KV-block push ("Disaggregated prefill/decode push connector" page,
+ * sections "Protocol" and "Thread model": the producer maps a request's KV
+ * block ids to memory descriptors, merges contiguous blocks into larger
+ * regions, writes them to every destination tensor-parallel rank, and each
+ * producer rank's write carries a completion notification that the
+ * consumer counts).
+ *
+ * Token i of a request lives at byte (blocks[i / block_tokens] *
+ * block_tokens + i % block_tokens) * token_bytes of a pool, on each side
+ * with its own block size and block table. A region moves `bytes` bytes
+ * from src_off to dst_off; `first` is its offset in the request's byte
+ * stream (the regions in token order, concatenated).
+ * ---------------------------------------------------------------------- */
+typedef struct ep_kv_region {
+  int64_t src_off;
+  int64_t dst_off;
+  int64_t bytes;
+  int64_t first;
+} ep_kv_region;
+
+/* Host only. Regions of one request of n_tokens tokens, in token order.
+ * merge != 0: maximal runs (a region grows while the next token continues
+ * on both sides); merge == 0: one region per piece of a source block that
+ * lies in one destination block (the descriptors before merging).
+ * token_bytes must be a positive multiple of 16; block sizes positive; ids
+ * non-negative. Writes at most max_regions regions and returns their number,
+ * or a negative EP_ERR_* code (EP_ERR_INVALID_ARG also when max_regions is
+ * too small; n_tokens regions always suffice). */
+EP_API int64_t ep_kv_plan(int64_t n_tokens, int64_t token_bytes,
+                          int64_t src_block_tokens, const int32_t *src_blocks,
+                          int64_t dst_block_tokens, const int32_t *dst_blocks,
+                          int32_t merge, ep_kv_region *regions,
+                          int64_t max_regions);
+
+/* Device push of one request to `ranks` tensor-parallel ranks: rank r's
+ * pools start at src_pool + r * src_rank_bytes and dst_pool +
+ * r * dst_rank_bytes. regions: device array [n_regions] from ep_kv_plan;
+ * total_bytes: their byte sum (a multiple of 16). notify: device int32 the
+ * caller zeroes; each rank adds 1 once all its bytes are written (in stream
+ * order after the copy), so the request has arrived when notify == ranks. A region that does not fit its pools (or is
+ * not 16-byte aligned) is skipped and sets EP_STATUS_BAD_REGION in status. */
+EP_API int ep_kv_push(int32_t ranks, const ep_kv_region *regions,
+                      int64_t n_regions, int64_t total_bytes,
+                      const void *src_pool, int64_t src_rank_bytes,
+                      void *dst_pool, int64_t dst_rank_bytes,
+                      int32_t *notify, int32_t *status, hipStream_t stream);
+
+/* The staged relay for comparison (EFA intra-node page, section "SAR":
+ * segmentation and reassembly through bounce buffers of 32 KiB, at most 64
+ * per message round, two copies per chunk): each rank's byte stream goes
+ * round by round through `bounce` (device or pinned host memory of
+ * bounce_slots * 32 KiB bytes, 1 <= bounce_slots <= 64), a sender copy into
+ * the slots, then a receiver copy out of them. Same result and completion
+ * counting as ep_kv_push. */
+EP_API int ep_kv_push_staged(int32_t ranks, const ep_kv_region *regions,
+                             int64_t n_regions, int64_t total_bytes,
+                             const void *src_pool, int64_t src_rank_bytes,
+                             void *dst_pool, int64_t dst_rank_bytes,
+                             void *bounce, int32_t bounce_slots,
+                             int32_t *notify, int32_t *status,
+                             hipStream_t stream);
 
 /* Stand-in for the grouped GEMM (outside the method; used by tests and the
  * benchmark to produce expert outputs). expert_out is bf16 [N][cap][H].
