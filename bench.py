@@ -46,33 +46,42 @@ def algorithmic_bytes(sh, row_d: int, quant: bool) -> dict:
     return {"stages": stages, "step": sum(stages.values())}
 
 
-def kernel_source_hash() -> str:
-    """Hash of the device sources (kernels and device headers), to tell
-    whether recorded counters still apply."""
-    import glob
+# Device sources each stage's kernels are built from (recorded counters of a
+# kernel stay valid while these files are unchanged).
+STAGE_SOURCES = {
+    "plan": ["ep_plan.hip", "ep_kernels.hpp", "ep_device.hpp"],
+    "pack": ["ep_dispatch.hip", "ep_device.hpp"],
+    "pack_quant": ["ep_quant.hip", "ep_device.hpp"],
+    "recv": ["ep_dispatch.hip", "ep_device.hpp"],
+    "combine": ["ep_combine.hip", "ep_device.hpp"],
+}
+
+
+def kernel_source_hash(files) -> str:
+    """Hash of the named device sources under combine_ep_plan_amd/csrc."""
     import hashlib
 
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "combine_ep_plan_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(ROOT, "combine_ep_plan_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, or None if there is none or the kernels changed since."""
+def recorded_traffic(workload: str, stage: str):
+    """HBM bytes per launch of the stage's kernel from the committed
+    rocprofv3 counter summary of this workload, or None if there is none or
+    the kernel's sources changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_sha256_16") != kernel_source_hash():
+    k = rec.get("stages", {}).get(stage)
+    if k is None or k.get("source_sha256_16") != kernel_source_hash(STAGE_SOURCES[stage]):
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k["traffic_bytes"]
+    return k["traffic_bytes"]
 
 
 def cpu_baseline(sh, wl, budget_s: float, quant: bool) -> dict:
@@ -532,7 +541,8 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": recorded_traffic(args.config, f"{dom}_kernel"),
+            "traffic": recorded_traffic(args.config, "pack_quant" if dom == "pack" and quant
+                                        else dom),
             "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
             "algorithmic_bytes": ab["stages"][dom],
             "avg_us": round(dom_ms * 1e3, 2),
