@@ -284,17 +284,19 @@ def measure_presum(ep, torch, np, d, b, sh, wl, steps: int, warmup: int) -> dict
 
 
 def measure_kv(ep, torch, np, W, reps: int = 10) -> dict:
-    """KV-block push of one 4096-token request to 8 tensor-parallel ranks:
-    merged regions, per-block descriptors, and the staged relay through
-    32 KiB x 64 bounce slots in device memory and in pinned host memory."""
+    """KV-block push of one 16k-token request to 8 tensor-parallel ranks
+    (Qwen3-32B shapes, 16-token blocks): merged regions, per-block
+    descriptors, and the staged relay through 32 KiB x 64 bounce slots in
+    device memory and in pinned host memory."""
     import statistics as st
 
-    sh = W.KV_CONFIGS["kv_prompt4k"]
+    sh = W.KV_CONFIGS["kv_qwen32b_16k"]
     src_t, dst_t = W.make_kv_tables(sh)
     tok = sh.token_bytes
-    src = torch.randint(0, 256, (sh.ranks, sh.src_pool_blocks * tok), dtype=torch.uint8,
+    bs, bd = sh.src_block_tokens, sh.dst_block_tokens
+    src = torch.randint(0, 256, (sh.ranks, sh.src_pool_blocks * bs * tok), dtype=torch.uint8,
                         device="cuda")
-    dst = torch.zeros((sh.ranks, sh.dst_pool_blocks * tok), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros((sh.ranks, sh.dst_pool_blocks * bd * tok), dtype=torch.uint8, device="cuda")
     notify = torch.zeros(1, dtype=torch.int32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     s = torch.cuda.current_stream()
@@ -302,8 +304,8 @@ def measure_kv(ep, torch, np, W, reps: int = 10) -> dict:
     total = sh.tokens * tok
     moved = 2 * total * sh.ranks            # read + write, all ranks
     res = {"workload": (f"{sh.name}: {sh.tokens} tokens x {tok} B per rank, {sh.ranks} ranks, "
-                        f"page size 1, free-list runs of mean {sh.src_mean_run:g} (source) and "
-                        f"{sh.dst_mean_run:g} (destination) blocks"),
+                        f"{bs}-token blocks, free-list runs of mean {sh.src_mean_run:g} (source) "
+                        f"and {sh.dst_mean_run:g} (destination) blocks"),
            "bytes_per_push": moved}
     bounce_dev = torch.empty(64 * 32768, dtype=torch.uint8, device="cuda")
     bounce_host = torch.empty(64 * 32768, dtype=torch.uint8, pin_memory=True)
@@ -319,7 +321,7 @@ def measure_kv(ep, torch, np, W, reps: int = 10) -> dict:
             ("staged_pinned_host", True, lambda r, m: ep.kv_push_staged(
                 sh.ranks, r, m, total, src, src.shape[1], dst, dst.shape[1], bounce_host, 64,
                 notify, status, sp))):
-        reg = ep.kv_plan(sh.tokens, tok, 1, src_t, 1, dst_t, merge=merge)
+        reg = ep.kv_plan(sh.tokens, tok, bs, src_t, bd, dst_t, merge=merge)
         reg_dev = torch.from_numpy(reg).cuda()
         n = 2 if name == "staged_pinned_host" else reps
         fn(reg_dev, len(reg))

@@ -1,11 +1,12 @@
 // KV-block push: the device side of the prefill-to-decode KV transfer.
 //
-// Method: "Disaggregated prefill/decode push connector" page, sections
-// "Protocol" and "Thread model": the producer maps a request's KV block ids
-// to memory descriptors, merges contiguous blocks into larger regions and
-// writes them to each destination tensor-parallel rank; every producer rank's
-// write carries a completion notification and the consumer counts them.
-// And "libfabric shm and SAR" (EFA intra-node page, section "SAR"): the
+// Method: "vLLMにおける分離型推論のTTFTとTPOTを改善するプッシュ型KV転送" (push-mode
+// KV transfer for disaggregated vLLM serving), sections 「実装の詳細」 and
+// 「スレッドモデル」: the producer maps a request's KV block ids to memory
+// descriptors, merges contiguous blocks into larger regions and writes them
+// to each destination tensor-parallel rank; each producer rank's write
+// carries a completion notification and the consumer counts them.
+// And "EFA の同じノード内の GPU 間通信: libfabric の shm と SAR", section 「SAR」: the
 // fallback path relays a message through 32 KiB bounce buffers, at most 64
 // per message round, with two copies per chunk.
 //

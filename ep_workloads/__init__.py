@@ -203,10 +203,16 @@ class KvShape:
 
 KV_CONFIGS = {
     "kv_tiny": KvShape("kv_tiny", 2, 37, 64, 4, 1, 40, 120, 3.0, 2.0),
-    # page size 1 on both sides (the measured serving setting of the pages),
-    # a 4096-token prompt, 40 KiB per token per rank (80 layers x 8 KV heads x
-    # 128 x K,V x bf16 over 8 tensor-parallel ranks), 8 ranks
-    "kv_prompt4k": KvShape("kv_prompt4k", 8, 4096, 40960, 1, 1, 16384, 16384, 256.0, 32.0),
+    # The push-connector page's setting: Qwen3-32B served with tensor
+    # parallelism 8 (64 layers, 8 KV heads of 128, bf16: one KV head per
+    # rank, K and V, 64 x 2 x 128 x 2 B = 32 KiB per token per rank), a
+    # 16k-token prompt (the longest of its 1k-16k sweep), vLLM's 16-token
+    # blocks; free lists fragmented into runs of 64 (prefill) and 8 (decode)
+    # blocks on average.
+    "kv_qwen32b_16k": KvShape("kv_qwen32b_16k", 8, 16384, 32768, 16, 16, 2048, 2048, 64.0, 8.0),
+    # The same request size with page size 1 (the SGLang setting of the
+    # shm / SAR page), 4096 tokens.
+    "kv_page1_4k": KvShape("kv_page1_4k", 8, 4096, 32768, 1, 1, 16384, 16384, 256.0, 32.0),
 }
 
 

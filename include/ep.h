@@ -237,12 +237,12 @@ EP_API int ep_dispatch_recv_split(const ep_desc *d, const void *const send[2],
                                   int32_t *status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * KV-block push ("Disaggregated prefill/decode push connector" page,
- * sections "Protocol" and "Thread model": the producer maps a request's KV
- * block ids to memory descriptors, merges contiguous blocks into larger
- * regions, writes them to every destination tensor-parallel rank, and each
- * producer rank's write carries a completion notification that the
- * consumer counts).
+ * KV-block push ("vLLMにおける分離型推論のTTFTとTPOTを改善するプッシュ型KV転送",
+ * sections 「実装の詳細」 and 「スレッドモデル」: the producer maps a
+ * request's KV block ids to memory descriptors, merges contiguous blocks
+ * into larger regions, writes them to every destination tensor-parallel
+ * rank, and each producer rank's write carries a completion notification
+ * that the consumer counts).
  *
  * Token i of a request lives at byte (blocks[i / block_tokens] *
  * block_tokens + i % block_tokens) * token_bytes of a pool, on each side
@@ -284,7 +284,7 @@ EP_API int ep_kv_push(int32_t ranks, const ep_kv_region *regions,
                       void *dst_pool, int64_t dst_rank_bytes,
                       int32_t *notify, int32_t *status, hipStream_t stream);
 
-/* The staged relay for comparison (EFA intra-node page, section "SAR":
+/* The staged relay for comparison ("EFA の同じノード内の GPU 間通信: libfabric の shm と SAR", section 「SAR」:
  * segmentation and reassembly through bounce buffers of 32 KiB, at most 64
  * per message round, two copies per chunk): each rank's byte stream goes
  * round by round through `bounce` (device or pinned host memory of

@@ -595,9 +595,10 @@ void oracle_combine_presum(int N, int T, int E, int R, int H, int64_t cap,
 }
 
 /* ---------------------------------------------------------------------- */
-/* KV-block push (the prefill-to-decode KV transfer of the pages: block ids  */
-/* are mapped to memory descriptors and contiguous blocks are merged into    */
-/* larger transfer regions before one write per region).                    */
+/* KV-block push ("vLLMにおける分離型推論のTTFTとTPOTを改善するプッシュ型KV転送",   */
+/* 「スレッドモデル」: block ids are mapped to memory descriptors and        */
+/* contiguous blocks are merged into larger transfer regions, one write per  */
+/* region).                                                                  */
 /* ---------------------------------------------------------------------- */
 
 /* Byte offset of token i of a request in a pool of blocks of `bs` tokens of

@@ -125,24 +125,29 @@ def test_kv_push_rejects_bad_arguments():
                           torch.empty(32768, dtype=torch.uint8), 1, z, z)
 
 
-@pytest.mark.parametrize("mode", ["direct", "staged"])
-def test_kv_push_full_size(mode):
-    sh = W.KV_CONFIGS["kv_prompt4k"]
+@pytest.mark.parametrize("name,mode", [("kv_qwen32b_16k", "direct"), ("kv_qwen32b_16k", "staged"),
+                                       ("kv_page1_4k", "direct")])
+def test_kv_push_full_size(name, mode):
+    """Whole request on the device: every token's block slot on the
+    destination holds its source bytes (torch gather), nothing else is
+    written; the planner's regions equal the oracle's."""
+    sh = W.KV_CONFIGS[name]
     note(f"kv full-size {sh.name} {mode}")
     src_t, dst_t = W.make_kv_tables(sh)
-    reg = ep.kv_plan(sh.tokens, sh.token_bytes, 1, src_t, 1, dst_t)
-    np.testing.assert_array_equal(reg[:, :3], oracle.kv_regions(sh.tokens, sh.token_bytes, 1,
-                                                                src_t, 1, dst_t))
-    tok = sh.token_bytes
-    src = torch.randint(0, 256, (sh.ranks, sh.src_pool_blocks * tok), dtype=torch.uint8,
+    bs, bd, tok = sh.src_block_tokens, sh.dst_block_tokens, sh.token_bytes
+    reg = ep.kv_plan(sh.tokens, tok, bs, src_t, bd, dst_t)
+    np.testing.assert_array_equal(reg[:, :3], oracle.kv_regions(sh.tokens, tok, bs, src_t, bd,
+                                                                dst_t))
+    src = torch.randint(0, 256, (sh.ranks, _pool_bytes(sh, "src")), dtype=torch.uint8,
                         device="cuda")
-    dst = torch.zeros((sh.ranks, sh.dst_pool_blocks * tok), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros((sh.ranks, _pool_bytes(sh, "dst")), dtype=torch.uint8, device="cuda")
     assert push(sh, reg, src, dst, mode) == (sh.ranks, 0)
-    sv = src.view(sh.ranks, sh.src_pool_blocks, tok)
-    dv = dst.view(sh.ranks, sh.dst_pool_blocks, tok)
-    st = torch.from_numpy(src_t.astype(np.int64)).cuda()
-    dt = torch.from_numpy(dst_t.astype(np.int64)).cuda()
+    i = torch.arange(sh.tokens, device="cuda")
+    st = torch.from_numpy(src_t.astype(np.int64)).cuda()[i // bs] * bs + i % bs
+    dt = torch.from_numpy(dst_t.astype(np.int64)).cuda()[i // bd] * bd + i % bd
+    sv = src.view(sh.ranks, -1, tok)
+    dv = dst.view(sh.ranks, -1, tok)
     assert torch.equal(dv[:, dt], sv[:, st])
-    untouched = torch.ones(sh.dst_pool_blocks, dtype=torch.bool, device="cuda")
+    untouched = torch.ones(dv.shape[1], dtype=torch.bool, device="cuda")
     untouched[dt] = False
     assert not dv[:, untouched].any()
