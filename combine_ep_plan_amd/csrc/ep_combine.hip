@@ -6,8 +6,9 @@
 // their routing-weighted average into the output tensor; accumulation
 // happens on the receiving (source) side only.
 //
-// Two waves per output token, each owning alternate column blocks of 64 x 7
-// 16-byte chunks (for H = 7168 each wave takes one half of the row). Per
+// Two waves per output token (seven at prefill scale, see launch_combine),
+// each owning alternate column blocks of 64 x V 16-byte chunks (for H = 7168
+// and V = 7 each wave takes one half of the row). Per
 // block the wave loads two of the token's expert rows at a time (both in
 // flight) and accumulates w_k * y_k in fp32 with fused multiply-adds in k
 // order, then rounds once to bf16 (nearest, ties to even) and stores 16
@@ -42,44 +43,48 @@ __device__ __forceinline__ void fma_row(float (&acc)[V][8], const RowRegs<V>& r,
   }
 }
 
-__device__ __forceinline__ void store_acc(float (&acc)[kCombV][8], u32x4* o, int base, int n16) {
-  RowRegs<kCombV> res;
+template <int V>
+__device__ __forceinline__ void store_acc(float (&acc)[V][8], u32x4* o, int base, int n16) {
+  RowRegs<V> res;
 #pragma unroll
-  for (int i = 0; i < kCombV; ++i)
+  for (int i = 0; i < V; ++i)
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       res.v[i][h] = f32_to_bf16_bits(acc[i][2 * h]) | (f32_to_bf16_bits(acc[i][2 * h + 1]) << 16);
   store_row16(res, o, base, n16);
 }
 
+// V chunks per lane per column block, W waves per token, ROWS expert rows
+// in flight per wave.
+template <int V, int W, int ROWS>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const uint16_t* y, const float* w,
                                                          const int32_t* comb_row, uint16_t* out,
                                                          int NT, int R, int H, int64_t rows_in) {
   const int wv = wave_index();
-  const int tok = wv / kCombWaves;
-  const int part = wv % kCombWaves;
+  const int tok = wv / W;
+  const int part = wv % W;
   if (tok >= NT) return;
   const int32_t* rows = comb_row + (size_t)tok * R;
   const float* wt = w + (size_t)tok * R;
   const int n16 = H / 8;
   const u32x4* ybase = (const u32x4*)y;
   u32x4* o = (u32x4*)(out + (size_t)tok * H);
-  for (int base = part * kWave * kCombV; base < n16; base += kCombWaves * kWave * kCombV) {
-    float acc[kCombV][8];
+  for (int base = part * kWave * V; base < n16; base += W * kWave * V) {
+    float acc[V][8];
 #pragma unroll
-    for (int i = 0; i < kCombV; ++i)
+    for (int i = 0; i < V; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-    for (int k0 = 0; k0 < R; k0 += kCombRows) {
-      // Rows k0 .. k0 + kCombRows - 1: loads of all in flight, then the FMAs.
+    for (int k0 = 0; k0 < R; k0 += ROWS) {
+      // Rows k0 .. k0 + ROWS - 1: loads of all in flight, then the FMAs.
       // Rows outside [0, rows_in) (dropped slots) contribute nothing.
-      RowRegs<kCombV> v[kCombRows];
+      RowRegs<V> v[ROWS];
 #pragma unroll
-      for (int b = 0; b < kCombRows; ++b)
+      for (int b = 0; b < ROWS; ++b)
         if (k0 + b < R && rows[k0 + b] >= 0 && rows[k0 + b] < rows_in)
           load_row16(v[b], ybase + (size_t)rows[k0 + b] * n16, base, n16);
 #pragma unroll
-      for (int b = 0; b < kCombRows; ++b)
+      for (int b = 0; b < ROWS; ++b)
         if (k0 + b < R && rows[k0 + b] >= 0 && rows[k0 + b] < rows_in)
           fma_row(acc, v[b], wt[k0 + b]);
     }
@@ -248,11 +253,22 @@ unsigned blocks_for(int64_t waves) {
 
 }  // namespace
 
+// Shape by token count, as measured on gfx950: at decode scale (4096 tokens)
+// two waves of 7 chunks per lane per token ran 87-88 us and seven waves of 2
+// chunks 88-89 us; at prefill scale (32768 tokens) the seven-wave form ran
+// 696 us against 721-723 us. Both give identical bytes (same FMA order).
 hipError_t launch_combine(const Dims& d, const uint16_t* y, const float* w, const PlanPtrs& p,
                           uint16_t* out, hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(d.NT * kCombWaves)), dim3(kBlock), 0,
-                     stream, y, w, p.comb_row, out, (int)d.NT, d.R, d.H, (int64_t)d.N * d.cap);
+  const int64_t rows_in = (int64_t)d.N * d.cap;
+  if (d.NT >= 16384) {
+    hipLaunchKernelGGL((combine_kernel<2, 7, 2>), dim3(blocks_for(d.NT * 7)), dim3(kBlock), 0,
+                       stream, y, w, p.comb_row, out, (int)d.NT, d.R, d.H, rows_in);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<kCombV, kCombWaves, kCombRows>),
+                       dim3(blocks_for(d.NT * kCombWaves)), dim3(kBlock), 0, stream, y, w,
+                       p.comb_row, out, (int)d.NT, d.R, d.H, rows_in);
+  }
   return hipGetLastError();
 }
 
