@@ -13,7 +13,7 @@
 // one ballot per id bit, and waves, sub-chunks and chunks are combined with
 // exclusive prefix sums.
 //
-// Two launches:
+// Two launches (one, plan_fused_kernel, for small problems):
 //   count:    grid (chunks, N). Per chunk of up to kPlanChunk slots of one
 //             source: rank of each slot among earlier slots of the chunk with
 //             the same expert (kept in send_pos), and the chunk's counts.
@@ -70,28 +70,29 @@ __device__ void block_exclusive_scan(int32_t* a, int n, int32_t* scratch, int32_
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(
-    const int32_t* __restrict__ idx, int E, int64_t TR, int nchunks,
-    int32_t* __restrict__ lrank, int32_t* __restrict__ chunk_cnt,
-    int32_t* __restrict__ status) {
-  extern __shared__ int32_t lds[];
+// Ranks of the slots of chunk c of source s (ids in `src`, TR slots): for
+// each of the kPlanSub sub-chunks of kPlanThreads slots, each wave ranks its
+// 64 slots among equal ids (one ballot per id bit), and the waves' counts
+// are combined by an exclusive prefix in LDS, continuing the running count
+// of earlier sub-chunks. Returns, per sub-chunk, the slot's id (E for an
+// invalid id or no slot) and its rank among the chunk's earlier slots with
+// the same id; on return run[e] holds the chunk's count of id e.
+// LDS: wcnt [kPlanThreads / 64][E + 1], run [E + 1].
+__device__ __forceinline__ void chunk_ranks(const int32_t* __restrict__ src, int E, int64_t TR,
+                                            int c, int32_t* wcnt, int32_t* run, int* e_of,
+                                            int* rank_of, bool& bad) {
   constexpr int kWaves = kPlanThreads / kWave;
   const int Ep = E + 1;                 // bucket E collects invalid ids
-  int32_t* wcnt = lds;                  // [kWaves][Ep]
-  int32_t* run = lds + kWaves * Ep;     // [Ep] running count over sub-chunks
-  const int s = blockIdx.y;
-  const int c = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int nbits = 32 - __clz(E);      // bits of the values 0..E
-  const int32_t* src = idx + (size_t)s * TR;
-  int32_t* lr = lrank + (size_t)s * TR;
-  bool bad = false;
-
   for (int q = tid; q < Ep; q += kPlanThreads) run[q] = 0;
+#pragma unroll
   for (int sub = 0; sub < kPlanSub; ++sub) {
+    e_of[sub] = E;
+    rank_of[sub] = 0;
     const int64_t first = (int64_t)c * kPlanChunk + (int64_t)sub * kPlanThreads;
-    if (first >= TR) break;                                   // block-uniform
+    if (first >= TR) continue;                                // block-uniform
     for (int q = tid; q < kWaves * Ep; q += kPlanThreads) wcnt[q] = 0;
     __syncthreads();
     const int64_t i = first + tid;
@@ -108,8 +109,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(
     const int rank = __popcll(peers & lanes_below());
     if (active && rank == 0) wcnt[wave * Ep + e] = __popcll(peers);
     __syncthreads();
-    // Per expert: exclusive prefix over the waves, continuing the running
-    // count of earlier sub-chunks.
     for (int q = tid; q < Ep; q += kPlanThreads) {
       int r = run[q];
       for (int w = 0; w < kWaves; ++w) {
@@ -120,8 +119,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(
       run[q] = r;
     }
     __syncthreads();
-    if (active) lr[i] = wcnt[wave * Ep + e] + rank;
+    e_of[sub] = e;
+    if (active) rank_of[sub] = wcnt[wave * Ep + e] + rank;
     __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(
+    const int32_t* __restrict__ idx, int E, int64_t TR, int nchunks,
+    int32_t* __restrict__ lrank, int32_t* __restrict__ chunk_cnt,
+    int32_t* __restrict__ status) {
+  extern __shared__ int32_t lds[];
+  constexpr int kWaves = kPlanThreads / kWave;
+  int32_t* wcnt = lds;                        // [kWaves][E+1]
+  int32_t* run = lds + kWaves * (E + 1);      // [E+1]
+  const int s = blockIdx.y;
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
+  int e_of[kPlanSub], rank_of[kPlanSub];
+  bool bad = false;
+  chunk_ranks(idx + (size_t)s * TR, E, TR, c, wcnt, run, e_of, rank_of, bad);
+  int32_t* lr = lrank + (size_t)s * TR;
+#pragma unroll
+  for (int sub = 0; sub < kPlanSub; ++sub) {
+    const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * kPlanThreads + tid;
+    if (i < TR) lr[i] = rank_of[sub];
   }
   for (int q = tid; q < E; q += kPlanThreads)
     chunk_cnt[((size_t)s * nchunks + c) * E + q] = run[q];
@@ -391,6 +413,73 @@ __global__ __launch_bounds__(kPlanThreads) void plan_exchange_kernel(
                  scratch);
 }
 
+// The whole plan in one launch, for small problems (launch-bound: every
+// block reads all N T R routing ids): block (c, s) ranks its chunk's
+// slots, then builds the exchange directly from all sources' ids with LDS
+// atomic counters (order-free totals, as the pages count), then writes both
+// sides' tables like the finalize launch. Saves the count launch and the
+// chunk-count round trip through memory.
+__global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
+    const int32_t* __restrict__ idx, int N, int E, int L, int64_t TR, int64_t cap, PlanPtrs p,
+    int32_t* __restrict__ status) {
+  extern __shared__ int32_t lds[];
+  constexpr int kWaves = kPlanThreads / kWave;
+  int32_t* soff = lds;               // [E+1] rows of s to e -> send offsets
+  int32_t* pre = soff + (E + 1);     // [E]   rows of s to e in earlier chunks
+  int32_t* sro = pre + E;            // [E]   rows earlier sources send to e
+  int32_t* sros = sro + E;           // [E+1]
+  int32_t* gsc = sros + (E + 1);     // [E+1] rows all sources send to e
+  int32_t* dstart = gsc + (E + 1);   // [N+1]
+  int32_t* scratch = dstart + (N + 1);          // [kWaves]
+  int32_t* wcnt = scratch + kWaves;             // [kWaves][E+1] (chunk ranks)
+  int32_t* run = wcnt + kWaves * (E + 1);       // [E+1]
+  const int s = blockIdx.y;
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPlanThreads) {
+    soff[e] = 0;
+    pre[e] = 0;
+    sro[e] = 0;
+    gsc[e] = 0;
+  }
+  int e_of[kPlanSub], rank_of[kPlanSub], within_of[kPlanSub];
+  bool bad = false;
+  chunk_ranks(idx + (size_t)s * TR, E, TR, c, wcnt, run, e_of, rank_of, bad);
+  if (bad) atomicOr(status, kStatusBadExpert);
+  // The exchange: histograms over every source's ids.
+  const int64_t mine = (int64_t)c * kPlanChunk;  // own slots before this chunk
+  for (int s2 = 0; s2 < N; ++s2) {
+    const int32_t* src = idx + (size_t)s2 * TR;
+    for (int64_t j = tid; j < TR; j += kPlanThreads) {
+      const int e = src[j];
+      if (e < 0 || e >= E) continue;
+      atomicAdd(&gsc[e], 1);
+      if (s2 < s) {
+        atomicAdd(&sro[e], 1);
+      } else if (s2 == s) {
+        atomicAdd(&soff[e], 1);
+        if (j < mine) atomicAdd(&pre[e], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) sros[e] = sro[e];
+  __syncthreads();
+  send_tables(e_of, rank_of, s, c, E, TR, p, soff, pre, scratch, within_of);
+  receive_tables(e_of, within_of, s, c, N, E, L, TR, cap, p, status, sro, sros, gsc, dstart,
+                 scratch);
+}
+
+bool fused_plan_fits(const Dims& d) {
+  return d.NTR <= kFusedPlanSlots && d.E <= 1024 && d.N <= 1024;
+}
+
+size_t lds_fused_bytes(const Dims& d) {
+  constexpr int kWaves = kPlanThreads / kWave;
+  return sizeof(int32_t) * ((size_t)5 * (d.E + 1) + (d.N + 1) + kWaves +
+                            (size_t)(kWaves + 1) * (d.E + 1));
+}
+
 // LDS bytes of the finalize and exchange launches (the larger of the two
 // layouts) and of the count launch.
 size_t lds_count_bytes(const Dims& d) {
@@ -411,7 +500,8 @@ hipError_t allow_large_lds() {
   static bool done[64] = {};
   if (dev >= 0 && dev < 64 && done[dev]) return hipSuccess;
   for (const void* f : {(const void*)plan_count_kernel, (const void*)plan_finalize_kernel,
-                        (const void*)plan_local_kernel, (const void*)plan_exchange_kernel}) {
+                        (const void*)plan_local_kernel, (const void*)plan_exchange_kernel,
+                        (const void*)plan_fused_kernel}) {
     e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
   }
@@ -433,6 +523,11 @@ hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                        int32_t* status, hipStream_t stream) {
   hipError_t e = allow_large_lds();
   if (e != hipSuccess) return e;
+  if (fused_plan_fits(d)) {
+    hipLaunchKernelGGL(plan_fused_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
+                       lds_fused_bytes(d), stream, idx, d.N, d.E, d.L, d.TR, d.cap, p, status);
+    return hipGetLastError();
+  }
   e = launch_count(d, idx, p, status, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_finalize_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
