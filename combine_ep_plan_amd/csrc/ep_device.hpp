@@ -100,14 +100,16 @@ __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) {
 
 // Loads are unconditional: a lane past the end re-reads the row's last
 // chunk (clamped index, always in bounds), so no branch separates the loads
-// and all V of them are in flight together. Requires n16 >= 1.
-template <int V>
+// and all V of them are in flight together. Requires n16 >= 1. NT selects
+// non-temporal loads (the default) or ordinary cached ones.
+template <int V, bool NT = true>
 __device__ __forceinline__ void load_row16(RowRegs<V>& r, const u32x4* src, int base, int n16) {
   const int lane = lane_id();
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int c = base + lane + kWave * i;
-    r.v[i] = load_stream(&src[c < n16 ? c : n16 - 1]);
+    const u32x4* q = &src[c < n16 ? c : n16 - 1];
+    r.v[i] = NT ? load_stream(q) : *q;
   }
   // Compiler memory barrier: keeps every load above the caller's stores
   // (otherwise each load is sunk next to its store and the row's loads

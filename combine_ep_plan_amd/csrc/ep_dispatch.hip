@@ -24,6 +24,12 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWavesPerBlock * kWave;
 constexpr int kSegV = 7;   // 16-byte chunks per lane in a row segment
 constexpr int kSeg = kWave * kSegV;  // 16-byte chunks per segment (7 KB)
+// The senders read token rows with ordinary (cached) loads: measured on
+// gfx950 against non-temporal loads, pack took 405 vs 466 us at prefill
+// scale and 185 vs 211 us on the all-to-one workload, and was neutral at
+// decode scale. Every other copy reads non-temporally (its reads measured
+// faster that way: the receiver 157 vs 169 us at decode scale).
+constexpr bool kPackNtLoads = false;
 
 struct Planes {
   const uint8_t* src[2];
@@ -90,8 +96,8 @@ __device__ __forceinline__ void pack_plane(const uint8_t* x, uint8_t* send,
   const int n16 = (int)(row >> 4);
   for (int base = 0; base < n16; base += kWave * V) {
     RowRegs<V> r0, r1;
-    load_row16(r0, (const u32x4*)(x + (size_t)tok0 * row), base, n16);
-    if (two) load_row16(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), base, n16);
+    load_row16<V, kPackNtLoads>(r0, (const u32x4*)(x + (size_t)tok0 * row), base, n16);
+    if (two) load_row16<V, kPackNtLoads>(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), base, n16);
     pack_stores(r0, send + (size_t)(tok0 / T) * TR * row, send_pos + (size_t)tok0 * R, R, TR,
                 row, base, n16);
     if (two)
@@ -145,8 +151,8 @@ __device__ __forceinline__ void pack_pass(const uint8_t* x, uint8_t* send, const
   const int TR = T * R;
   const int n16 = row >> 4;
   RowRegs<V> r0, r1;
-  load_row16(r0, (const u32x4*)(x + (size_t)tok0 * row), 0, n16);
-  if (two) load_row16(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), 0, n16);
+  load_row16<V, kPackNtLoads>(r0, (const u32x4*)(x + (size_t)tok0 * row), 0, n16);
+  if (two) load_row16<V, kPackNtLoads>(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), 0, n16);
   for (int u = 0; u < (two ? 2 : 1); ++u) {
     const int tok = tok0 + u;
     const int s = tok / T;
@@ -218,8 +224,8 @@ __device__ __forceinline__ void pack_split_plane(const uint8_t* x, uint8_t* send
   const int n16 = (int)(row >> 4);
   for (int base = 0; base < n16; base += kWave * V) {
     RowRegs<V> r0, r1;
-    load_row16(r0, (const u32x4*)(x + (size_t)tok0 * row), base, n16);
-    if (two) load_row16(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), base, n16);
+    load_row16<V, kPackNtLoads>(r0, (const u32x4*)(x + (size_t)tok0 * row), base, n16);
+    if (two) load_row16<V, kPackNtLoads>(r1, (const u32x4*)(x + (size_t)(tok0 + 1) * row), base, n16);
     for (int u = 0; u < (two ? 2 : 1); ++u) {
       const int tok = tok0 + u;
       const int s = tok / T;
