@@ -122,7 +122,7 @@ def test_plan_views_layout():
 
 
 def test_status_strings():
-    for c in [0, -1, -2, -3, -4, 1, 2, 3, 99]:
+    for c in [0, -1, -2, -3, -4, 1, 2, 3, 4, 99]:
         assert isinstance(ep.status_string(c), str) and ep.status_string(c)
 
 
