@@ -20,6 +20,8 @@
 //   finalize: grid (chunks, N). Every block sums the chunk counts it needs
 //             (all sources: the exchange), forms the prefix sums, writes the
 //             tables once (chunk 0 blocks) and finishes its slots' positions.
+#include <atomic>
+
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 
@@ -492,20 +494,23 @@ size_t lds_final_bytes(const Dims& d) {
   return sizeof(int32_t) * ((size_t)5 * (d.E + 1) + (d.N + 1) + kWaves + (size_t)2 * groups * d.E);
 }
 
-// Kernels using more than 64 KB of LDS must opt in, once per device.
+// Kernels using more than 64 KB of LDS must opt in, once per device. The
+// flags are atomics so that concurrent first calls from several threads are
+// safe (the opt-in itself is idempotent).
 hipError_t allow_large_lds() {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  static bool done[64] = {};
-  if (dev >= 0 && dev < 64 && done[dev]) return hipSuccess;
+  static std::atomic<bool> done[64];
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached && done[dev].load(std::memory_order_acquire)) return hipSuccess;
   for (const void* f : {(const void*)plan_count_kernel, (const void*)plan_finalize_kernel,
                         (const void*)plan_local_kernel, (const void*)plan_exchange_kernel,
                         (const void*)plan_fused_kernel}) {
     e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
   }
-  if (dev >= 0 && dev < 64) done[dev] = true;
+  if (cached) done[dev].store(true, std::memory_order_release);
   return hipSuccess;
 }
 
