@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark: one MoE dispatch + combine step of the whole EP group on one GPU.
 
-A step is ep_plan -> ep_dispatch_pack -> ep_dispatch_recv -> ep_combine over
-the decode-scale workload (N=32 virtual ranks x T=128 tokens, H=7168 bf16,
-E=256 experts, top-8 uniform routing, softmax weights). The stand-in expert
-(per-expert scale) runs once before timing; its output is what combine reads
-in every timed step, so no expert work is inside the timed region.
+A step is ep_dispatch (plan, pack and receive) -> ep_combine over the
+decode-scale workload (N=32 virtual ranks x T=128 tokens, H=7168 bf16, E=256
+experts, top-8 uniform routing, softmax weights); fp8 workloads use
+ep_dispatch_quant (the sender quantises bf16 rows). The stand-in expert (per-expert scale) runs once before timing;
+its output is what combine reads in every timed step, so no expert work is
+inside the timed region.
 
 Prints one JSON line. `value` is the effective HBM throughput of the step:
 the algorithmic bytes of dispatch + combine divided by the step time.
@@ -180,6 +181,20 @@ def measure_split(ep, torch, d, b, sh, P: int, steps: int, warmup: int) -> dict:
         recv()
         comb()
 
+    def split_overlapped():
+        # the exchange on the second stream while the first one packs
+        ep.dispatch_send_plan(d, b.idx, b.plan_ws, b.status, spa)
+        counts = torch.cuda.Event()
+        counts.record(sa)
+        sb.wait_event(counts)
+        ep.dispatch_recv_plan(d, b.plan_ws, b.status, sb.cuda_stream)
+        offsets = torch.cuda.Event()
+        offsets.record(sb)
+        ep.dispatch_send_pack(d, b.idx, b.x, b.plan_ws, b.send, priv, P, spa)
+        sa.wait_event(offsets)
+        ep.dispatch_recv_pull(d, b.send, priv, P, b.plan_ws, b.grouped, spa)
+        comb()
+
     def sequential():
         send()
         gemm()
@@ -199,7 +214,7 @@ def measure_split(ep, torch, d, b, sh, P: int, steps: int, warmup: int) -> dict:
         done.record(sb)
         sa.wait_event(done)
 
-    for fn in (split_step, gemm, sequential, overlapped):
+    for fn in (split_step, split_overlapped, gemm, sequential, overlapped):
         for _ in range(warmup):
             fn()
     torch.cuda.synchronize()
@@ -222,14 +237,22 @@ def measure_split(ep, torch, d, b, sh, P: int, steps: int, warmup: int) -> dict:
         split_step()
     e1.record(sa)
     torch.cuda.synchronize()
+    t_split = e0.elapsed_time(e1) / steps * 1e3
+    e0.record(sa)
+    for _ in range(steps):
+        split_overlapped()
+    e1.record(sa)
+    torch.cuda.synchronize()
+    t_ovl_step = e0.elapsed_time(e1) / steps * 1e3
     reps = max(steps // 5, 5)
     t_gemm = timed(gemm, reps)
     t_seq = timed(sequential, reps)
     t_ovl = timed(overlapped, reps)
     return {
         "priv_rows": P,
-        "us_per_dispatch_combine": round(e0.elapsed_time(e1) / steps * 1e3, 2),
+        "us_per_dispatch_combine": round(t_split, 2),
         "stages_us": {n: round(st.mean(v), 2) for n, v in stages.items()},
+        "us_exchange_overlapped_with_pack": round(t_ovl_step, 2),
         "shared_expert_stand_in": f"bf16 GEMMs [{NT},{H}]x[{H},2048] then x[2048,{H}]",
         "shared_expert_us": round(t_gemm, 2),
         "sequential_us": round(t_seq, 2),
@@ -406,7 +429,8 @@ def main() -> int:
         print(f"plan status {b.status.item()}", file=sys.stderr)
         return 1
 
-    def step(ev=None):
+    def staged_step(ev=None):
+        """The four calls one by one, with an event between stages."""
         if ev is not None:
             ev[0].record(stream)
         ep.plan(d, b.idx, b.plan_ws, b.status, sp)
@@ -422,13 +446,30 @@ def main() -> int:
         if ev is not None:
             ev[4].record(stream)
 
+    def fused_step(ev=None):
+        """ep_dispatch / ep_dispatch_quant (plan + pack + receive, the count
+        exchange folded into the sender launch) and ep_combine."""
+        if ev is not None:
+            ev[0].record(stream)
+        if quant:
+            ep.dispatch_quant(d, b.idx, x_bf16, b.plan_ws, b.send, b.grouped, b.status, sp)
+        else:
+            ep.dispatch(d, b.idx, b.x, b.plan_ws, b.send, b.grouped, b.status, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, sp)
+        if ev is not None:
+            ev[2].record(stream)
+
+    # A step is the one-call dispatch and the combine.
+    step = fused_step
+    n_ev = 3
     for _ in range(args.warmup):
         step()
-    # Per-stage events only on every `sample_every`-th step: an event record
-    # between two kernels costs a few microseconds of GPU time, so recording
-    # five per step would inflate the step it measures.
+    # Events only on every `sample_every`-th step: an event record between
+    # two kernels costs a few microseconds of GPU time.
     sampled = list(range(0, args.steps, args.sample_every))
-    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for i in sampled}
+    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for i in sampled}
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -438,13 +479,24 @@ def main() -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
+    steps_ms = [ev[0].elapsed_time(ev[-1]) for ev in events.values()]
+    dispatch_call_us = statistics.mean(ev[0].elapsed_time(ev[1]) for ev in events.values()) * 1e3
+    # Per-stage times (and the dominant kernel's) from the four separate
+    # calls, after the timed region; the receiver kernel is the same launch
+    # in both forms of the step.
     stage_names = ["plan", "pack", "recv", "combine"]
     per = {n: [] for n in stage_names}
-    steps_ms = []
-    for ev in events.values():
+    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                for _ in range(max(len(sampled), 5))]
+    for _ in range(3):
+        staged_step()
+    for ev in stage_ev:
+        staged_step()
+        staged_step(ev)
+    torch.cuda.synchronize()
+    for ev in stage_ev:
         for j, n in enumerate(stage_names):
             per[n].append(ev[j].elapsed_time(ev[j + 1]))
-        steps_ms.append(ev[0].elapsed_time(ev[4]))
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     ab = algorithmic_bytes(sh, row_d, quant)
@@ -531,7 +583,11 @@ def main() -> int:
         "us_per_dispatch_combine": round(ms_per_step * 1e3, 2),
         "frac_of_hbm_peak": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": ab["step"],
+        "step_form": ("ep_dispatch_quant" if quant else "ep_dispatch") +
+                     " (plan + pack + recv) then ep_combine",
+        "dispatch_call_us": round(dispatch_call_us, 2),
         "stages_us": {n: round(statistics.mean(per[n]) * 1e3, 2) for n in stage_names},
+        "stages_from": "the four separate calls, sampled after the timed steps",
         "instrumented_step_us_p10_p50_p90": [round(float(np.percentile(steps_ms, q)) * 1e3, 2)
                                              for q in (10, 50, 90)],
         "instrumented_steps": len(steps_ms),

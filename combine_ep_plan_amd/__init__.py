@@ -31,9 +31,13 @@ EP_PAYLOAD_FP8_B128 = 1
 # Every entry point the C header declares (checked by the tests).
 EXPORTS = (
     "ep_recv_bound", "ep_capacity", "ep_num_planes", "ep_row_bytes",
-    "ep_plan_bytes", "ep_plan_views", "ep_plan", "ep_dispatch_pack", "ep_dispatch_pack_quant",
+    "ep_plan_bytes", "ep_plan_views", "ep_plan", "ep_dispatch", "ep_dispatch_quant",
+    "ep_dispatch_pack",
+    "ep_dispatch_pack_quant",
     "ep_dispatch_transfer", "ep_dispatch_unpack", "ep_dispatch_recv",
-    "ep_dispatch_send", "ep_dispatch_recv_split", "ep_expert_stub", "ep_combine",
+    "ep_dispatch_send", "ep_dispatch_recv_split", "ep_dispatch_send_plan",
+    "ep_dispatch_send_pack", "ep_dispatch_recv_plan", "ep_dispatch_recv_pull",
+    "ep_expert_stub", "ep_combine",
     "ep_combine_presum", "ep_kv_plan", "ep_kv_push", "ep_kv_push_staged",
     "ep_probe_copy", "ep_status_string",
     "ep_last_error",
@@ -81,6 +85,8 @@ def _load() -> ctypes.CDLL:
         "ep_plan_bytes": (ctypes.c_size_t, [D]),
         "ep_plan_views": (ctypes.c_int, [D, P, ctypes.POINTER(PlanView)]),
         "ep_plan": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_dispatch": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
+        "ep_dispatch_quant": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
         "ep_dispatch_pack": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_pack_quant": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_transfer": (ctypes.c_int, [D, P, P, P, P]),
@@ -88,6 +94,10 @@ def _load() -> ctypes.CDLL:
         "ep_dispatch_recv": (ctypes.c_int, [D, P, P, P, P]),
         "ep_dispatch_send": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_int32, P, P]),
         "ep_dispatch_recv_split": (ctypes.c_int, [D, P, P, ctypes.c_int32, P, P, P, P]),
+        "ep_dispatch_send_plan": (ctypes.c_int, [D, P, P, P, P]),
+        "ep_dispatch_send_pack": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_int32, P]),
+        "ep_dispatch_recv_plan": (ctypes.c_int, [D, P, P, P]),
+        "ep_dispatch_recv_pull": (ctypes.c_int, [D, P, P, ctypes.c_int32, P, P, P]),
         "ep_expert_stub": (ctypes.c_int, [D, P, P, P, P, P]),
         "ep_combine": (ctypes.c_int, [D, P, P, P, P, P]),
         "ep_combine_presum": (ctypes.c_int, [D, P, P, P, P, P, P]),
@@ -193,6 +203,20 @@ def plan(d: Desc, topk_idx, plan_ws, status, stream=None) -> None:
                         _stream(stream)), "ep_plan")
 
 
+def dispatch(d: Desc, topk_idx, x: Sequence, plan_ws, send: Sequence, grouped: Sequence, status,
+             stream=None) -> None:
+    _check(_lib.ep_dispatch(ctypes.byref(d), _addr(topk_idx), _planes(x), _addr(plan_ws),
+                            _planes(send), _planes(grouped), _addr(status), _stream(stream)),
+           "ep_dispatch")
+
+
+def dispatch_quant(d: Desc, topk_idx, x_bf16, plan_ws, send: Sequence, grouped: Sequence, status,
+                   stream=None) -> None:
+    _check(_lib.ep_dispatch_quant(ctypes.byref(d), _addr(topk_idx), _addr(x_bf16), _addr(plan_ws),
+                                  _planes(send), _planes(grouped), _addr(status), _stream(stream)),
+           "ep_dispatch_quant")
+
+
 def dispatch_pack(d: Desc, x: Sequence, plan_ws, send: Sequence, stream=None) -> None:
     _check(_lib.ep_dispatch_pack(ctypes.byref(d), _planes(x), _addr(plan_ws), _planes(send),
                                  _stream(stream)), "ep_dispatch_pack")
@@ -230,6 +254,30 @@ def dispatch_recv_split(d: Desc, send: Sequence, priv: Sequence, priv_rows: int,
     _check(_lib.ep_dispatch_recv_split(ctypes.byref(d), _planes(send), _planes(priv),
                                        int(priv_rows), _addr(plan_ws), _planes(grouped),
                                        _addr(status), _stream(stream)), "ep_dispatch_recv_split")
+
+
+def dispatch_send_plan(d: Desc, topk_idx, plan_ws, status, stream=None) -> None:
+    _check(_lib.ep_dispatch_send_plan(ctypes.byref(d), _addr(topk_idx), _addr(plan_ws),
+                                      _addr(status), _stream(stream)), "ep_dispatch_send_plan")
+
+
+def dispatch_send_pack(d: Desc, topk_idx, x: Sequence, plan_ws, send: Sequence, priv: Sequence,
+                       priv_rows: int, stream=None) -> None:
+    _check(_lib.ep_dispatch_send_pack(ctypes.byref(d), _addr(topk_idx), _planes(x),
+                                      _addr(plan_ws), _planes(send), _planes(priv),
+                                      int(priv_rows), _stream(stream)), "ep_dispatch_send_pack")
+
+
+def dispatch_recv_plan(d: Desc, plan_ws, status, stream=None) -> None:
+    _check(_lib.ep_dispatch_recv_plan(ctypes.byref(d), _addr(plan_ws), _addr(status),
+                                      _stream(stream)), "ep_dispatch_recv_plan")
+
+
+def dispatch_recv_pull(d: Desc, send: Sequence, priv: Sequence, priv_rows: int, plan_ws,
+                       grouped: Sequence, stream=None) -> None:
+    _check(_lib.ep_dispatch_recv_pull(ctypes.byref(d), _planes(send), _planes(priv),
+                                      int(priv_rows), _addr(plan_ws), _planes(grouped),
+                                      _stream(stream)), "ep_dispatch_recv_pull")
 
 
 def priv_buffers(d: Desc, priv_rows: int, device="cuda") -> list:

@@ -273,6 +273,20 @@ int ep_plan(const ep_desc* d, const int32_t* topk_idx, void* plan_ws, int32_t* s
   return EP_OK;
 }
 
+int ep_dispatch(const ep_desc* d, const int32_t* topk_idx, const void* const x[2],
+                void* plan_ws, void* const send[2], void* const grouped[2], int32_t* status,
+                hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_ptr(status, scope.device(), "status"));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  EP_CHECK(check_planes(dims, (const void* const*)x, scope.device(), "x", dims.NT));
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
+  const hipError_t e = ep::launch_dispatch(dims, topk_idx, x, pp, send, grouped, status, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch");
+  return EP_OK;
+}
+
 int ep_dispatch_pack(const ep_desc* d, const void* const x[2], const void* plan_ws,
                      void* const send[2], hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
@@ -295,6 +309,24 @@ int ep_dispatch_pack_quant(const ep_desc* d, const uint16_t* x, const void* plan
   EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
   const hipError_t e = ep::launch_pack_quant(dims, x, pp, send, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_dispatch_pack_quant");
+  return EP_OK;
+}
+
+int ep_dispatch_quant(const ep_desc* d, const int32_t* topk_idx, const uint16_t* x,
+                      void* plan_ws, void* const send[2], void* const grouped[2], int32_t* status,
+                      hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  if (dims.payload != EP_PAYLOAD_FP8_B128)
+    return fail(EP_ERR_INVALID_ARG, "ep_dispatch_quant needs the fp8 payload descriptor");
+  if (dims.NT * (((int64_t)dims.H + 1023) / 1024) >= kMaxWaves)
+    return fail(EP_ERR_UNSUPPORTED, "tokens x 1024-value row segments must be < 2^26");
+  EP_CHECK(check_ptr(status, scope.device(), "status"));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  EP_CHECK(check_ptr(x, scope.device(), "x", dims.NT * 2 * (int64_t)dims.H));
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
+  const hipError_t e = ep::launch_dispatch_quant(dims, topk_idx, x, pp, send, grouped, status, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_quant");
   return EP_OK;
 }
 
@@ -335,34 +367,81 @@ int check_priv(const ep::Dims& d, void* const priv[2], int32_t P, int dev) {
   return check_planes(d, (const void* const*)priv, dev, "priv", (int64_t)d.N * d.N * P);
 }
 
-int ep_dispatch_send(const ep_desc* d, const int32_t* topk_idx, const void* const x[2],
-                     void* plan_ws, void* const send[2], void* const priv[2], int32_t priv_rows,
-                     int32_t* status, hipStream_t stream) {
+int ep_dispatch_send_plan(const ep_desc* d, const int32_t* topk_idx, void* plan_ws,
+                          int32_t* status, hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
   EP_CHECK(check_ptr(status, scope.device(), "status"));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  const hipError_t e = ep::launch_plan_local(dims, topk_idx, pp, status, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_send_plan");
+  return EP_OK;
+}
+
+int ep_dispatch_send_pack(const ep_desc* d, const int32_t* topk_idx, const void* const x[2],
+                          const void* plan_ws, void* const send[2], void* const priv[2],
+                          int32_t priv_rows, hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
   EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
   EP_CHECK(check_planes(dims, (const void* const*)x, scope.device(), "x", dims.NT));
   EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
   EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
-  hipError_t e = ep::launch_plan_local(dims, topk_idx, pp, status, stream);
-  if (e == hipSuccess)
-    e = ep::launch_pack_split(dims, topk_idx, x, pp, send, priv, priv_rows, stream);
-  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_send");
+  const hipError_t e = ep::launch_pack_split(dims, topk_idx, x, pp, send, priv, priv_rows, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_send_pack");
   return EP_OK;
+}
+
+int ep_dispatch_recv_plan(const ep_desc* d, void* plan_ws, int32_t* status, hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_ptr(status, scope.device(), "status"));
+  const hipError_t e = ep::launch_plan_exchange(dims, pp, status, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_recv_plan");
+  return EP_OK;
+}
+
+int ep_dispatch_recv_pull(const ep_desc* d, const void* const send[2], void* const priv[2],
+                          int32_t priv_rows, const void* plan_ws, void* const grouped[2],
+                          hipStream_t stream) {
+  EP_PROLOGUE(d, stream, plan_ws);
+  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+  EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
+  EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
+  const hipError_t e = ep::launch_recv_split(dims, send, priv, priv_rows, pp, grouped, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_recv_pull");
+  return EP_OK;
+}
+
+int ep_dispatch_send(const ep_desc* d, const int32_t* topk_idx, const void* const x[2],
+                     void* plan_ws, void* const send[2], void* const priv[2], int32_t priv_rows,
+                     int32_t* status, hipStream_t stream) {
+  // Check everything before enqueueing the first half.
+  {
+    EP_PROLOGUE(d, stream, plan_ws);
+    EP_CHECK(check_ptr(status, scope.device(), "status"));
+    EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+    EP_CHECK(check_planes(dims, (const void* const*)x, scope.device(), "x", dims.NT));
+    EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+    EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
+    (void)pp;
+  }
+  EP_CHECK(ep_dispatch_send_plan(d, topk_idx, plan_ws, status, stream));
+  return ep_dispatch_send_pack(d, topk_idx, x, plan_ws, send, priv, priv_rows, stream);
 }
 
 int ep_dispatch_recv_split(const ep_desc* d, const void* const send[2], void* const priv[2],
                            int32_t priv_rows, void* plan_ws, void* const grouped[2],
                            int32_t* status, hipStream_t stream) {
-  EP_PROLOGUE(d, stream, plan_ws);
-  EP_CHECK(check_ptr(status, scope.device(), "status"));
-  EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
-  EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
-  EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
-  hipError_t e = ep::launch_plan_exchange(dims, pp, status, stream);
-  if (e == hipSuccess) e = ep::launch_recv_split(dims, send, priv, priv_rows, pp, grouped, stream);
-  if (e != hipSuccess) return fail_hip(e, "ep_dispatch_recv_split");
-  return EP_OK;
+  // Check everything before enqueueing the first half.
+  {
+    EP_PROLOGUE(d, stream, plan_ws);
+    EP_CHECK(check_ptr(status, scope.device(), "status"));
+    EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
+    EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
+    EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped",
+                          dims.N * dims.cap));
+    (void)pp;
+  }
+  EP_CHECK(ep_dispatch_recv_plan(d, plan_ws, status, stream));
+  return ep_dispatch_recv_pull(d, send, priv, priv_rows, plan_ws, grouped, stream);
 }
 
 int ep_expert_stub(const ep_desc* d, const void* const grouped[2], const float* alpha,

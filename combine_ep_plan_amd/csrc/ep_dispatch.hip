@@ -16,6 +16,7 @@
 // wave-uniform and live in scalar registers.
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
+#include "ep_plan_device.hpp"
 
 namespace ep {
 namespace {
@@ -182,6 +183,30 @@ __global__ __launch_bounds__(kBlock) void pack_fast2_kernel(const uint8_t* x0, u
   if (tok0 >= NT) return;
   pack_pass<V0>(x0, send0, sp, tok0, tok0 + 1 < NT, T, R, row0);
   pack_pass<V1>(x1, send1, sp, tok0, tok0 + 1 < NT, T, R, row1);
+}
+
+// Dispatch in one go for sources whose slots fit one plan chunk: after the
+// send side of the plan (own counts, offsets and positions), the first N
+// blocks of this kernel do the count exchange and write the receive side of
+// the plan (the receiver needs it, the sender does not) while the other
+// blocks move the rows, one wave per token pair as in pack_fast1/2. The
+// exchange (a latency-bound ~10 us) so hides under the bandwidth-bound
+// sender instead of delaying it. V1 = 0: one payload plane.
+template <int V0, int V1>
+__global__ __launch_bounds__(kBlock) void pack_exchange_kernel(
+    const uint8_t* x0, uint8_t* send0, const uint8_t* x1, uint8_t* send1, PlanPtrs p, int N,
+    int E, int L, int T, int R, int64_t cap, int row0, int row1, int32_t* status) {
+  extern __shared__ int32_t lds[];
+  const int b = blockIdx.x;
+  if (b < N) {  // block-uniform
+    exchange_block<kBlock>(b, 0, b, N, N, E, L, (int64_t)T * R, cap, p, status, lds);
+    return;
+  }
+  const int tok0 = 2 * wave_uniform((b - N) * kWavesPerBlock + (int)threadIdx.x / kWave);
+  const int NT = N * T;
+  if (tok0 >= NT) return;
+  pack_pass<V0>(x0, send0, p.send_pos, tok0, tok0 + 1 < NT, T, R, row0);
+  if (V1 > 0) pack_pass<(V1 > 0 ? V1 : 1)>(x1, send1, p.send_pos, tok0, tok0 + 1 < NT, T, R, row1);
 }
 
 // Chunks per lane for a single pass over a plane of `row` bytes: 14, 7 or 1;
@@ -463,6 +488,38 @@ hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
   return hipGetLastError();
 }
 
+// The count exchange can share the sender's launch when every source's
+// slots fit one plan chunk and the exchange's LDS stays small (E <= 512).
+bool dispatch_fused_fits(const Dims& d) {
+  return d.nchunks == 1 && d.TR <= kPlanChunk && d.E <= 512 && d.N <= 1024;
+}
+
+// ... and the plain sender has its single-pass form for these rows.
+bool pack_exchange_fits(const Dims& d) {
+  const int v0 = pass_v(d.row[0]);
+  const int v1 = d.planes > 1 ? pass_v(d.row[1]) : 0;
+  return dispatch_fused_fits(d) && v0 > 0 && (d.planes == 1 || v1 == 1);
+}
+
+// LDS of the exchange with kBlock threads (see exchange_block).
+size_t lds_exchange_bytes(const Dims& d) {
+  const int groups = d.E >= kBlock ? 1 : kBlock / d.E;
+  return sizeof(int32_t) * ((size_t)4 * (d.E + 1) + (d.N + 1) + kBlock / kWave +
+                            (size_t)2 * groups * d.E);
+}
+
+template <int V0, int V1>
+hipError_t launch_pack_exchange_v(const Dims& d, const void* const x[2], const PlanPtrs& p,
+                                  void* const send[2], int32_t* status, hipStream_t stream) {
+  const unsigned grid = (unsigned)d.N + blocks_for((d.NT + 1) / 2);
+  hipLaunchKernelGGL((pack_exchange_kernel<V0, V1>), dim3(grid), dim3(kBlock),
+                     lds_exchange_bytes(d), stream, (const uint8_t*)x[0], (uint8_t*)send[0],
+                     d.planes > 1 ? (const uint8_t*)x[1] : nullptr,
+                     d.planes > 1 ? (uint8_t*)send[1] : nullptr, p, d.N, d.E, d.L, d.T, d.R,
+                     d.cap, (int)d.row[0], d.planes > 1 ? (int)d.row[1] : 0, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs& p,
                        void* const grouped[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
@@ -471,6 +528,32 @@ hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs&
                      make_planes(d, send, grouped), p.grp_slot, p.send_pos, p.comb_row,
                      (int)d.NTR, (int)d.TR, (int64_t)d.N * d.cap, wps);
   return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const Dims& d, const int32_t* idx, const void* const x[2],
+                           const PlanPtrs& p, void* const send[2], void* const grouped[2],
+                           int32_t* status, hipStream_t stream) {
+  if (!pack_exchange_fits(d) || d.NT == 0) {
+    hipError_t e = launch_plan(d, idx, p, status, stream);
+    if (e == hipSuccess) e = launch_pack(d, x, p, send, stream);
+    if (e == hipSuccess) e = launch_recv(d, send, p, grouped, stream);
+    return e;
+  }
+  hipError_t e = launch_plan_local(d, idx, p, status, stream);
+  if (e != hipSuccess) return e;
+  const int v0 = pass_v(d.row[0]);
+  const int v1 = d.planes > 1 ? pass_v(d.row[1]) : 0;
+  if (v1 == 0) {
+    if (v0 == 2 * kSegV) e = launch_pack_exchange_v<2 * kSegV, 0>(d, x, p, send, status, stream);
+    else if (v0 == kSegV) e = launch_pack_exchange_v<kSegV, 0>(d, x, p, send, status, stream);
+    else e = launch_pack_exchange_v<1, 0>(d, x, p, send, status, stream);
+  } else {
+    if (v0 == 2 * kSegV) e = launch_pack_exchange_v<2 * kSegV, 1>(d, x, p, send, status, stream);
+    else if (v0 == kSegV) e = launch_pack_exchange_v<kSegV, 1>(d, x, p, send, status, stream);
+    else e = launch_pack_exchange_v<1, 1>(d, x, p, send, status, stream);
+  }
+  if (e != hipSuccess) return e;
+  return launch_recv(d, send, p, grouped, stream);
 }
 
 Split make_split(const Dims& d, void* const priv[2], int P, const PlanPtrs& p) {
@@ -488,6 +571,7 @@ hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* cons
                              const PlanPtrs& p, void* const send[2], void* const priv[2], int P,
                              hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
+  if (P == 0) return launch_pack(d, x, p, send, stream);  // no private rows: the plain sender
   hipLaunchKernelGGL(pack_split_kernel, dim3(blocks_for((d.NT + 1) / 2)), dim3(kBlock), 0, stream,
                      make_planes(d, x, send), make_split(d, priv, P, p), idx, p.send_pos,
                      (int)d.NT, d.T, d.R);
@@ -497,6 +581,7 @@ hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* cons
 hipError_t launch_recv_split(const Dims& d, const void* const send[2], void* const priv[2], int P,
                              const PlanPtrs& p, void* const grouped[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
+  if (P == 0) return launch_recv(d, send, p, grouped, stream);  // the plain receiver
   const int wps = waves_per_row(d);
   hipLaunchKernelGGL(recv_split_kernel, dim3(blocks_for(d.NTR * wps)), dim3(kBlock), 0, stream,
                      make_planes(d, send, grouped), make_split(d, priv, P, p), p.grp_slot,

@@ -51,6 +51,18 @@ hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* cons
                              hipStream_t stream);
 hipError_t launch_recv_split(const Dims& d, const void* const send[2], void* const priv[2], int P,
                              const PlanPtrs& p, void* const grouped[2], hipStream_t stream);
+// Plan, pack and receive in one call (fewer launches when a source's slots
+// fit one plan chunk; otherwise the three steps in turn).
+hipError_t launch_dispatch(const Dims& d, const int32_t* idx, const void* const x[2],
+                           const PlanPtrs& p, void* const send[2], void* const grouped[2],
+                           int32_t* status, hipStream_t stream);
+hipError_t launch_dispatch_quant(const Dims& d, const int32_t* idx, const uint16_t* x,
+                                 const PlanPtrs& p, void* const send[2], void* const grouped[2],
+                                 int32_t* status, hipStream_t stream);
+// Whether the one-call dispatch can fold the count exchange into the sender
+// launch, and the LDS bytes the exchange blocks need.
+bool dispatch_fused_fits(const Dims& d);
+size_t lds_exchange_bytes(const Dims& d);
 hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
                        void* const send[2], hipStream_t stream);
 hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p,

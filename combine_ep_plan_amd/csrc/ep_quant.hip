@@ -16,6 +16,7 @@
 // the integer codes are decided in the same precision everywhere.
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
+#include "ep_plan_device.hpp"
 
 namespace ep {
 namespace {
@@ -54,10 +55,11 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
   return sign | code;
 }
 
-__global__ __launch_bounds__(kBlock) void pack_quant_kernel(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
-    const int32_t* __restrict__ send_pos, int NT, int T, int R, int H, int nseg) {
-  const int w = wave_index();
+// The sender's work for wave w (token w / nseg, segment w % nseg).
+__device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x,
+                                           uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                           const int32_t* __restrict__ send_pos, int NT, int T,
+                                           int R, int H, int nseg) {
   const int tok = w / nseg;
   if (tok >= NT) return;
   const int lane = lane_id();
@@ -125,6 +127,28 @@ __global__ __launch_bounds__(kBlock) void pack_quant_kernel(
   }
 }
 
+__global__ __launch_bounds__(kBlock) void pack_quant_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
+    const int32_t* __restrict__ send_pos, int NT, int T, int R, int H, int nseg) {
+  quant_wave(wave_index(), x, codes, scales, send_pos, NT, T, R, H, nseg);
+}
+
+// As pack_quant_kernel, with the count exchange done by the first N blocks
+// (see pack_exchange_kernel): for sources whose slots fit one plan chunk.
+__global__ __launch_bounds__(kBlock) void pack_quant_exchange_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
+    PlanPtrs p, int N, int E, int L, int T, int R, int H, int nseg, int64_t cap,
+    int32_t* status) {
+  extern __shared__ int32_t lds[];
+  const int b = blockIdx.x;
+  if (b < N) {  // block-uniform
+    exchange_block<kBlock>(b, 0, b, N, N, E, L, (int64_t)T * R, cap, p, status, lds);
+    return;
+  }
+  const int w = wave_uniform((b - N) * kWavesPerBlock + (int)threadIdx.x / kWave);
+  quant_wave(w, x, codes, scales, p.send_pos, N * T, T, R, H, nseg);
+}
+
 }  // namespace
 
 hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p,
@@ -136,6 +160,28 @@ hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p
                      dim3(kBlock), 0, stream, x, (uint8_t*)send[0], (float*)send[1], p.send_pos,
                      (int)d.NT, d.T, d.R, d.H, nseg);
   return hipGetLastError();
+}
+
+hipError_t launch_dispatch_quant(const Dims& d, const int32_t* idx, const uint16_t* x,
+                                 const PlanPtrs& p, void* const send[2], void* const grouped[2],
+                                 int32_t* status, hipStream_t stream) {
+  if (!dispatch_fused_fits(d) || d.NT == 0) {
+    hipError_t e = launch_plan(d, idx, p, status, stream);
+    if (e == hipSuccess) e = launch_pack_quant(d, x, p, send, stream);
+    if (e == hipSuccess) e = launch_recv(d, send, p, grouped, stream);
+    return e;
+  }
+  hipError_t e = launch_plan_local(d, idx, p, status, stream);
+  if (e != hipSuccess) return e;
+  const int nseg = (d.H / 8 + kQSeg - 1) / kQSeg;
+  const int64_t waves = d.NT * nseg;
+  const unsigned grid = (unsigned)d.N + (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  hipLaunchKernelGGL(pack_quant_exchange_kernel, dim3(grid), dim3(kBlock), lds_exchange_bytes(d),
+                     stream, x, (uint8_t*)send[0], (float*)send[1], p, d.N, d.E, d.L, d.T, d.R,
+                     d.H, nseg, d.cap, status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_recv(d, send, p, grouped, stream);
 }
 
 }  // namespace ep

@@ -202,6 +202,25 @@ EP_API int ep_dispatch_recv(const ep_desc *d, const void *const send[2],
                      const void *plan_ws, void *const grouped[2],
                      hipStream_t stream);
 
+/* The whole dispatch in one call: ep_plan, ep_dispatch_pack and
+ * ep_dispatch_recv, with identical results (plan_ws tables, send, grouped,
+ * status). When a source's T R slots fit one plan chunk (4096) and E <= 512,
+ * it takes three launches instead of four: the send side of the plan, then
+ * the sender with the count exchange ("Send and receive buffers") done by
+ * extra blocks of the same launch, then the receiver. */
+EP_API int ep_dispatch(const ep_desc *d, const int32_t *topk_idx,
+                       const void *const x[2], void *plan_ws,
+                       void *const send[2], void *const grouped[2],
+                       int32_t *status, hipStream_t stream);
+
+/* ep_dispatch with the quantising sender: ep_plan, ep_dispatch_pack_quant
+ * and ep_dispatch_recv in one call (x: bf16 [N][T][H]; fp8 descriptor),
+ * with the same results and the same launch saving. */
+EP_API int ep_dispatch_quant(const ep_desc *d, const int32_t *topk_idx,
+                             const uint16_t *x, void *plan_ws,
+                             void *const send[2], void *const grouped[2],
+                             int32_t *status, hipStream_t stream);
+
 /* Split dispatch ("Dispatch and combine": dispatch is split into a sender
  * half and a receiver half so that other work can run between them; "Send
  * and receive buffers": each receiver keeps a small private region per
@@ -224,6 +243,18 @@ EP_API int ep_dispatch_send(const ep_desc *d, const int32_t *topk_idx,
                             int32_t priv_rows, int32_t *status,
                             hipStream_t stream);
 
+/* The sender half in two steps (ep_dispatch_send = send_plan, then
+ * send_pack): send_plan writes cnt[s], send_off[s], send_pos[s] (the
+ * routing information each source publishes) and flags bad ids in status;
+ * send_pack moves the rows (priv as for ep_dispatch_send). */
+EP_API int ep_dispatch_send_plan(const ep_desc *d, const int32_t *topk_idx,
+                                 void *plan_ws, int32_t *status,
+                                 hipStream_t stream);
+EP_API int ep_dispatch_send_pack(const ep_desc *d, const int32_t *topk_idx,
+                                 const void *const x[2], const void *plan_ws,
+                                 void *const send[2], void *const priv[2],
+                                 int32_t priv_rows, hipStream_t stream);
+
 /* Receiver half, after ep_dispatch_send on the same plan_ws (stream order
  * or an event). The exchange reads every source's published cnt row and
  * computes the receive side of the plan (src_off, recv_off, grp_off,
@@ -235,6 +266,19 @@ EP_API int ep_dispatch_recv_split(const ep_desc *d, const void *const send[2],
                                   void *const priv[2], int32_t priv_rows,
                                   void *plan_ws, void *const grouped[2],
                                   int32_t *status, hipStream_t stream);
+
+/* The receiver half in two steps (ep_dispatch_recv_split = recv_plan, then
+ * recv_pull). recv_plan needs only the counts the senders published
+ * (after ep_dispatch_send_plan), not their rows, so it may run on another
+ * stream while ep_dispatch_send_pack moves the data ("Send and receive
+ * buffers": data movement need not wait for the count exchange);
+ * recv_pull needs both. */
+EP_API int ep_dispatch_recv_plan(const ep_desc *d, void *plan_ws,
+                                 int32_t *status, hipStream_t stream);
+EP_API int ep_dispatch_recv_pull(const ep_desc *d, const void *const send[2],
+                                 void *const priv[2], int32_t priv_rows,
+                                 const void *plan_ws, void *const grouped[2],
+                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * KV-block push ("vLLMにおける分離型推論のTTFTとTPOTを改善するプッシュ型KV転送",

@@ -141,3 +141,46 @@ def test_pack_quant_full_size(name):
         ys = [oracle.expert_row(row, int(e), 1, H, None) for e in wl.idx[s[i], t[i]]]
         want = oracle.combine_token(wl.weights[s[i], t[i]], ys)
         assert bf16_close(out[i], want).all()
+
+
+@pytest.mark.parametrize("sh", QUANT_SHAPES + [W.CONFIGS["decode_fp8"], W.CONFIGS["prefill"]],
+                         ids=[s.name for s in QUANT_SHAPES] + ["decode_fp8", "prefill"])
+def test_dispatch_quant_equals_three_calls(sh):
+    """ep_dispatch_quant == ep_plan + ep_dispatch_pack_quant + ep_dispatch_recv:
+    plan tables, send planes and delivered grouped rows."""
+    from gpu_util import PLAN_FIELDS
+    wl = W.make_workload(sh)
+    d = desc_of(sh)
+    cap = ep.capacity(d)
+    N = sh.n_ranks
+    note(f"dispatch_quant {sh.name}")
+    x = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda()
+    ref = ep.Buffers(d)
+    ref.idx.copy_(torch.from_numpy(wl.idx))
+    ref.status.zero_()
+    ep.plan(d, ref.idx, ref.plan_ws, ref.status)
+    ep.dispatch_pack_quant(d, x, ref.plan_ws, ref.send)
+    ep.dispatch_recv(d, ref.send, ref.plan_ws, ref.grouped)
+    torch.cuda.synchronize()
+    want = plan_arrays(d, ref)
+    totals = want["recv_off"][:, N]
+    rows = [min(int(totals[dd]), cap) for dd in range(N)]
+    ref_send = [t.clone() for t in ref.send]
+    ref_grouped = [[g[dd, :rows[dd]].clone() for dd in range(N)] for g in ref.grouped]
+    del ref
+    gc.collect()
+    b = ep.Buffers(d)
+    b.idx.copy_(torch.from_numpy(wl.idx))
+    b.plan_ws.fill_(0x3C)
+    b.status.zero_()
+    ep.dispatch_quant(d, b.idx, x, b.plan_ws, b.send, b.grouped, b.status)
+    torch.cuda.synchronize()
+    assert int(b.status.item()) == 0
+    got = plan_arrays(d, b)
+    for f in PLAN_FIELDS:
+        np.testing.assert_array_equal(got[f], want[f], err_msg=f)
+    for t, rt in zip(b.send, ref_send):
+        assert torch.equal(t, rt)
+    for g, rg in zip(b.grouped, ref_grouped):
+        for dd in range(N):
+            assert torch.equal(g[dd, :rows[dd]], rg[dd]), f"grouped {dd}"

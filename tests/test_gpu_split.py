@@ -231,3 +231,69 @@ def test_split_full_size(name, P):
         for dd in range(N):
             assert torch.equal(g[dd, :rows[dd]], rg[dd]), f"grouped {dd}"
     assert torch.equal(b.out, ref_out)
+
+
+def run_overlapped(d, b, wl, P, sa, sb):
+    """send_plan on stream A; the exchange (recv_plan) on stream B while A
+    packs; the pull after both."""
+    priv = ep.priv_buffers(d, P) if P > 0 else []
+    alpha = torch.from_numpy(wl.alpha).to(b.idx.device) if wl.alpha is not None else None
+    b.status.zero_()
+    torch.cuda.synchronize()
+    ep.dispatch_send_plan(d, b.idx, b.plan_ws, b.status, sa)
+    counts_ready = torch.cuda.Event()
+    counts_ready.record(sa)
+    sb.wait_event(counts_ready)
+    ep.dispatch_recv_plan(d, b.plan_ws, b.status, sb)
+    offsets_ready = torch.cuda.Event()
+    offsets_ready.record(sb)
+    ep.dispatch_send_pack(d, b.idx, b.x, b.plan_ws, b.send, priv, P, sa)
+    sa.wait_event(offsets_ready)
+    ep.dispatch_recv_pull(d, b.send, priv, P, b.plan_ws, b.grouped, sa)
+    ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out, sa)
+    ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, sa)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,P", [("tiny", 0), ("tiny_zipf", 3), ("decode", 0), ("decode", 4),
+                                    ("worst", 2)])
+def test_exchange_overlapped_with_pack_equals_unsplit(name, P):
+    sh = W.CONFIGS[name]
+    wl = W.make_workload(sh)
+    d = desc_of(sh)
+    N = sh.n_ranks
+    cap = ep.capacity(d)
+    note(f"split overlapped {name} P={P}")
+    ref = ep.Buffers(d)
+    upload(ref, wl)
+    run_path(d, ref, wl)
+    torch.cuda.synchronize()
+    want = plan_arrays(d, ref)
+    totals = want["recv_off"][:, N]
+    rows = [min(int(totals[dd]), cap) for dd in range(N)]
+    ref_grouped = [[g[dd, :rows[dd]].clone() for dd in range(N)] for g in ref.grouped]
+    ref_out = ref.out.clone()
+    del ref
+    gc.collect()
+    b = ep.Buffers(d)
+    upload(b, wl)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    run_overlapped(d, b, wl, P, sa, sb)
+    assert int(b.status.item()) == 0
+    got = plan_arrays(d, b)
+    for f in PLAN_FIELDS:
+        np.testing.assert_array_equal(got[f], want[f], err_msg=f)
+    for g, rg in zip(b.grouped, ref_grouped):
+        for dd in range(N):
+            assert torch.equal(g[dd, :rows[dd]], rg[dd]), f"grouped {dd}"
+    assert torch.equal(b.out, ref_out)
+
+
+def test_split_pieces_validate_before_enqueueing():
+    sh = W.CONFIGS["tiny"]
+    d = desc_of(sh)
+    b = ep.Buffers(d)
+    with pytest.raises(ep.EPError):
+        ep.dispatch_send(d, b.idx, b.x, b.plan_ws, [None], [], 0, b.status)   # null send plane
+    with pytest.raises(ep.EPError):
+        ep.dispatch_recv_pull(d, b.send, [], 1, b.plan_ws, b.grouped)          # P > 0, no priv
