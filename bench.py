@@ -50,11 +50,16 @@ def algorithmic_bytes(sh, row_d: int, quant: bool) -> dict:
 # Device sources each stage's kernels are built from (recorded counters of a
 # kernel stay valid while these files are unchanged).
 STAGE_SOURCES = {
-    "plan": ["ep_plan.hip", "ep_kernels.hpp", "ep_device.hpp"],
+    "plan": ["ep_plan.hip", "ep_plan_device.hpp", "ep_kernels.hpp", "ep_device.hpp"],
     "pack": ["ep_dispatch.hip", "ep_device.hpp"],
     "pack_quant": ["ep_quant.hip", "ep_device.hpp"],
     "recv": ["ep_dispatch.hip", "ep_device.hpp"],
     "combine": ["ep_combine.hip", "ep_device.hpp"],
+    "plan_local": ["ep_plan.hip", "ep_plan_device.hpp", "ep_kernels.hpp", "ep_device.hpp"],
+    "pack_exchange": ["ep_dispatch.hip", "ep_plan_device.hpp", "ep_kernels.hpp",
+                      "ep_device.hpp"],
+    "pack_quant_exchange": ["ep_quant.hip", "ep_plan_device.hpp", "ep_kernels.hpp",
+                            "ep_device.hpp"],
 }
 
 
