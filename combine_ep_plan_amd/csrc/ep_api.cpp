@@ -178,11 +178,22 @@ int check_ptr(const void* p, int dev, const char* name, int64_t bytes = 1) {
 }
 
 // rows: rows of every plane buffer (its bytes are rows * row bytes).
+// Row buffers are moved with 16-byte vector accesses: their base must be
+// 16-byte aligned (every row then is, row sizes being multiples of 16 or
+// moved 4 bytes at a time).
+int check_aligned16(const void* p, const char* name) {
+  if (((uintptr_t)p & 15) != 0)
+    return fail(EP_ERR_INVALID_ARG, (std::string("not 16-byte aligned: ") + name).c_str());
+  return EP_OK;
+}
+
 int check_planes(const ep::Dims& d, const void* const* pl, int dev, const char* name,
                  int64_t rows) {
   if (!pl) return fail(EP_ERR_INVALID_ARG, (std::string("null plane array: ") + name).c_str());
   for (int q = 0; q < d.planes; ++q) {
-    const int rc = check_ptr(pl[q], dev, name, rows * d.row[q]);
+    int rc = check_ptr(pl[q], dev, name, rows * d.row[q]);
+    if (rc != EP_OK) return rc;
+    rc = check_aligned16(pl[q], name);
     if (rc != EP_OK) return rc;
   }
   if (d.planes == 1 && pl[1] != nullptr)
@@ -306,6 +317,7 @@ int ep_dispatch_pack_quant(const ep_desc* d, const uint16_t* x, const void* plan
   if (dims.NT * (((int64_t)dims.H + 1023) / 1024) >= kMaxWaves)
     return fail(EP_ERR_UNSUPPORTED, "tokens x 1024-value row segments must be < 2^26");
   EP_CHECK(check_ptr(x, scope.device(), "x", dims.NT * 2 * (int64_t)dims.H));
+  EP_CHECK(check_aligned16(x, "x"));
   EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
   const hipError_t e = ep::launch_pack_quant(dims, x, pp, send, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_dispatch_pack_quant");
@@ -323,6 +335,7 @@ int ep_dispatch_quant(const ep_desc* d, const int32_t* topk_idx, const uint16_t*
   EP_CHECK(check_ptr(status, scope.device(), "status"));
   EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
   EP_CHECK(check_ptr(x, scope.device(), "x", dims.NT * 2 * (int64_t)dims.H));
+  EP_CHECK(check_aligned16(x, "x"));
   EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
   EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
   const hipError_t e = ep::launch_dispatch_quant(dims, topk_idx, x, pp, send, grouped, status, stream);
@@ -449,6 +462,7 @@ int ep_expert_stub(const ep_desc* d, const void* const grouped[2], const float* 
   EP_PROLOGUE(d, stream, plan_ws);
   EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
   EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap));
+  EP_CHECK(check_aligned16(expert_out, "expert_out"));
   if (alpha) {
     if (dims.payload != EP_PAYLOAD_BF16)
       return fail(EP_ERR_INVALID_ARG, "alpha applies to the bf16 payload only");
@@ -465,6 +479,8 @@ int ep_combine(const ep_desc* d, const uint16_t* expert_out, const float* weight
   EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap));
   EP_CHECK(check_ptr(out, scope.device(), "out", dims.NT));
   EP_CHECK(check_ptr(weights, scope.device(), "weights", dims.NTR));
+  EP_CHECK(check_aligned16(expert_out, "expert_out"));
+  EP_CHECK(check_aligned16(out, "out"));
   const hipError_t e = ep::launch_combine(dims, expert_out, weights, pp, out, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_combine");
   return EP_OK;
@@ -477,6 +493,9 @@ int ep_combine_presum(const ep_desc* d, const uint16_t* expert_out, const float*
   EP_CHECK(check_ptr(partial, scope.device(), "partial", dims.NTR));
   EP_CHECK(check_ptr(out, scope.device(), "out", dims.NT));
   EP_CHECK(check_ptr(weights, scope.device(), "weights", dims.NTR));
+  EP_CHECK(check_aligned16(expert_out, "expert_out"));
+  EP_CHECK(check_aligned16(partial, "partial"));
+  EP_CHECK(check_aligned16(out, "out"));
   const hipError_t e = ep::launch_combine_presum(dims, expert_out, weights, pp, partial, out, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_combine_presum");
   return EP_OK;

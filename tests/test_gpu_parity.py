@@ -347,3 +347,17 @@ def test_full_size_prefill_fp8():
         for t in range(T):
             want[s, t] = oracle.expert_row([wl.planes[0][s, t], wl.planes[1][s, t]], 0, 1, H, None)
     assert_tokens_equal(b.out, want, "prefill combine")
+
+
+def test_misaligned_row_buffers_are_rejected():
+    sh = W.CONFIGS["tiny"]
+    d = desc_of(sh)
+    b = ep.Buffers(d)
+    raw = torch.empty(b.x[0].numel() + 64, dtype=torch.uint8, device="cuda")
+    shifted = raw[8:8 + b.x[0].numel()]                  # 8-byte aligned only
+    with pytest.raises(ep.EPError) as e:
+        ep.dispatch_pack(d, [shifted], b.plan_ws, b.send)
+    assert e.value.code == ep.EP_ERR_INVALID_ARG and "aligned" in str(e.value)
+    out_raw = torch.empty(b.out.numel() + 8, dtype=torch.int16, device="cuda")
+    with pytest.raises(ep.EPError):
+        ep.combine(d, b.expert_out, b.weights, b.plan_ws, out_raw[4:4 + b.out.numel()])

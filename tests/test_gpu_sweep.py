@@ -1,0 +1,83 @@
+"""Seeded sweep of random small shapes through the one-call dispatch, the
+stand-in expert, combine and the partial-sum combine, against the oracle:
+random N, experts per rank, R (including R > E / N with repeated ids), T
+(including 0), H, payload, invalid ids and tight capacities."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_plan_amd as ep
+import ep_workloads as W
+import oracle
+from gpu_util import bf16_close, desc_of, expected_plan_extras, note, plan_arrays, upload
+
+pytestmark = pytest.mark.gpu
+
+CASES = 40
+
+
+def draw_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    N = int(rng.integers(1, 17))
+    L = int(rng.integers(1, 9))
+    E = N * L
+    R = int(rng.integers(1, 13))
+    T = int(rng.choice([0, 1, 3, 17, 64, 129, 300]))
+    fp8 = bool(rng.random() < 0.3)
+    H = int(rng.choice([128, 256, 1024])) if fp8 else int(rng.choice([8, 64, 136, 1000, 2048]))
+    sh = W.Shape(f"sweep{seed}", N, T, H, E, R, payload=W.PAYLOAD_FP8_B128 if fp8 else W.PAYLOAD_BF16,
+                 expert="dequant" if fp8 else "scale", seed=seed)
+    idx = rng.integers(0, E, size=(N, T, R)).astype(np.int32)   # repeats allowed
+    if rng.random() < 0.3 and idx.size:
+        bad = rng.random(idx.shape) < 0.05
+        idx[bad] = rng.choice([-1, E, E + 7], size=int(bad.sum()))
+    wl = W.make_workload(sh, idx=idx)
+    cap = 0
+    if rng.random() < 0.3 and idx.size:
+        full = oracle.plan(N, T, E, R, oracle.recv_bound(N, T, E, R), idx)
+        cap = max(1, int(full["recv_off"][:, N].max()) - int(rng.integers(0, 4)))
+    return sh, wl, cap
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_sweep_against_oracle(seed):
+    sh, wl, cap = draw_case(seed)
+    d = desc_of(sh, cap)
+    cap = ep.capacity(d)
+    N = sh.n_ranks
+    note(f"sweep {seed}: N={N} T={sh.tokens} H={sh.hidden} E={sh.n_experts} R={sh.topk} "
+         f"payload={sh.payload} cap={cap}")
+    b = ep.Buffers(d)
+    upload(b, wl)
+    alpha = torch.from_numpy(wl.alpha).cuda() if wl.alpha is not None else None
+    b.status.zero_()
+    ep.dispatch(d, b.idx, b.x, b.plan_ws, b.send, b.grouped, b.status)
+    ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out)
+    ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out)
+    partial = torch.zeros((N, sh.tokens * sh.topk, sh.hidden), dtype=torch.int16, device="cuda")
+    pout = torch.zeros_like(b.out)
+    ep.combine_presum(d, b.expert_out, b.weights, b.plan_ws, partial, pout)
+    torch.cuda.synchronize()
+    ref = oracle.run(wl, cap=cap)
+    p = ref["plan"]
+    assert int(b.status.item()) == p["status"]
+    got = plan_arrays(d, b)
+    for f in ("cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos"):
+        np.testing.assert_array_equal(got[f], p[f], err_msg=f)
+    for f, v in expected_plan_extras(p, wl.idx, N, sh.n_experts, cap).items():
+        np.testing.assert_array_equal(got[f], v, err_msg=f)
+    totals = p["recv_off"][:, N]
+    for q in range(len(wl.planes)):
+        g = b.grouped[q].cpu().numpy()
+        for dd in range(N):
+            n = min(int(totals[dd]), cap)
+            np.testing.assert_array_equal(g[dd, :n], ref["grouped"][q][dd, :n])
+    out = b.out.cpu().numpy().view(np.uint16)
+    assert bf16_close(out, ref["out"]).all()
+    want_partial, want_out = oracle.combine_presum(ref["y"], wl.weights, wl.idx, p)
+    np.testing.assert_array_equal(pout.cpu().numpy().view(np.uint16), want_out)
+    np.testing.assert_array_equal(partial.cpu().numpy().view(np.uint16), want_partial)
+    del b
+    gc.collect()
