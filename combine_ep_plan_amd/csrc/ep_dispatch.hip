@@ -501,10 +501,10 @@ bool pack_exchange_fits(const Dims& d) {
   return dispatch_fused_fits(d) && v0 > 0 && (d.planes == 1 || v1 == 1);
 }
 
-// LDS of the exchange with kBlock threads (see exchange_block).
-size_t lds_exchange_bytes(const Dims& d) {
-  const int groups = d.E >= kBlock ? 1 : kBlock / d.E;
-  return sizeof(int32_t) * ((size_t)4 * (d.E + 1) + (d.N + 1) + kBlock / kWave +
+// LDS of the exchange with tpb threads per block (see exchange_block).
+size_t lds_exchange_bytes(const Dims& d, int tpb) {
+  const int groups = d.E >= tpb ? 1 : tpb / d.E;
+  return sizeof(int32_t) * ((size_t)4 * (d.E + 1) + (d.N + 1) + tpb / kWave +
                             (size_t)2 * groups * d.E);
 }
 
@@ -513,7 +513,7 @@ hipError_t launch_pack_exchange_v(const Dims& d, const void* const x[2], const P
                                   void* const send[2], int32_t* status, hipStream_t stream) {
   const unsigned grid = (unsigned)d.N + blocks_for((d.NT + 1) / 2);
   hipLaunchKernelGGL((pack_exchange_kernel<V0, V1>), dim3(grid), dim3(kBlock),
-                     lds_exchange_bytes(d), stream, (const uint8_t*)x[0], (uint8_t*)send[0],
+                     lds_exchange_bytes(d, kBlock), stream, (const uint8_t*)x[0], (uint8_t*)send[0],
                      d.planes > 1 ? (const uint8_t*)x[1] : nullptr,
                      d.planes > 1 ? (uint8_t*)send[1] : nullptr, p, d.N, d.E, d.L, d.T, d.R,
                      d.cap, (int)d.row[0], d.planes > 1 ? (int)d.row[1] : 0, status);

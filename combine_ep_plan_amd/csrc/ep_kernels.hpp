@@ -62,7 +62,7 @@ hipError_t launch_dispatch_quant(const Dims& d, const int32_t* idx, const uint16
 // Whether the one-call dispatch can fold the count exchange into the sender
 // launch, and the LDS bytes the exchange blocks need.
 bool dispatch_fused_fits(const Dims& d);
-size_t lds_exchange_bytes(const Dims& d);
+size_t lds_exchange_bytes(const Dims& d, int threads_per_block);
 hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
                        void* const send[2], hipStream_t stream);
 hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p,

@@ -55,11 +55,15 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
   return sign | code;
 }
 
-// The sender's work for wave w (token w / nseg, segment w % nseg).
+// The sender's work for wave w (token w / nseg, segment w % nseg). With
+// ROW_SCALES the wave also writes its blocks' scales to the R send rows;
+// otherwise it leaves them in tok_scale (LDS, indexed by block) for the
+// workgroup to write whole scale rows.
+template <bool ROW_SCALES>
 __device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x,
                                            uint8_t* __restrict__ codes, float* __restrict__ scales,
                                            const int32_t* __restrict__ send_pos, int NT, int T,
-                                           int R, int H, int nseg) {
+                                           int R, int H, int nseg, float* tok_scale) {
   const int tok = w / nseg;
   if (tok >= NT) return;
   const int lane = lane_id();
@@ -110,6 +114,7 @@ __device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x
   }
   const int blk0 = base / 16;
   const int seg_blocks = nblk - blk0 < kQBlocks ? nblk - blk0 : kQBlocks;
+  if (!ROW_SCALES && lane < seg_blocks) tok_scale[blk0 + lane] = my_scale;
   for (int k = 0; k < R; ++k) {
     const int p = send_pos[(size_t)tok * R + k];
     if (p < 0 || p >= TR) continue;
@@ -122,15 +127,58 @@ __device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x
         __builtin_nontemporal_store((uint64_t)packed[i][0] | ((uint64_t)packed[i][1] << 32),
                                     &crow[c]);
     }
-    if (lane < seg_blocks)
+    if (ROW_SCALES && lane < seg_blocks)
       __builtin_nontemporal_store(my_scale, &scales[row * nblk + blk0 + lane]);
+  }
+}
+
+// One workgroup of kTokWaves waves per token (H <= kTokWaves * 1024): the
+// waves quantise their segments and write the codes, then the token's whole
+// scale row (4 H / 128 bytes) goes to each of its R send rows in one store.
+// Scale rows written in 32-byte pieces by separate waves cost ~10% of the
+// sender's time (51 vs 46 us at decode shapes with the scale stores left
+// out); with whole rows the decode-shape dispatch + combine step took 226 us
+// against 232 us (prefill shapes: unchanged).
+constexpr int kTokThreads = 512;
+constexpr int kTokWaves = kTokThreads / kWave;
+
+template <bool EXCHANGE>
+__global__ __launch_bounds__(kTokThreads) void pack_quant_tok_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
+    PlanPtrs p, int NT, int N, int E, int L, int T, int R, int H, int nseg, int64_t cap,
+    int32_t* status) {
+  __shared__ float tok_scale[kTokWaves * kQBlocks];
+  extern __shared__ int32_t lds[];
+  int b = blockIdx.x;
+  if (EXCHANGE) {
+    if (b < N) {  // block-uniform: the count exchange (see pack_exchange_kernel)
+      exchange_block<kTokThreads>(b, 0, b, N, N, E, L, (int64_t)T * R, cap, p, status, lds);
+      return;
+    }
+    b -= N;
+  }
+  const int tok = b;
+  if (tok >= NT) return;  // block-uniform
+  const int wv = (int)threadIdx.x / kWave;
+  if (wv < nseg)
+    quant_wave<false>(tok * nseg + wv, x, codes, scales, p.send_pos, NT, T, R, H, nseg, tok_scale);
+  __syncthreads();
+  const int lane = lane_id();
+  const int nblk = H / 128;
+  const int TR = T * R;
+  const int s = tok / T;
+  for (int k = wv; k < R; k += kTokWaves) {
+    const int pos = p.send_pos[(size_t)tok * R + k];
+    if (pos < 0 || pos >= TR) continue;
+    if (lane < nblk)
+      __builtin_nontemporal_store(tok_scale[lane], &scales[((size_t)s * TR + pos) * nblk + lane]);
   }
 }
 
 __global__ __launch_bounds__(kBlock) void pack_quant_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, float* __restrict__ scales,
     const int32_t* __restrict__ send_pos, int NT, int T, int R, int H, int nseg) {
-  quant_wave(wave_index(), x, codes, scales, send_pos, NT, T, R, H, nseg);
+  quant_wave<true>(wave_index(), x, codes, scales, send_pos, NT, T, R, H, nseg, nullptr);
 }
 
 // As pack_quant_kernel, with the count exchange done by the first N blocks
@@ -146,7 +194,7 @@ __global__ __launch_bounds__(kBlock) void pack_quant_exchange_kernel(
     return;
   }
   const int w = wave_uniform((b - N) * kWavesPerBlock + (int)threadIdx.x / kWave);
-  quant_wave(w, x, codes, scales, p.send_pos, N * T, T, R, H, nseg);
+  quant_wave<true>(w, x, codes, scales, p.send_pos, N * T, T, R, H, nseg, nullptr);
 }
 
 }  // namespace
@@ -155,6 +203,12 @@ hipError_t launch_pack_quant(const Dims& d, const uint16_t* x, const PlanPtrs& p
                              void* const send[2], hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
   const int nseg = (d.H / 8 + kQSeg - 1) / kQSeg;
+  if (nseg <= kTokWaves) {
+    hipLaunchKernelGGL(pack_quant_tok_kernel<false>, dim3((unsigned)d.NT), dim3(kTokThreads), 0,
+                       stream, x, (uint8_t*)send[0], (float*)send[1], p, (int)d.NT, d.N, d.E,
+                       d.L, d.T, d.R, d.H, nseg, d.cap, (int32_t*)nullptr);
+    return hipGetLastError();
+  }
   const int64_t waves = d.NT * nseg;
   hipLaunchKernelGGL(pack_quant_kernel, dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                      dim3(kBlock), 0, stream, x, (uint8_t*)send[0], (float*)send[1], p.send_pos,
@@ -174,9 +228,19 @@ hipError_t launch_dispatch_quant(const Dims& d, const int32_t* idx, const uint16
   hipError_t e = launch_plan_local(d, idx, p, status, stream);
   if (e != hipSuccess) return e;
   const int nseg = (d.H / 8 + kQSeg - 1) / kQSeg;
+  if (nseg <= kTokWaves) {
+    hipLaunchKernelGGL(pack_quant_tok_kernel<true>, dim3((unsigned)(d.N + d.NT)),
+                       dim3(kTokThreads), lds_exchange_bytes(d, kTokThreads), stream, x,
+                       (uint8_t*)send[0], (float*)send[1], p, (int)d.NT, d.N, d.E, d.L, d.T, d.R,
+                       d.H, nseg, d.cap, status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_recv(d, send, p, grouped, stream);
+  }
   const int64_t waves = d.NT * nseg;
   const unsigned grid = (unsigned)d.N + (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-  hipLaunchKernelGGL(pack_quant_exchange_kernel, dim3(grid), dim3(kBlock), lds_exchange_bytes(d),
+  hipLaunchKernelGGL(pack_quant_exchange_kernel, dim3(grid), dim3(kBlock),
+                     lds_exchange_bytes(d, kBlock),
                      stream, x, (uint8_t*)send[0], (float*)send[1], p, d.N, d.E, d.L, d.T, d.R,
                      d.H, nseg, d.cap, status);
   e = hipGetLastError();
