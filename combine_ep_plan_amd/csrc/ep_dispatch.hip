@@ -1,5 +1,6 @@
-// Dispatch data movement: sender pack, the per-pair transfer, the receiver
-// unpack, and the receiver with the transfer fused in (pull).
+// Dispatch data movement: the senders (plain, split with private regions,
+// and with the count exchange folded in), the per-pair transfer, the
+// receiver unpack, and the receivers with the transfer fused in (pull).
 //
 // Method: "Enabling trillion-parameter models on AWS EFA", section
 // "Dispatch and combine": the sender shuffles tokens into a send buffer laid
@@ -7,13 +8,15 @@
 // receive buffer into the grouped-GEMM input; within a node, buffers mapped
 // into the peers let a rank pull tokens directly.
 //
-// All kernels move rows as opaque bytes, in segments of 448 16-byte chunks
-// (7 KB): one wave owns one segment of a row (a 14 KB bf16 row at H = 7168 is
-// two waves), lane l moves chunks l, l+64, ... of the segment, and all of a
-// segment's chunks are loaded before the first store. Measured on gfx950, a
-// plain copy runs at 6.4 TB/s with 7 KB per wave against 5.8 TB/s with 14 KB
-// per wave (more waves resident at fewer registers each). Row indices are
-// wave-uniform and live in scalar registers.
+// Rows move as opaque bytes; lane l of a wave moves 16-byte chunks l, l+64,
+// ... and all chunks a wave holds are loaded before the first store. The
+// receivers, the transfer and the unpack give one wave each 448-chunk (7 KB)
+// segment of a row (a 14 KB bf16 row at H = 7168 is two waves): measured on
+// gfx950, a plain copy runs at 6.4 TB/s with 7 KB per wave against 5.8 TB/s
+// with 14 KB per wave (more waves resident at fewer registers each). The
+// senders give one wave a token pair instead (store-heavy: each row is
+// written R times). Row indices are wave-uniform and live in scalar
+// registers.
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 #include "ep_plan_device.hpp"
