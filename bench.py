@@ -64,14 +64,21 @@ STAGE_SOURCES = {
 
 
 def kernel_source_hash(files) -> str:
-    """Hash of the named device sources under combine_ep_plan_amd/csrc."""
+    """Hash of the code (comments and blank lines dropped) of the named device
+    sources under combine_ep_plan_amd/csrc."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in files:
         h.update(f.encode())
-        with open(os.path.join(ROOT, "combine_ep_plan_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "combine_ep_plan_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
