@@ -387,6 +387,9 @@ def main() -> int:
     ap.add_argument("--prequantized", action="store_true",
                     help="fp8 payloads: send pre-quantised rows with the plain sender "
                          "instead of quantising bf16 rows in the sender")
+    ap.add_argument("--flushed-steps", type=int, default=20,
+                    help="extra steps, each after a 1 GiB copy that evicts the caches, "
+                         "timed one by one (reported beside the main figure)")
     ap.add_argument("--split", type=int, default=-1, metavar="P",
                     help="also measure the split dispatch with P private rows per "
                          "(destination, source) pair, alone and overlapped with a "
@@ -547,6 +550,19 @@ def main() -> int:
     c1.record(stream)
     torch.cuda.synchronize()
     copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    # Cold-cache steps: before each one, a 1 GiB copy (outside the events)
+    # evicts what the previous step left in the L2s and the MALL; each step is
+    # timed alone between two events.
+    flushed = []
+    for i in range(args.flushed_steps):
+        ep.probe_copy(dst, src, nbytes, sp)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        step()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        flushed.append(f0.elapsed_time(f1) * 1e3)
     del src, dst
 
     split = None
@@ -618,6 +634,8 @@ def main() -> int:
         "instrumented_step_us_p10_p50_p90": [round(float(np.percentile(steps_ms, q)) * 1e3, 2)
                                              for q in (10, 50, 90)],
         "instrumented_steps": len(steps_ms),
+        "cold_cache_step_us_p10_p50_p90": ([round(float(np.percentile(flushed, q)), 2)
+                                            for q in (10, 50, 90)] if flushed else None),
         "wall_ms": round(wall_ms, 3),
         "roofline": {
             "kernel": f"ep_dispatch_{dom}" if dom in ("pack", "recv") else f"ep_{dom}",
