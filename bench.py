@@ -601,6 +601,7 @@ def main() -> int:
         payload_name = "fp8 e4m3 + fp32 scale per 128 values, quantised in the sender"
     else:
         payload_name = "fp8 e4m3 + fp32 scale per 128 values, pre-quantised"
+    traffic = recorded_traffic(args.config, "pack_quant" if dom == "pack" and quant else dom)
     res = {
         "metric": METRIC,
         "value": round(eff, 2),
@@ -624,6 +625,7 @@ def main() -> int:
             "global_batch": sh.n_ranks * sh.tokens,
         },
         "us_per_dispatch_combine": round(ms_per_step * 1e3, 2),
+        "us_per_virtual_rank": round(ms_per_step * 1e3 / sh.n_ranks, 3),
         "frac_of_hbm_peak": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": ab["step"],
         "step_form": ("ep_dispatch_quant" if quant else "ep_dispatch") +
@@ -644,8 +646,8 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": recorded_traffic(args.config, "pack_quant" if dom == "pack" and quant
-                                        else dom),
+            "traffic": traffic,
+            "traffic_GBps": None if traffic is None else round(traffic / (dom_ms * 1e-3) / 1e9, 2),
             "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
             "algorithmic_bytes": ab["stages"][dom],
             "avg_us": round(dom_ms * 1e3, 2),
