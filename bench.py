@@ -537,6 +537,15 @@ def main() -> int:
     dom_ms = k0.elapsed_time(k1) / 20
     achieved = ab["stages"][dom] / (dom_ms * 1e-3) / 1e9
 
+    # the stand-in expert, outside the step (reported, not part of the metric)
+    x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    x0.record(stream)
+    for _ in range(5):
+        ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out, sp)
+    x1.record(stream)
+    torch.cuda.synchronize()
+    expert_us = x0.elapsed_time(x1) / 5 * 1e3
+
     # copy ceiling of this GPU with the library's own row-copy loop (context)
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
@@ -626,6 +635,7 @@ def main() -> int:
         },
         "us_per_dispatch_combine": round(ms_per_step * 1e3, 2),
         "us_per_virtual_rank": round(ms_per_step * 1e3 / sh.n_ranks, 3),
+        "expert_stand_in_us": round(expert_us, 2),
         "frac_of_hbm_peak": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": ab["step"],
         "step_form": ("ep_dispatch_quant" if quant else "ep_dispatch") +
