@@ -376,6 +376,45 @@ def measure_kv(ep, torch, np, W, reps: int = 10) -> dict:
     return res
 
 
+def measure_staged(ep, torch, d, sh, wl, steps: int, warmup: int) -> dict:
+    """The dispatch with the network write materialised (ep_dispatch_transfer
+    into receive buffers, then ep_dispatch_unpack) against the receiver with
+    the transfer fused in (ep_dispatch_recv)."""
+    import statistics as st
+
+    b = ep.Buffers(d, device="cuda:0", staged=True)
+    b.idx.copy_(torch.from_numpy(wl.idx))
+    b.weights.copy_(torch.from_numpy(wl.weights))
+    for q, plane in enumerate(wl.planes):
+        b.x[q].copy_(torch.from_numpy(plane))
+    s = torch.cuda.current_stream()
+    sp = s.cuda_stream
+    ep.plan(d, b.idx, b.plan_ws, b.status, sp)
+    ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)
+
+    def staged():
+        ep.dispatch_transfer(d, b.send, b.plan_ws, b.recv, sp)
+        ep.dispatch_unpack(d, b.recv, b.plan_ws, b.grouped, sp)
+
+    def fused():
+        ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp)
+
+    out = {}
+    for name, fn in (("transfer_then_unpack_us", staged), ("fused_pull_us", fused)):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+    del b
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,6 +433,9 @@ def main() -> int:
                     help="also measure the split dispatch with P private rows per "
                          "(destination, source) pair, alone and overlapped with a "
                          "shared-expert stand-in on a second stream")
+    ap.add_argument("--staged", action="store_true",
+                    help="also time the materialised network write + unpack against the "
+                         "fused receiver")
     ap.add_argument("--presum", action="store_true",
                     help="also measure the combine with partial sums on the expert side")
     ap.add_argument("--kv", action="store_true",
@@ -582,6 +624,10 @@ def main() -> int:
     if args.presum:
         presum = measure_presum(ep, torch, np, d, b, sh, wl, args.steps, args.warmup)
 
+    staged = None
+    if args.staged:
+        staged = measure_staged(ep, torch, d, sh, wl, max(args.steps // 5, 10), 3)
+
     kv = None
     if args.kv:
         kv = measure_kv(ep, torch, np, W)
@@ -672,6 +718,8 @@ def main() -> int:
         res["presum"] = presum
     if kv is not None:
         res["kv_push"] = kv
+    if staged is not None:
+        res["staged_receive"] = staged
     print(json.dumps(res), flush=True)
     return 0
 
