@@ -433,6 +433,9 @@ def main() -> int:
                     help="also measure the split dispatch with P private rows per "
                          "(destination, source) pair, alone and overlapped with a "
                          "shared-expert stand-in on a second stream")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps as one HIP graph and replay it (removes "
+                         "launch overhead; matters for launch-bound small workloads)")
     ap.add_argument("--staged", action="store_true",
                     help="also time the materialised network write + unpack against the "
                          "fused receiver")
@@ -538,6 +541,32 @@ def main() -> int:
     wall_ms = (time.perf_counter() - t0) * 1e3
     steps_ms = [ev[0].elapsed_time(ev[-1]) for ev in events.values()]
     dispatch_call_us = statistics.mean(ev[0].elapsed_time(ev[1]) for ev in events.values()) * 1e3
+
+    graph_step_us = None
+    if args.graph:
+        # The same K steps captured once as a HIP graph (timing events cannot
+        # be recorded inside a capture, so none are) and replayed: one launch
+        # for K steps, which removes the per-call launch cost.
+        cap_stream = torch.cuda.Stream()
+        cap_stream.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap_stream):
+            cs = cap_stream.cuda_stream
+            for _ in range(args.steps):
+                if quant:
+                    ep.dispatch_quant(d, b.idx, x_bf16, b.plan_ws, b.send, b.grouped, b.status, cs)
+                else:
+                    ep.dispatch(d, b.idx, b.x, b.plan_ws, b.send, b.grouped, b.status, cs)
+                ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, cs)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_step_us = g0.elapsed_time(g1) * 1e3 / args.steps
+        del graph
     # Per-stage times (and the dominant kernel's) from the four separate
     # calls, after the timed region; the receiver kernel is the same launch
     # in both forms of the step.
@@ -687,6 +716,9 @@ def main() -> int:
         "step_form": ("ep_dispatch_quant" if quant else "ep_dispatch") +
                      " (plan + pack + recv) then ep_combine",
         "dispatch_call_us": round(dispatch_call_us, 2),
+        **({"graph_step_us": round(graph_step_us, 2),
+            "graph_from": "the K steps captured as one HIP graph, one replay between two events"}
+           if graph_step_us is not None else {}),
         "stages_us": {n: round(statistics.mean(per[n]) * 1e3, 2) for n in stage_names},
         "stages_from": "the four separate calls, sampled after the timed steps",
         "instrumented_step_us_p10_p50_p90": [round(float(np.percentile(steps_ms, q)) * 1e3, 2)
