@@ -91,12 +91,12 @@ int derive(const ep_desc* d, ep::Dims* o) {
 
 // Plan workspace: int32 arrays, each starting on a 256-byte boundary.
 struct Layout {
-  size_t off[10];
+  size_t off[11];
   size_t bytes;
 };
 
 Layout layout_of(const ep::Dims& d) {
-  const size_t n[10] = {
+  const size_t n[11] = {
       (size_t)d.N * d.E,                       // cnt
       (size_t)d.N * (d.E + 1),                 // send_off
       (size_t)d.NTR,                           // send_pos
@@ -107,10 +107,11 @@ Layout layout_of(const ep::Dims& d) {
       (size_t)d.NTR,                           // comb_row
       (size_t)d.NTR,                           // grp_slot
       (size_t)d.N * d.nchunks * d.E,           // chunk_cnt
+      (size_t)d.NTR,                           // send_slot
   };
   Layout l{};
   size_t at = 0;
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < 11; ++i) {
     l.off[i] = at;
     at += (n[i] * sizeof(int32_t) + 255) & ~(size_t)255;
   }
@@ -132,6 +133,7 @@ ep::PlanPtrs plan_ptrs(const ep::Dims& d, const void* ws) {
   p.comb_row = (int32_t*)(b + l.off[7]);
   p.grp_slot = (int32_t*)(b + l.off[8]);
   p.chunk_cnt = (int32_t*)(b + l.off[9]);
+  p.send_slot = (int32_t*)(b + l.off[10]);
   return p;
 }
 
@@ -271,6 +273,7 @@ int ep_plan_views(const ep_desc* d, void* plan_ws, ep_plan_view* v) {
   v->src_off = p.src_off;
   v->comb_row = p.comb_row;
   v->grp_slot = p.grp_slot;
+  v->send_slot = p.send_slot;
   return EP_OK;
 }
 

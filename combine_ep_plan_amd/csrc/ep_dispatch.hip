@@ -212,6 +212,122 @@ __global__ __launch_bounds__(kBlock) void pack_exchange_kernel(
   if (V1 > 0) pack_pass<(V1 > 0 ? V1 : 1)>(x1, send1, p.send_pos, tok0, tok0 + 1 < NT, T, R, row1);
 }
 
+// XCD-aware block order. A launch's workgroups go to gfx950's 8 XCDs in
+// turn (block b runs on XCD b mod 8), and each XCD has its own L2.
+// Renumbering block b as (b mod 8) * nb/8 + b/8 hands XCD x the x-th eighth
+// of the work, in order. nb must be a multiple of 8.
+__device__ __forceinline__ int xcd_block(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
+
+// Division of n < 2^31 by a divisor d >= 1 fixed at launch, with one
+// multiply-high, an add and a shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994: with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l).
+struct FastDiv {
+  uint32_t m, l;
+};
+
+FastDiv fast_div_of(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  return FastDiv{(uint32_t)((((1ull << l) - d) << 32) / d + 1), l};
+}
+
+__device__ __forceinline__ int fast_div(int n, FastDiv f) {
+  return (int)(((uint64_t)__umulhi((uint32_t)n, f.m) + (uint32_t)n) >> f.l);
+}
+
+// Sender in send order. The send buffers of all sources are one array of
+// N T R rows; wave w writes the w-th 1 KB piece of a plane's rows (one
+// 16-byte chunk per lane), reading the token row that send_slot names.
+// Measured on gfx950 (decode scale, 32 x 1024 send rows of 14 KB):
+//   - stores that advance through memory as one front (consecutive waves on
+//     consecutive pieces) run faster than whole rows per wave: a fill writes
+//     6.8 TB/s with 1 KB per wave against 5.3 TB/s with 14 KB;
+//   - each token row is read R times, from L2 (ordinary cached loads), and
+//     the XCD renumbering makes each XCD work through whole sources, so the
+//     rows it re-reads stay in its own L2;
+//   - the sender so takes 73 us against 99 us for the token-order sender
+//     (one wave per token pair, R stores per row); 2 KB and 7 KB pieces per
+//     wave took 76 and 78 us.
+// The fp8 scale plane (rows of H/32 bytes) is too narrow for pieces: there
+// each lane moves one unit (16 bytes, or 4 when the row is not a multiple of
+// 16) of the plane's rows in address order, so every wave writes whole lines.
+struct GatherPlane {
+  const uint8_t* x;
+  uint8_t* send;
+  FastDiv per_row_div;
+  int unit;     // bytes per lane access in the unit path: 16 or 4
+  int per_row;  // pieces per row (piece path) or units per row (unit path)
+  int n16;      // 16-byte chunks per row (piece path)
+  int pieces;   // 1: piece path; 0: unit path
+  int waves;    // waves covering the plane
+  int blocks;   // blocks covering it, a multiple of 8
+};
+
+struct GatherArgs {
+  GatherPlane pl[2];
+  const int32_t* send_slot;
+  FastDiv r_div;
+  int NT, NTR;
+};
+
+__device__ __forceinline__ void gather_wave(const GatherArgs& a, const GatherPlane& pl, int w) {
+  if (pl.pieces) {
+    const int g = wave_uniform(fast_div(w, pl.per_row_div));  // send row
+    const int base = (w - g * pl.per_row) * kWave;
+    const int slot = wave_uniform(a.send_slot[g]);
+    if (slot < 0) return;  // a row its source does not fill
+    const int tok = fast_div(slot, a.r_div);
+    if (tok >= a.NT) return;
+    const size_t row = (size_t)pl.n16 * 16;
+    RowRegs<1> r;
+    load_row16<1, false>(r, (const u32x4*)(pl.x + (size_t)tok * row), base, pl.n16);
+    store_row16(r, (u32x4*)(pl.send + (size_t)g * row), base, pl.n16);
+    return;
+  }
+  const int64_t c = (int64_t)w * kWave + lane_id();
+  if (c >= (int64_t)a.NTR * pl.per_row) return;
+  const int g = (int)(c / pl.per_row);
+  const int u = (int)(c - (int64_t)g * pl.per_row);
+  const int slot = a.send_slot[g];
+  if (slot < 0) return;
+  const int tok = fast_div(slot, a.r_div);
+  if (tok >= a.NT) return;
+  const size_t src = (size_t)tok * pl.per_row + u;
+  if (pl.unit == 16)
+    store_stream((u32x4*)pl.send + c, ((const u32x4*)pl.x)[src]);
+  else
+    __builtin_nontemporal_store(((const uint32_t*)pl.x)[src], (uint32_t*)pl.send + c);
+}
+
+// Blocks [0, xblocks) do the count exchange when EXCHANGE (blocks < N; the
+// rest of them idle, so xblocks, a multiple of 8, keeps the XCD of every
+// later block equal to its index mod 8); then the blocks of plane 0, then of
+// plane 1, each range renumbered per XCD.
+template <bool EXCHANGE>
+__global__ __launch_bounds__(kBlock) void pack_gather_kernel(GatherArgs a, PlanPtrs p, int N, int E,
+                                                             int L, int T, int R, int64_t cap,
+                                                             int xblocks, int32_t* status) {
+  extern __shared__ int32_t lds[];
+  int b = blockIdx.x;
+  if (EXCHANGE) {
+    if (b < xblocks) {  // block-uniform
+      if (b < N) exchange_block<kBlock>(b, 0, b, N, N, E, L, (int64_t)T * R, cap, p, status, lds);
+      return;
+    }
+    b -= xblocks;
+  }
+  if (b < a.pl[0].blocks) {
+    const int w = xcd_block(b, a.pl[0].blocks) * kWavesPerBlock + (int)threadIdx.x / kWave;
+    if (w < a.pl[0].waves) gather_wave(a, a.pl[0], w);
+  } else {
+    b -= a.pl[0].blocks;
+    if (b >= a.pl[1].blocks) return;
+    const int w = xcd_block(b, a.pl[1].blocks) * kWavesPerBlock + (int)threadIdx.x / kWave;
+    if (w < a.pl[1].waves) gather_wave(a, a.pl[1], w);
+  }
+}
+
 // Chunks per lane for a single pass over a plane of `row` bytes: 14, 7 or 1;
 // 0 if the plane needs the general kernel.
 int pass_v(int64_t row) {
@@ -465,9 +581,15 @@ int waves_per_row(const Dims& d) {
 
 }  // namespace
 
+hipError_t launch_pack_gather(const Dims& d, const void* const x[2], const PlanPtrs& p,
+                              void* const send[2], bool exchange, int32_t* status,
+                              hipStream_t stream);
+bool gather_fits(const Dims& d);
+
 hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
                        void* const send[2], hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
+  if (gather_fits(d)) return launch_pack_gather(d, x, p, send, false, nullptr, stream);
   const dim3 grid(blocks_for((d.NT + 1) / 2));
   const Planes pl = make_planes(d, x, send);
   const int v0 = pass_v(d.row[0]);
@@ -523,6 +645,66 @@ hipError_t launch_pack_exchange_v(const Dims& d, const void* const x[2], const P
   return hipGetLastError();
 }
 
+// The send-order sender re-reads each token row R times and relies on an
+// XCD's 4 MB L2 holding the rows of the source it works on: used when one
+// source's token rows (all planes) take at most this many bytes. Measured
+// at H = 7168 (bf16) against the token-order sender, whole dispatch +
+// combine steps: 1.8 MB per source 90 vs 96 us (8 ranks) and 329 vs 352 us
+// (32 ranks); 3.7 MB 170 vs 182 us; 7.3 MB even; 14.7 MB 743 vs 698 us.
+constexpr int64_t kGatherSourceBytes = 4 << 20;
+
+bool gather_fits(const Dims& d) {
+  int64_t bytes = 0;
+  for (int q = 0; q < d.planes; ++q) bytes += d.row[q];
+  return (int64_t)d.T * bytes <= kGatherSourceBytes;
+}
+
+// A plane takes the piece path when its rows hold at least one 1 KB piece
+// and are a multiple of 16 bytes; otherwise the unit path.
+GatherPlane gather_plane(const void* x, void* send, int64_t row, int64_t NTR) {
+  GatherPlane g{};
+  g.x = (const uint8_t*)x;
+  g.send = (uint8_t*)send;
+  int64_t waves;
+  if ((row & 15) == 0 && row >= 16 * kWave) {
+    g.pieces = 1;
+    g.unit = 16;
+    g.n16 = (int)(row >> 4);
+    g.per_row = (g.n16 + kWave - 1) / kWave;
+    waves = NTR * g.per_row;
+  } else {
+    g.pieces = 0;
+    g.unit = (row & 15) == 0 ? 16 : 4;
+    g.per_row = (int)(row / g.unit);
+    waves = (NTR * g.per_row + kWave - 1) / kWave;
+  }
+  g.per_row_div = fast_div_of((uint32_t)g.per_row);
+  g.waves = (int)waves;
+  g.blocks = (int)((blocks_for(waves) + 7) / 8 * 8);
+  return g;
+}
+
+hipError_t launch_pack_gather(const Dims& d, const void* const x[2], const PlanPtrs& p,
+                              void* const send[2], bool exchange, int32_t* status,
+                              hipStream_t stream) {
+  GatherArgs a{};
+  for (int q = 0; q < d.planes; ++q) a.pl[q] = gather_plane(x[q], send[q], d.row[q], d.NTR);
+  a.send_slot = p.send_slot;
+  a.r_div = fast_div_of((uint32_t)d.R);
+  a.NT = (int)d.NT;
+  a.NTR = (int)d.NTR;
+  const int xblocks = exchange ? (d.N + 7) / 8 * 8 : 0;
+  const unsigned grid = (unsigned)(xblocks + a.pl[0].blocks + a.pl[1].blocks);
+  const size_t lds = exchange ? lds_exchange_bytes(d, kBlock) : 0;
+  if (exchange)
+    hipLaunchKernelGGL(pack_gather_kernel<true>, dim3(grid), dim3(kBlock), lds, stream, a, p, d.N,
+                       d.E, d.L, d.T, d.R, d.cap, xblocks, status);
+  else
+    hipLaunchKernelGGL(pack_gather_kernel<false>, dim3(grid), dim3(kBlock), 0, stream, a, p, d.N,
+                       d.E, d.L, d.T, d.R, d.cap, 0, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs& p,
                        void* const grouped[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
@@ -536,7 +718,7 @@ hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs&
 hipError_t launch_dispatch(const Dims& d, const int32_t* idx, const void* const x[2],
                            const PlanPtrs& p, void* const send[2], void* const grouped[2],
                            int32_t* status, hipStream_t stream) {
-  if (!pack_exchange_fits(d) || d.NT == 0) {
+  if (!(pack_exchange_fits(d) || (dispatch_fused_fits(d) && gather_fits(d))) || d.NT == 0) {
     hipError_t e = launch_plan(d, idx, p, status, stream);
     if (e == hipSuccess) e = launch_pack(d, x, p, send, stream);
     if (e == hipSuccess) e = launch_recv(d, send, p, grouped, stream);
@@ -544,6 +726,11 @@ hipError_t launch_dispatch(const Dims& d, const int32_t* idx, const void* const 
   }
   hipError_t e = launch_plan_local(d, idx, p, status, stream);
   if (e != hipSuccess) return e;
+  if (gather_fits(d)) {
+    e = launch_pack_gather(d, x, p, send, true, status, stream);
+    if (e != hipSuccess) return e;
+    return launch_recv(d, send, p, grouped, stream);
+  }
   const int v0 = pass_v(d.row[0]);
   const int v1 = d.planes > 1 ? pass_v(d.row[1]) : 0;
   if (v1 == 0) {

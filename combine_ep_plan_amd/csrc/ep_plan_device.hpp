@@ -260,7 +260,9 @@ __device__ __forceinline__ void source_sums(const int32_t* __restrict__ chunk_cn
 }
 
 // Send side of the plan for the slots of block (c, s): cnt[s] and
-// send_off[s] (block c == 0) and the final send positions. Returns each
+// send_off[s] (block c == 0), the final send positions and their inverse
+// (send_slot: the slot each send row holds, -1 for the rows past the last
+// one s fills). Returns each
 // slot's index among the rows s sends to its expert (-1 for a bad id).
 template <int TPB>
 __device__ __forceinline__ void send_tables(const int* e_of, const int* rank_of, int s, int c,
@@ -271,8 +273,10 @@ __device__ __forceinline__ void send_tables(const int* e_of, const int* rank_of,
   if (c == 0)
     for (int e = tid; e < E; e += TPB) p.cnt[(size_t)s * E + e] = soff[e];
   block_exclusive_scan<TPB>(soff, E, scratch, &soff[E]);
-  if (c == 0)
+  if (c == 0) {
     for (int e = tid; e <= E; e += TPB) p.send_off[(size_t)s * (E + 1) + e] = soff[e];
+    for (int64_t j = soff[E] + tid; j < TR; j += TPB) p.send_slot[(size_t)s * TR + j] = -1;
+  }
 #pragma unroll
   for (int sub = 0; sub < (kPlanChunk / TPB); ++sub) {
     const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * TPB + tid;
@@ -285,6 +289,7 @@ __device__ __forceinline__ void send_tables(const int* e_of, const int* rank_of,
     }
     within_of[sub] = pre[e] + rank_of[sub];
     p.send_pos[(size_t)s * TR + i] = soff[e] + within_of[sub];
+    p.send_slot[(size_t)s * TR + soff[e] + within_of[sub]] = (int32_t)((size_t)s * TR + i);
   }
 }
 

@@ -113,6 +113,8 @@ typedef struct ep_plan_view {
                                      rows of rank 0 in grouped order, then
                                      rank 1, ...; slot id (s*T + t)*R + k;
                                      -1 after the last delivered row */
+    int32_t *send_slot; /* [N][T*R]  slot id (s*T + t)*R + k that send row p
+                                     of source s holds; -1 for p >= send_off[s][E] */
 } ep_plan_view;
 
 /* Worst-case receive rows N * T * max(R, E/N) ("Send and receive buffers");
@@ -151,7 +153,9 @@ EP_API int ep_plan_views(const ep_desc *d, void *plan_ws, ep_plan_view *v);
  *   comb_row        = d * cap + grp_pos;
  *   grp_slot[j]     = the slot whose row is the j-th delivered row when the
  *                     ranks' grouped layouts are concatenated in rank order
- *                     (each truncated to cap rows); -1 for j past the end.
+ *                     (each truncated to cap rows); -1 for j past the end;
+ *   send_slot[s][p] = the slot (s*T + t)*R + k with send_pos[s][t][k] = p
+ *                     (the inverse of send_pos); -1 for p >= send_off[s][E].
  * Slots with an id outside [0, E) get -1 and set EP_STATUS_BAD_EXPERT; rows
  * with grp_pos >= cap get -1 and set EP_STATUS_CAPACITY. status: device
  * int32, bits OR-ed in. Deterministic: equal inputs give equal bytes. */
@@ -162,8 +166,9 @@ EP_API int ep_plan(const ep_desc *d, const int32_t *topk_idx, void *plan_ws,
  * send buffer so that each peer takes one bulk write). For each plane p:
  * x[p] is [N][T][row_p], send[p] is [N][T*R][row_p];
  * send[p][s][send_pos[s][t][k]] = x[p][s][t] byte for byte. Each token row
- * is read once and written R times. Slots with send_pos = -1 are skipped.
- * plane 1 pointers must be NULL for bf16. */
+ * is written R times. Slots with send_pos = -1 are skipped, and send rows
+ * past send_off[s][E] are left untouched. plane 1 pointers must be NULL for
+ * bf16. */
 EP_API int ep_dispatch_pack(const ep_desc *d, const void *const x[2],
                      const void *plan_ws, void *const send[2],
                      hipStream_t stream);

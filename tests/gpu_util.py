@@ -10,7 +10,7 @@ import combine_ep_plan_amd as ep
 import ep_workloads as W
 
 PLAN_FIELDS = ("cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos",
-               "src_off", "comb_row", "grp_slot")
+               "src_off", "comb_row", "grp_slot", "send_slot")
 
 
 def note(msg: str) -> None:
@@ -53,7 +53,8 @@ def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
     L = E // N
     shapes = {"cnt": (N, E), "send_off": (N, E + 1), "send_pos": (N, T, R),
               "recv_off": (N, N + 1), "grp_off": (N, L + 1), "grp_pos": (N, T, R),
-              "src_off": (N, E), "comb_row": (N, T, R), "grp_slot": (N * T * R,)}
+              "src_off": (N, E), "comb_row": (N, T, R), "grp_slot": (N * T * R,),
+              "send_slot": (N, T * R)}
     v = ep.plan_views(d, b.plan_ws)
     base = b.plan_ws.data_ptr()
     ws = b.plan_ws.cpu().numpy()
@@ -66,8 +67,8 @@ def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
 
 
 def expected_plan_extras(p: dict, idx: np.ndarray, N: int, E: int, cap: int) -> dict:
-    """src_off, comb_row and grp_slot from the oracle's cnt and grp_pos,
-    by their definitions."""
+    """src_off, comb_row, grp_slot and send_slot from the oracle's cnt,
+    grp_pos and send_pos, by their definitions."""
     L = E // N
     cnt = p["cnt"].astype(np.int64)
     src_off = np.vstack([np.zeros((1, E), np.int64), np.cumsum(cnt, axis=0)[:-1]])
@@ -80,8 +81,15 @@ def expected_plan_extras(p: dict, idx: np.ndarray, N: int, E: int, cap: int) -> 
     dd = (idx.reshape(-1) // L)
     ok = gp >= 0
     grp_slot[dstart[dd[ok]] + gp[ok]] = np.nonzero(ok)[0]
+    # send_slot: the inverse of send_pos per source, -1 past the filled rows
+    T, R = idx.shape[1], idx.shape[2]
+    send_slot = np.full((N, T * R), -1, np.int64)
+    sp = p["send_pos"].reshape(N, T * R)
+    for s in range(N):
+        have = sp[s] >= 0
+        send_slot[s, sp[s][have]] = s * T * R + np.nonzero(have)[0]
     return {"src_off": src_off.astype(np.int32), "comb_row": comb.astype(np.int32),
-            "grp_slot": grp_slot.astype(np.int32)}
+            "grp_slot": grp_slot.astype(np.int32), "send_slot": send_slot.astype(np.int32)}
 
 
 def bf16_close(got: np.ndarray, want: np.ndarray, rel: float = 8e-3) -> np.ndarray:

@@ -111,8 +111,8 @@ def test_plan_views_layout():
     v = ep.plan_views(d, base)
     N, E, L, NTR = 8, 256, 32, 8 * 4096 * 8
     names = ["cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos", "src_off",
-             "comb_row", "grp_slot"]
-    sizes = [N * E, N * (E + 1), NTR, N * (N + 1), N * (L + 1), NTR, N * E, NTR, NTR]
+             "comb_row", "grp_slot", "send_slot"]
+    sizes = [N * E, N * (E + 1), NTR, N * (N + 1), N * (L + 1), NTR, N * E, NTR, NTR, NTR]
     ptrs = [getattr(v, n) for n in names]
     assert ptrs[0] == base
     for p, q, n in zip(ptrs, ptrs[1:], sizes):
