@@ -82,7 +82,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
   source_sums<kPlanThreads>(p.chunk_cnt, s, c, E, nchunks, soff, pre);
   __syncthreads();
   send_tables<kPlanThreads>(e_of, rank_of, s, c, E, TR, p, soff, pre, scratch, within_of);
-  receive_tables<kPlanThreads>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, sro, sros, gsc,
+  receive_tables<kPlanThreads>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, soff, sro,
+                               sros, gsc,
                                dstart, scratch, (int64_t)blockIdx.y * gridDim.x + blockIdx.x,
                                (int64_t)gridDim.x * gridDim.y);
 }
@@ -168,7 +169,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   for (int e = tid; e < E; e += kPlanThreads) sros[e] = sro[e];
   __syncthreads();
   send_tables<kPlanThreads>(e_of, rank_of, s, c, E, TR, p, soff, pre, scratch, within_of);
-  receive_tables<kPlanThreads>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, sro, sros, gsc,
+  receive_tables<kPlanThreads>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, soff, sro,
+                               sros, gsc,
                                dstart, scratch, (int64_t)blockIdx.y * gridDim.x + blockIdx.x,
                                (int64_t)gridDim.x * gridDim.y);
 }

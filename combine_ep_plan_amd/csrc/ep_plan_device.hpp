@@ -175,14 +175,15 @@ __device__ __forceinline__ void column_sums(Count count, int N, int E, int s, in
 // column_sums. within_of[sub] is the slot's index among the rows that s
 // sends to its expert (negative: dropped slot). Writes src_off[s] and
 // recv_off[.][s] (block c == 0), grp_off, the receive totals and the
-// capacity flag (block (0, 0)), and grp_pos, comb_row and grp_slot of the
-// block's slots; then clears the receive-order entries past the last
-// delivered row (shared by all blocks).
+// capacity flag (block (0, 0)), and grp_pos, comb_row, grp_slot and
+// recv_rows of the block's slots; then clears the receive-order entries
+// past the last delivered row (shared by all blocks). so: send_off[s].
 template <int TPB>
 __device__ void receive_tables(const int* e_of, const int* within_of, int s, int c, int N, int E,
                                int L, int64_t TR, int64_t cap, const PlanPtrs& p,
-                               int32_t* status, int32_t* sro, int32_t* sros, int32_t* gsc,
-                               int32_t* dstart, int32_t* scratch, int64_t bl, int64_t nblocks) {
+                               int32_t* status, const int32_t* so, int32_t* sro, int32_t* sros,
+                               int32_t* gsc, int32_t* dstart, int32_t* scratch, int64_t bl,
+                               int64_t nblocks) {
   const int tid = threadIdx.x;
   if (c == 0)
     for (int e = tid; e < E; e += TPB) p.src_off[(size_t)s * E + e] = sro[e];
@@ -231,14 +232,18 @@ __device__ void receive_tables(const int* e_of, const int* within_of, int s, int
       p.grp_pos[gi] = (int32_t)g;
       p.comb_row[gi] = (int32_t)((int64_t)d * cap + g);
       p.grp_slot[dstart[d] + g] = (int32_t)gi;
+      ((int2*)p.recv_rows)[dstart[d] + g] =
+          make_int2((int32_t)((int64_t)s * TR + so[e] + within), (int32_t)((int64_t)d * cap + g));
     } else {
       p.grp_pos[gi] = -1;
       p.comb_row[gi] = -1;
     }
   }
   for (int64_t j = dstart[N] + bl * TPB + tid; j < (int64_t)N * TR;
-       j += nblocks * TPB)
+       j += nblocks * TPB) {
     p.grp_slot[j] = -1;
+    ((int2*)p.recv_rows)[j] = make_int2(-1, -1);
+  }
 }
 
 // Per-source sums of the chunk counts: soff[e] = rows of s to e, pre[e] =
@@ -330,7 +335,7 @@ __device__ void exchange_block(int s, int c, int64_t bl, int64_t nblocks, int N,
     e_of[sub] = lo;
     within_of[sub] = pos - so[lo];
   }
-  receive_tables<TPB>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, sro, sros, gsc, dstart,
+  receive_tables<TPB>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, so, sro, sros, gsc, dstart,
                       scratch, bl, nblocks);
 }
 

@@ -115,6 +115,11 @@ typedef struct ep_plan_view {
                                      -1 after the last delivered row */
     int32_t *send_slot; /* [N][T*R]  slot id (s*T + t)*R + k that send row p
                                      of source s holds; -1 for p >= send_off[s][E] */
+    int32_t *recv_rows; /* [N*T*R][2] receive order as row pairs: for the
+                                     j-th delivered row (order of grp_slot),
+                                     its send row s*T*R + send_pos and its
+                                     grouped row d*cap + grp_pos; -1, -1 past
+                                     the last delivered row */
 } ep_plan_view;
 
 /* Worst-case receive rows N * T * max(R, E/N) ("Send and receive buffers");
@@ -155,7 +160,8 @@ EP_API int ep_plan_views(const ep_desc *d, void *plan_ws, ep_plan_view *v);
  *                     ranks' grouped layouts are concatenated in rank order
  *                     (each truncated to cap rows); -1 for j past the end;
  *   send_slot[s][p] = the slot (s*T + t)*R + k with send_pos[s][t][k] = p
- *                     (the inverse of send_pos); -1 for p >= send_off[s][E].
+ *                     (the inverse of send_pos); -1 for p >= send_off[s][E];
+ *   recv_rows[j]    = (s*T*R + send_pos, comb_row) of the slot grp_slot[j].
  * Slots with an id outside [0, E) get -1 and set EP_STATUS_BAD_EXPERT; rows
  * with grp_pos >= cap get -1 and set EP_STATUS_CAPACITY. status: device
  * int32, bits OR-ed in. Deterministic: equal inputs give equal bytes. */
