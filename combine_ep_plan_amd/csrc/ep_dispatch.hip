@@ -9,14 +9,19 @@
 // into the peers let a rank pull tokens directly.
 //
 // Rows move as opaque bytes; lane l of a wave moves 16-byte chunks l, l+64,
-// ... and all chunks a wave holds are loaded before the first store. The
-// receivers, the transfer and the unpack give one wave each 448-chunk (7 KB)
-// segment of a row (a 14 KB bf16 row at H = 7168 is two waves): measured on
-// gfx950, a plain copy runs at 6.4 TB/s with 7 KB per wave against 5.8 TB/s
-// with 14 KB per wave (more waves resident at fewer registers each). The
-// senders give one wave a token pair instead (store-heavy: each row is
-// written R times). Row indices are wave-uniform and live in scalar
-// registers.
+// ... and all chunks a wave holds are loaded before the first store. Row
+// indices are wave-uniform and live in scalar registers. Two shapes:
+//   - 1 KB pieces in output order (the sender in send order and the
+//     receiver in receive order): consecutive waves write consecutive 1 KB
+//     pieces, so the stores advance through memory as one front; measured
+//     on gfx950 this beats whole rows per wave for store-heavy copies (a
+//     fill writes 6.8 TB/s with 1 KB per wave against 5.3 TB/s with 14 KB).
+//     Each wave needs one table load to find its rows.
+//   - 7 KB row segments (the split receiver, the per-pair transfer and the
+//     unpack): one wave per 448-chunk segment (a 14 KB bf16 row at H = 7168
+//     is two waves), 6.4 TB/s for a plain copy against 5.8 TB/s with 14 KB
+//     per wave. The token-order sender (large sources, and the split
+//     sender) gives one wave a token pair and writes each row R times.
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 #include "ep_plan_device.hpp"
@@ -304,10 +309,12 @@ __device__ __forceinline__ void gather_wave(const GatherArgs& a, const MovePlane
 // rest of them idle, so xblocks, a multiple of 8, keeps the XCD of every
 // later block equal to its index mod 8); then the blocks of plane 0, then of
 // plane 1, each range renumbered per XCD.
+// At most 64 VGPRs (8 waves per SIMD): the exchange code would otherwise
+// set the register count, and so the occupancy, of every sender wave.
 template <bool EXCHANGE>
-__global__ __launch_bounds__(kBlock) void pack_gather_kernel(GatherArgs a, PlanPtrs p, int N, int E,
-                                                             int L, int T, int R, int64_t cap,
-                                                             int xblocks, int32_t* status) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8))) void
+pack_gather_kernel(GatherArgs a, PlanPtrs p, int N, int E, int L, int T, int R, int64_t cap,
+                   int xblocks, int32_t* status) {
   extern __shared__ int32_t lds[];
   int b = blockIdx.x;
   if (EXCHANGE) {
@@ -336,8 +343,8 @@ __global__ __launch_bounds__(kBlock) void pack_gather_kernel(GatherArgs a, PlanP
 // lane one 16- or 4-byte unit, rows in receive order). Reads are
 // non-temporal: every send row is read once. Every row index is range
 // checked. Measured at decode scale: 152.8 us against 158.0 us for 7 KB row
-// segments per wave (recv_kernel, two levels of table loads); with fp8
-// rows 80.3 against 85.8 us.
+// segments per wave (two levels of table loads: grp_slot, then send_pos and
+// comb_row); with fp8 rows 80.3 against 85.8 us.
 struct RecvArgs {
   MovePlane pl[2];
   const int2* recv_rows;
@@ -472,7 +479,8 @@ __global__ __launch_bounds__(kBlock) void pack_split_kernel(Planes pl, Split sp,
   }
 }
 
-// Receiver half of a split dispatch: recv_kernel, reading each row from
+// Receiver half of a split dispatch: a row-segment receiver in receive order
+// (grp_slot), reading each row from
 // the private region or the send buffer, wherever the sender put it.
 __global__ __launch_bounds__(kBlock) void recv_split_kernel(Planes pl, Split sp,
                                                             const int32_t* __restrict__ grp_slot,
@@ -495,35 +503,6 @@ __global__ __launch_bounds__(kBlock) void recv_split_kernel(Planes pl, Split sp,
     const int64_t row = pl.row[q];
     wave_copy_segment(split_row(sp, q, (uint8_t*)pl.src[q], s, d, p, TR, (size_t)row),
                       pl.dst[q] + (size_t)g * row, row, seg);
-  }
-}
-
-// Receiver with the transfer fused in: wave j pulls the j-th row of the
-// receive order (grp_slot: each rank's grouped rows in turn) from its
-// source's send buffer into the grouped layout on its expert's rank
-// (comb_row = rank * cap + grouped position). Visiting rows in receive
-// order makes every rank's grouped buffer a sequential write stream (the
-// pulls from the send buffers are the scattered side, which costs less).
-// Every row index is range checked, so no plan content can make the kernel
-// leave its buffers.
-__global__ __launch_bounds__(kBlock) void recv_kernel(Planes pl, const int32_t* __restrict__ grp_slot,
-                                                      const int32_t* __restrict__ send_pos,
-                                                      const int32_t* __restrict__ comb_row,
-                                                      int NTR, int TR, int64_t rows_out, int wps) {
-  const int w = wave_index();
-  const int j = w / wps;
-  const int seg = w % wps;
-  if (j >= NTR) return;
-  const int slot = grp_slot[j];
-  if (slot < 0 || slot >= NTR) return;
-  const int p = send_pos[slot];
-  const int g = comb_row[slot];
-  if (p < 0 || p >= TR || g < 0 || g >= rows_out) return;
-  const int s = slot / TR;
-  for (int q = 0; q < pl.planes; ++q) {
-    const int64_t row = pl.row[q];
-    wave_copy_segment(pl.src[q] + ((size_t)s * TR + p) * row, pl.dst[q] + (size_t)g * row, row,
-                      seg);
   }
 }
 
@@ -698,10 +677,6 @@ hipError_t launch_pack_exchange_v(const Dims& d, const void* const x[2], const P
   return hipGetLastError();
 }
 
-// The receiver moves 1 KB pieces in receive order (recv_rows_kernel)
-// rather than 7 KB row segments (recv_kernel).
-constexpr bool kRecvPieces = true;
-
 // The send-order sender re-reads each token row R times and relies on an
 // XCD's 4 MB L2 holding the rows of the source it works on: used when one
 // source's token rows (all planes) take at most this many bytes. Measured
@@ -765,20 +740,13 @@ hipError_t launch_pack_gather(const Dims& d, const void* const x[2], const PlanP
 hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs& p,
                        void* const grouped[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
-  if (kRecvPieces) {
-    RecvArgs a{};
-    for (int q = 0; q < d.planes; ++q) a.pl[q] = move_plane(send[q], grouped[q], d.row[q], d.NTR);
-    a.recv_rows = (const int2*)p.recv_rows;
-    a.NTR = (int)d.NTR;
-    a.rows_out = (int64_t)d.N * d.cap;
-    hipLaunchKernelGGL(recv_rows_kernel, dim3((unsigned)(a.pl[0].blocks + a.pl[1].blocks)),
-                       dim3(kBlock), 0, stream, a);
-    return hipGetLastError();
-  }
-  const int wps = waves_per_row(d);
-  hipLaunchKernelGGL(recv_kernel, dim3(blocks_for(d.NTR * wps)), dim3(kBlock), 0, stream,
-                     make_planes(d, send, grouped), p.grp_slot, p.send_pos, p.comb_row,
-                     (int)d.NTR, (int)d.TR, (int64_t)d.N * d.cap, wps);
+  RecvArgs a{};
+  for (int q = 0; q < d.planes; ++q) a.pl[q] = move_plane(send[q], grouped[q], d.row[q], d.NTR);
+  a.recv_rows = (const int2*)p.recv_rows;
+  a.NTR = (int)d.NTR;
+  a.rows_out = (int64_t)d.N * d.cap;
+  hipLaunchKernelGGL(recv_rows_kernel, dim3((unsigned)(a.pl[0].blocks + a.pl[1].blocks)),
+                     dim3(kBlock), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -171,19 +171,17 @@ __device__ __forceinline__ void column_sums(Count count, int N, int E, int s, in
   __syncthreads();
 }
 
-// Receive side of the plan for the slots of block (c, s), from the sums of
-// column_sums. within_of[sub] is the slot's index among the rows that s
-// sends to its expert (negative: dropped slot). Writes src_off[s] and
-// recv_off[.][s] (block c == 0), grp_off, the receive totals and the
-// capacity flag (block (0, 0)), and grp_pos, comb_row, grp_slot and
-// recv_rows of the block's slots; then clears the receive-order entries
-// past the last delivered row (shared by all blocks). so: send_off[s].
+// Receive side of the plan for source s, in three parts, from the sums of
+// column_sums (sro, sros, gsc).
+//
+// receive_prefix: src_off[s] and recv_off[.][s] (chunk c == 0), grp_off,
+// the receive totals and the capacity flag (block (0, 0)). On return
+// (synced) gsc[e] = rows all sources send to experts before e, sro[e] = rows
+// sources before s send to e, dstart[d] = first receive-order row of rank d.
 template <int TPB>
-__device__ void receive_tables(const int* e_of, const int* within_of, int s, int c, int N, int E,
-                               int L, int64_t TR, int64_t cap, const PlanPtrs& p,
-                               int32_t* status, const int32_t* so, int32_t* sro, int32_t* sros,
-                               int32_t* gsc, int32_t* dstart, int32_t* scratch, int64_t bl,
-                               int64_t nblocks) {
+__device__ void receive_prefix(int s, int c, int N, int E, int L, int64_t cap, const PlanPtrs& p,
+                               int32_t* status, int32_t* sro, int32_t* sros, int32_t* gsc,
+                               int32_t* dstart, int32_t* scratch) {
   const int tid = threadIdx.x;
   if (c == 0)
     for (int e = tid; e < E; e += TPB) p.src_off[(size_t)s * E + e] = sro[e];
@@ -213,37 +211,62 @@ __device__ void receive_tables(const int* e_of, const int* within_of, int s, int
       }
     }
   }
+}
 
-#pragma unroll
-  for (int sub = 0; sub < (kPlanChunk / TPB); ++sub) {
-    const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * TPB + tid;
-    if (i >= TR) break;
-    const size_t gi = (size_t)s * TR + i;
-    const int e = e_of[sub];
-    const int within = within_of[sub];
-    if (e < 0 || e >= E || within < 0) {
-      p.grp_pos[gi] = -1;
-      p.comb_row[gi] = -1;
-      continue;
-    }
-    const int d = e / L;
-    const int64_t g = (int64_t)(gsc[e] - gsc[d * L]) + sro[e] + within;
-    if (g < cap) {
-      p.grp_pos[gi] = (int32_t)g;
-      p.comb_row[gi] = (int32_t)((int64_t)d * cap + g);
-      p.grp_slot[dstart[d] + g] = (int32_t)gi;
-      ((int2*)p.recv_rows)[dstart[d] + g] =
-          make_int2((int32_t)((int64_t)s * TR + so[e] + within), (int32_t)((int64_t)d * cap + g));
-    } else {
-      p.grp_pos[gi] = -1;
-      p.comb_row[gi] = -1;
-    }
+// receive_slot: grp_pos, comb_row, grp_slot and recv_rows of slot i of s,
+// whose expert is e and which is the within-th row s sends to e (e outside
+// [0, E) or within < 0: a dropped slot). so: send_off[s].
+__device__ __forceinline__ void receive_slot(int64_t i, int e, int within, int s, int E, int L,
+                                             int64_t TR, int64_t cap, const PlanPtrs& p,
+                                             const int32_t* so, const int32_t* sro,
+                                             const int32_t* gsc, const int32_t* dstart) {
+  const size_t gi = (size_t)s * TR + i;
+  if (e < 0 || e >= E || within < 0) {
+    p.grp_pos[gi] = -1;
+    p.comb_row[gi] = -1;
+    return;
   }
-  for (int64_t j = dstart[N] + bl * TPB + tid; j < (int64_t)N * TR;
-       j += nblocks * TPB) {
+  const int d = e / L;
+  const int64_t g = (int64_t)(gsc[e] - gsc[d * L]) + sro[e] + within;
+  if (g < cap) {
+    p.grp_pos[gi] = (int32_t)g;
+    p.comb_row[gi] = (int32_t)((int64_t)d * cap + g);
+    p.grp_slot[dstart[d] + g] = (int32_t)gi;
+    ((int2*)p.recv_rows)[dstart[d] + g] =
+        make_int2((int32_t)((int64_t)s * TR + so[e] + within), (int32_t)((int64_t)d * cap + g));
+  } else {
+    p.grp_pos[gi] = -1;
+    p.comb_row[gi] = -1;
+  }
+}
+
+// receive_clear: the receive-order entries past the last delivered row,
+// shared by all nblocks blocks doing this work (this one is bl).
+template <int TPB>
+__device__ __forceinline__ void receive_clear(int N, int64_t TR, const PlanPtrs& p,
+                                              const int32_t* dstart, int64_t bl, int64_t nblocks) {
+  for (int64_t j = dstart[N] + bl * TPB + threadIdx.x; j < (int64_t)N * TR; j += nblocks * TPB) {
     p.grp_slot[j] = -1;
     ((int2*)p.recv_rows)[j] = make_int2(-1, -1);
   }
+}
+
+// All three for the slots of block (c, s), whose experts and within-expert
+// indices the caller holds (within_of[sub] < 0: dropped slot).
+template <int TPB>
+__device__ void receive_tables(const int* e_of, const int* within_of, int s, int c, int N, int E,
+                               int L, int64_t TR, int64_t cap, const PlanPtrs& p,
+                               int32_t* status, const int32_t* so, int32_t* sro, int32_t* sros,
+                               int32_t* gsc, int32_t* dstart, int32_t* scratch, int64_t bl,
+                               int64_t nblocks) {
+  receive_prefix<TPB>(s, c, N, E, L, cap, p, status, sro, sros, gsc, dstart, scratch);
+#pragma unroll
+  for (int sub = 0; sub < (kPlanChunk / TPB); ++sub) {
+    const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * TPB + threadIdx.x;
+    if (i >= TR) break;
+    receive_slot(i, e_of[sub], within_of[sub], s, E, L, TR, cap, p, so, sro, gsc, dstart);
+  }
+  receive_clear<TPB>(N, TR, p, dstart, bl, nblocks);
 }
 
 // Per-source sums of the chunk counts: soff[e] = rows of s to e, pre[e] =
@@ -315,28 +338,40 @@ __device__ void exchange_block(int s, int c, int64_t bl, int64_t nblocks, int N,
   int32_t* dstart = gsc + (E + 1);   // [N+1]
   int32_t* scratch = dstart + (N + 1);
   const int tid = threadIdx.x;
-  int e_of[(kPlanChunk / TPB)], pos_of[(kPlanChunk / TPB)], within_of[(kPlanChunk / TPB)];
-  fetch_slots<TPB>(nullptr, p.send_pos, s, c, TR, e_of, pos_of);
+  // The slots' send positions first, so that their latency overlaps the
+  // exchange; only the positions are held across it (the expert and the
+  // within-expert index are derived afterwards, which keeps the register
+  // count low for the sender launches this block shares).
+  int pos_of[kPlanChunk / TPB];
+#pragma unroll
+  for (int sub = 0; sub < (kPlanChunk / TPB); ++sub) {
+    const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * TPB + tid;
+    pos_of[sub] = i < TR ? p.send_pos[(size_t)s * TR + i] : -1;
+  }
   for (int e = tid; e <= E; e += TPB) so[e] = p.send_off[(size_t)s * (E + 1) + e];
   const int32_t* cnt = p.cnt;
   column_sums<TPB>([=](int s2, int e) { return cnt[(size_t)s2 * E + e]; }, N, E, s, sro, sros, gsc,
               scratch + TPB / kWave);
+  receive_prefix<TPB>(s, c, N, E, L, cap, p, status, sro, sros, gsc, dstart, scratch);
+  // The expert of a slot is the segment of send_off[s] its position falls in.
 #pragma unroll
   for (int sub = 0; sub < (kPlanChunk / TPB); ++sub) {
+    const int64_t i = (int64_t)c * kPlanChunk + (int64_t)sub * TPB + tid;
+    if (i >= TR) break;
     const int pos = pos_of[sub];
-    e_of[sub] = -1;
-    within_of[sub] = -1;
-    if (pos < 0 || pos >= so[E]) continue;
-    int lo = 0, hi = E - 1;  // largest e with so[e] <= pos
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (so[mid] <= pos) lo = mid; else hi = mid - 1;
+    int e = -1, within = -1;
+    if (pos >= 0 && pos < so[E]) {
+      int lo = 0, hi = E - 1;  // largest e with so[e] <= pos
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (so[mid] <= pos) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+      within = pos - so[lo];
     }
-    e_of[sub] = lo;
-    within_of[sub] = pos - so[lo];
+    receive_slot(i, e, within, s, E, L, TR, cap, p, so, sro, gsc, dstart);
   }
-  receive_tables<TPB>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, so, sro, sros, gsc, dstart,
-                      scratch, bl, nblocks);
+  receive_clear<TPB>(N, TR, p, dstart, bl, nblocks);
 }
 
 }  // namespace
