@@ -91,12 +91,12 @@ int derive(const ep_desc* d, ep::Dims* o) {
 
 // Plan workspace: int32 arrays, each starting on a 256-byte boundary.
 struct Layout {
-  size_t off[12];
+  size_t off[13];
   size_t bytes;
 };
 
 Layout layout_of(const ep::Dims& d) {
-  const size_t n[12] = {
+  const size_t n[13] = {
       (size_t)d.N * d.E,                       // cnt
       (size_t)d.N * (d.E + 1),                 // send_off
       (size_t)d.NTR,                           // send_pos
@@ -109,10 +109,11 @@ Layout layout_of(const ep::Dims& d) {
       (size_t)d.N * d.nchunks * d.E,           // chunk_cnt
       (size_t)d.NTR,                           // send_slot
       (size_t)2 * d.NTR,                       // recv_rows
+      (size_t)d.NTR,                           // send_seg
   };
   Layout l{};
   size_t at = 0;
-  for (int i = 0; i < 12; ++i) {
+  for (int i = 0; i < 13; ++i) {
     l.off[i] = at;
     at += (n[i] * sizeof(int32_t) + 255) & ~(size_t)255;
   }
@@ -136,6 +137,7 @@ ep::PlanPtrs plan_ptrs(const ep::Dims& d, const void* ws) {
   p.chunk_cnt = (int32_t*)(b + l.off[9]);
   p.send_slot = (int32_t*)(b + l.off[10]);
   p.recv_rows = (int32_t*)(b + l.off[11]);
+  p.send_seg = (int32_t*)(b + l.off[12]);
   return p;
 }
 
@@ -277,6 +279,7 @@ int ep_plan_views(const ep_desc* d, void* plan_ws, ep_plan_view* v) {
   v->grp_slot = p.grp_slot;
   v->send_slot = p.send_slot;
   v->recv_rows = p.recv_rows;
+  v->send_seg = p.send_seg;
   return EP_OK;
 }
 

@@ -269,14 +269,40 @@ struct MovePlane {
   int blocks;   // blocks covering it, a multiple of 8
 };
 
+// Private regions of a split dispatch: send row p of s that is row i < P of
+// the segment s -> d (send_seg[s][p] = d T R + i) lives in d's region for s,
+// priv[q][((d N + s) P + i) row], instead of the send buffer.
+struct PrivRegions {
+  uint8_t* priv[2];
+  const int32_t* send_seg;
+  FastDiv tr_div;
+  int TR, N, P;
+};
+
+// Row `g` (s T R + p) of plane q: in the private region when it is among the
+// first P rows of its segment, else `fallback` (its send-buffer row). An out
+// of range send_seg entry keeps the fallback.
+__device__ __forceinline__ uint8_t* split_dst(const PrivRegions& v, int q, int g, size_t row,
+                                              uint8_t* fallback) {
+  const int seg = v.send_seg[g];
+  const int d = fast_div(seg, v.tr_div);
+  const int i = seg - d * v.TR;
+  if (seg < 0 || d >= v.N || i >= v.P) return fallback;
+  const int s = fast_div(g, v.tr_div);
+  return v.priv[q] + (((size_t)d * v.N + s) * v.P + i) * row;
+}
+
 struct GatherArgs {
   MovePlane pl[2];
   const int32_t* send_slot;
   FastDiv r_div;
   int NT, NTR;
+  PrivRegions split;
 };
 
-__device__ __forceinline__ void gather_wave(const GatherArgs& a, const MovePlane& pl, int w) {
+template <bool SPLIT>
+__device__ __forceinline__ void gather_wave(const GatherArgs& a, const MovePlane& pl, int q,
+                                            int w) {
   if (pl.pieces) {
     const int g = wave_uniform(fast_div(w, pl.per_row_div));  // send row
     const int base = (w - g * pl.per_row) * kWave;
@@ -285,9 +311,11 @@ __device__ __forceinline__ void gather_wave(const GatherArgs& a, const MovePlane
     const int tok = fast_div(slot, a.r_div);
     if (tok >= a.NT) return;
     const size_t row = (size_t)pl.n16 * 16;
+    uint8_t* dst = pl.dst + (size_t)g * row;
+    if (SPLIT) dst = split_dst(a.split, q, g, row, dst);
     RowRegs<1> r;
     load_row16<1, false>(r, (const u32x4*)(pl.src + (size_t)tok * row), base, pl.n16);
-    store_row16(r, (u32x4*)(pl.dst + (size_t)g * row), base, pl.n16);
+    store_row16(r, (u32x4*)dst, base, pl.n16);
     return;
   }
   const int64_t c = (int64_t)w * kWave + lane_id();
@@ -299,10 +327,12 @@ __device__ __forceinline__ void gather_wave(const GatherArgs& a, const MovePlane
   const int tok = fast_div(slot, a.r_div);
   if (tok >= a.NT) return;
   const size_t src = (size_t)tok * pl.per_row + u;
+  uint8_t* dst = pl.dst + (size_t)g * pl.per_row * pl.unit;
+  if (SPLIT) dst = split_dst(a.split, q, g, (size_t)pl.per_row * pl.unit, dst);
   if (pl.unit == 16)
-    store_stream((u32x4*)pl.dst + c, ((const u32x4*)pl.src)[src]);
+    store_stream((u32x4*)dst + u, ((const u32x4*)pl.src)[src]);
   else
-    __builtin_nontemporal_store(((const uint32_t*)pl.src)[src], (uint32_t*)pl.dst + c);
+    __builtin_nontemporal_store(((const uint32_t*)pl.src)[src], (uint32_t*)dst + u);
 }
 
 // Blocks [0, xblocks) do the count exchange when EXCHANGE (blocks < N; the
@@ -311,7 +341,7 @@ __device__ __forceinline__ void gather_wave(const GatherArgs& a, const MovePlane
 // plane 1, each range renumbered per XCD.
 // At most 64 VGPRs (8 waves per SIMD): the exchange code would otherwise
 // set the register count, and so the occupancy, of every sender wave.
-template <bool EXCHANGE>
+template <bool EXCHANGE, bool SPLIT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8))) void
 pack_gather_kernel(GatherArgs a, PlanPtrs p, int N, int E, int L, int T, int R, int64_t cap,
                    int xblocks, int32_t* status) {
@@ -326,12 +356,12 @@ pack_gather_kernel(GatherArgs a, PlanPtrs p, int N, int E, int L, int T, int R, 
   }
   if (b < a.pl[0].blocks) {
     const int w = xcd_block(b, a.pl[0].blocks) * kWavesPerBlock + (int)threadIdx.x / kWave;
-    if (w < a.pl[0].waves) gather_wave(a, a.pl[0], w);
+    if (w < a.pl[0].waves) gather_wave<SPLIT>(a, a.pl[0], 0, w);
   } else {
     b -= a.pl[0].blocks;
     if (b >= a.pl[1].blocks) return;
     const int w = xcd_block(b, a.pl[1].blocks) * kWavesPerBlock + (int)threadIdx.x / kWave;
-    if (w < a.pl[1].waves) gather_wave(a, a.pl[1], w);
+    if (w < a.pl[1].waves) gather_wave<SPLIT>(a, a.pl[1], 1, w);
   }
 }
 
@@ -350,9 +380,11 @@ struct RecvArgs {
   const int2* recv_rows;
   int NTR;
   int64_t rows_out;
+  PrivRegions split;  // SPLIT: rows a sender left in the private regions
 };
 
-__device__ __forceinline__ void recv_wave(const RecvArgs& a, const MovePlane& pl, int w) {
+template <bool SPLIT>
+__device__ __forceinline__ void recv_wave(const RecvArgs& a, const MovePlane& pl, int q, int w) {
   if (pl.pieces) {
     const int j = wave_uniform(fast_div(w, pl.per_row_div));
     const int base = (w - j * pl.per_row) * kWave;
@@ -360,8 +392,10 @@ __device__ __forceinline__ void recv_wave(const RecvArgs& a, const MovePlane& pl
     const int src = wave_uniform(r.x), dst = wave_uniform(r.y);
     if (src < 0 || src >= a.NTR || dst < 0 || dst >= a.rows_out) return;
     const size_t row = (size_t)pl.n16 * 16;
+    const uint8_t* from = pl.src + (size_t)src * row;
+    if (SPLIT) from = split_dst(a.split, q, src, row, (uint8_t*)from);
     RowRegs<1> v;
-    load_row16<1, true>(v, (const u32x4*)(pl.src + (size_t)src * row), base, pl.n16);
+    load_row16<1, true>(v, (const u32x4*)from, base, pl.n16);
     store_row16(v, (u32x4*)(pl.dst + (size_t)dst * row), base, pl.n16);
     return;
   }
@@ -371,21 +405,25 @@ __device__ __forceinline__ void recv_wave(const RecvArgs& a, const MovePlane& pl
   const int u = (int)(c - (int64_t)j * pl.per_row);
   const int2 r = a.recv_rows[j];
   if (r.x < 0 || r.x >= a.NTR || r.y < 0 || r.y >= a.rows_out) return;
-  const size_t from = (size_t)r.x * pl.per_row + u, to = (size_t)r.y * pl.per_row + u;
+  const size_t row = (size_t)pl.per_row * pl.unit;
+  const uint8_t* from = pl.src + (size_t)r.x * row;
+  if (SPLIT) from = split_dst(a.split, q, r.x, row, (uint8_t*)from);
+  uint8_t* to = pl.dst + (size_t)r.y * row;
   if (pl.unit == 16)
-    store_stream((u32x4*)pl.dst + to, load_stream((const u32x4*)pl.src + from));
+    store_stream((u32x4*)to + u, load_stream((const u32x4*)from + u));
   else
-    __builtin_nontemporal_store(__builtin_nontemporal_load((const uint32_t*)pl.src + from),
-                                (uint32_t*)pl.dst + to);
+    __builtin_nontemporal_store(__builtin_nontemporal_load((const uint32_t*)from + u),
+                                (uint32_t*)to + u);
 }
 
 // Blocks of plane 0, then of plane 1.
+template <bool SPLIT>
 __global__ __launch_bounds__(kBlock) void recv_rows_kernel(RecvArgs a) {
   int b = blockIdx.x;
   const int q = b < a.pl[0].blocks ? 0 : 1;
   if (q) b -= a.pl[0].blocks;
   const int w = b * kWavesPerBlock + (int)threadIdx.x / kWave;
-  if (w < a.pl[q].waves) recv_wave(a, a.pl[q], w);
+  if (w < a.pl[q].waves) recv_wave<SPLIT>(a, a.pl[q], q, w);
 }
 
 // Chunks per lane for a single pass over a plane of `row` bytes: 14, 7 or 1;
@@ -479,32 +517,6 @@ __global__ __launch_bounds__(kBlock) void pack_split_kernel(Planes pl, Split sp,
   }
 }
 
-// Receiver half of a split dispatch: a row-segment receiver in receive order
-// (grp_slot), reading each row from
-// the private region or the send buffer, wherever the sender put it.
-__global__ __launch_bounds__(kBlock) void recv_split_kernel(Planes pl, Split sp,
-                                                            const int32_t* __restrict__ grp_slot,
-                                                            const int32_t* __restrict__ send_pos,
-                                                            const int32_t* __restrict__ comb_row,
-                                                            int NTR, int TR, int64_t cap,
-                                                            int wps) {
-  const int w = wave_index();
-  const int j = w / wps;
-  const int seg = w % wps;
-  if (j >= NTR) return;
-  const int slot = grp_slot[j];
-  if (slot < 0 || slot >= NTR) return;
-  const int p = send_pos[slot];
-  const int g = comb_row[slot];
-  if (p < 0 || p >= TR || g < 0 || g >= (int64_t)sp.N * cap) return;
-  const int s = slot / TR;
-  const int d = (int)(g / cap);
-  for (int q = 0; q < pl.planes; ++q) {
-    const int64_t row = pl.row[q];
-    wave_copy_segment(split_row(sp, q, (uint8_t*)pl.src[q], s, d, p, TR, (size_t)row),
-                      pl.dst[q] + (size_t)g * row, row, seg);
-  }
-}
 
 // The network write: send row i of source s lies in the segment of the rank
 // d with send_off[s][dL] <= i < send_off[s][(d+1)L] and lands in d's receive
@@ -615,7 +627,7 @@ int waves_per_row(const Dims& d) {
 
 hipError_t launch_pack_gather(const Dims& d, const void* const x[2], const PlanPtrs& p,
                               void* const send[2], bool exchange, int32_t* status,
-                              hipStream_t stream);
+                              hipStream_t stream, const PrivRegions* split = nullptr);
 bool gather_fits(const Dims& d);
 
 hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
@@ -718,8 +730,9 @@ MovePlane move_plane(const void* src, void* dst, int64_t row, int64_t NTR) {
 
 hipError_t launch_pack_gather(const Dims& d, const void* const x[2], const PlanPtrs& p,
                               void* const send[2], bool exchange, int32_t* status,
-                              hipStream_t stream) {
+                              hipStream_t stream, const PrivRegions* split) {
   GatherArgs a{};
+  if (split != nullptr) a.split = *split;
   for (int q = 0; q < d.planes; ++q) a.pl[q] = move_plane(x[q], send[q], d.row[q], d.NTR);
   a.send_slot = p.send_slot;
   a.r_div = fast_div_of((uint32_t)d.R);
@@ -728,26 +741,40 @@ hipError_t launch_pack_gather(const Dims& d, const void* const x[2], const PlanP
   const int xblocks = exchange ? (d.N + 7) / 8 * 8 : 0;
   const unsigned grid = (unsigned)(xblocks + a.pl[0].blocks + a.pl[1].blocks);
   const size_t lds = exchange ? lds_exchange_bytes(d, kBlock) : 0;
-  if (exchange)
-    hipLaunchKernelGGL(pack_gather_kernel<true>, dim3(grid), dim3(kBlock), lds, stream, a, p, d.N,
-                       d.E, d.L, d.T, d.R, d.cap, xblocks, status);
+  if (exchange && split == nullptr)
+    hipLaunchKernelGGL((pack_gather_kernel<true, false>), dim3(grid), dim3(kBlock), lds, stream, a,
+                       p, d.N, d.E, d.L, d.T, d.R, d.cap, xblocks, status);
+  else if (split == nullptr)
+    hipLaunchKernelGGL((pack_gather_kernel<false, false>), dim3(grid), dim3(kBlock), 0, stream, a,
+                       p, d.N, d.E, d.L, d.T, d.R, d.cap, 0, status);
   else
-    hipLaunchKernelGGL(pack_gather_kernel<false>, dim3(grid), dim3(kBlock), 0, stream, a, p, d.N,
-                       d.E, d.L, d.T, d.R, d.cap, 0, status);
+    hipLaunchKernelGGL((pack_gather_kernel<false, true>), dim3(grid), dim3(kBlock), 0, stream, a,
+                       p, d.N, d.E, d.L, d.T, d.R, d.cap, 0, status);
   return hipGetLastError();
 }
 
-hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs& p,
-                       void* const grouped[2], hipStream_t stream) {
+hipError_t launch_recv_rows(const Dims& d, const void* const send[2], const PlanPtrs& p,
+                            void* const grouped[2], const PrivRegions* split,
+                            hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
   RecvArgs a{};
   for (int q = 0; q < d.planes; ++q) a.pl[q] = move_plane(send[q], grouped[q], d.row[q], d.NTR);
   a.recv_rows = (const int2*)p.recv_rows;
   a.NTR = (int)d.NTR;
   a.rows_out = (int64_t)d.N * d.cap;
-  hipLaunchKernelGGL(recv_rows_kernel, dim3((unsigned)(a.pl[0].blocks + a.pl[1].blocks)),
-                     dim3(kBlock), 0, stream, a);
+  const dim3 grid((unsigned)(a.pl[0].blocks + a.pl[1].blocks));
+  if (split == nullptr) {
+    hipLaunchKernelGGL(recv_rows_kernel<false>, grid, dim3(kBlock), 0, stream, a);
+  } else {
+    a.split = *split;
+    hipLaunchKernelGGL(recv_rows_kernel<true>, grid, dim3(kBlock), 0, stream, a);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs& p,
+                       void* const grouped[2], hipStream_t stream) {
+  return launch_recv_rows(d, send, p, grouped, nullptr, stream);
 }
 
 hipError_t launch_dispatch(const Dims& d, const int32_t* idx, const void* const x[2],
@@ -792,11 +819,26 @@ Split make_split(const Dims& d, void* const priv[2], int P, const PlanPtrs& p) {
   return sp;
 }
 
+PrivRegions make_priv(const Dims& d, void* const priv[2], int P, const PlanPtrs& p) {
+  PrivRegions v{};
+  for (int q = 0; q < 2; ++q) v.priv[q] = (P > 0 && q < d.planes) ? (uint8_t*)priv[q] : nullptr;
+  v.send_seg = p.send_seg;
+  v.tr_div = fast_div_of((uint32_t)(d.TR > 0 ? d.TR : 1));
+  v.TR = (int)d.TR;
+  v.N = d.N;
+  v.P = P;
+  return v;
+}
+
 hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* const x[2],
                              const PlanPtrs& p, void* const send[2], void* const priv[2], int P,
                              hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
   if (P == 0) return launch_pack(d, x, p, send, stream);  // no private rows: the plain sender
+  if (gather_fits(d)) {
+    const PrivRegions v = make_priv(d, priv, P, p);
+    return launch_pack_gather(d, x, p, send, false, nullptr, stream, &v);
+  }
   hipLaunchKernelGGL(pack_split_kernel, dim3(blocks_for((d.NT + 1) / 2)), dim3(kBlock), 0, stream,
                      make_planes(d, x, send), make_split(d, priv, P, p), idx, p.send_pos,
                      (int)d.NT, d.T, d.R);
@@ -806,12 +848,8 @@ hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* cons
 hipError_t launch_recv_split(const Dims& d, const void* const send[2], void* const priv[2], int P,
                              const PlanPtrs& p, void* const grouped[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
-  if (P == 0) return launch_recv(d, send, p, grouped, stream);  // the plain receiver
-  const int wps = waves_per_row(d);
-  hipLaunchKernelGGL(recv_split_kernel, dim3(blocks_for(d.NTR * wps)), dim3(kBlock), 0, stream,
-                     make_planes(d, send, grouped), make_split(d, priv, P, p), p.grp_slot,
-                     p.send_pos, p.comb_row, (int)d.NTR, (int)d.TR, d.cap, wps);
-  return hipGetLastError();
+  const PrivRegions v = make_priv(d, priv, P, p);
+  return launch_recv_rows(d, send, p, grouped, P > 0 ? &v : nullptr, stream);
 }
 
 hipError_t launch_transfer(const Dims& d, const void* const send[2], const PlanPtrs& p,

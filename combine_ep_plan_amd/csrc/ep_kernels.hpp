@@ -25,7 +25,7 @@ struct Dims {
 // Plan workspace pointers (int32 arrays, see ep_plan_view).
 struct PlanPtrs {
   int32_t *cnt, *send_off, *send_pos, *recv_off, *grp_off, *grp_pos, *src_off,
-      *comb_row, *grp_slot, *chunk_cnt, *send_slot, *recv_rows;
+      *comb_row, *grp_slot, *chunk_cnt, *send_slot, *recv_rows, *send_seg;
 };
 
 constexpr int kPlanThreads = 1024;

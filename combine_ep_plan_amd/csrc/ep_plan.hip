@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
       N, E, s, sro, sros, gsc, scratch + kPlanThreads / kWave);
   source_sums<kPlanThreads>(p.chunk_cnt, s, c, E, nchunks, soff, pre);
   __syncthreads();
-  send_tables<kPlanThreads>(e_of, rank_of, s, c, E, TR, p, soff, pre, scratch, within_of);
+  send_tables<kPlanThreads>(e_of, rank_of, s, c, E, L, TR, p, soff, pre, scratch, within_of);
   receive_tables<kPlanThreads>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, soff, sro,
                                sros, gsc,
                                dstart, scratch, (int64_t)blockIdx.y * gridDim.x + blockIdx.x,
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_finalize_kernel(
 // Sender half of a split dispatch: the send side of the plan from the
 // source's own chunk counts only (no data of any other rank).
 __global__ __launch_bounds__(kPlanThreads) void plan_local_kernel(
-    const int32_t* __restrict__ idx, int E, int64_t TR, int nchunks, PlanPtrs p) {
+    const int32_t* __restrict__ idx, int E, int L, int64_t TR, int nchunks, PlanPtrs p) {
   extern __shared__ int32_t lds[];
   int32_t* soff = lds;               // [E+1]
   int32_t* pre = soff + (E + 1);     // [E]
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_local_kernel(
   fetch_slots<kPlanThreads>(idx, p.send_pos, s, c, TR, e_of, rank_of);
   source_sums<kPlanThreads>(p.chunk_cnt, s, c, E, nchunks, soff, pre);
   __syncthreads();
-  send_tables<kPlanThreads>(e_of, rank_of, s, c, E, TR, p, soff, pre, scratch, within_of);
+  send_tables<kPlanThreads>(e_of, rank_of, s, c, E, L, TR, p, soff, pre, scratch, within_of);
 }
 
 // Receiver half of a split dispatch: the exchange reads the counts every
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   __syncthreads();
   for (int e = tid; e < E; e += kPlanThreads) sros[e] = sro[e];
   __syncthreads();
-  send_tables<kPlanThreads>(e_of, rank_of, s, c, E, TR, p, soff, pre, scratch, within_of);
+  send_tables<kPlanThreads>(e_of, rank_of, s, c, E, L, TR, p, soff, pre, scratch, within_of);
   receive_tables<kPlanThreads>(e_of, within_of, s, c, N, E, L, TR, cap, p, status, soff, sro,
                                sros, gsc,
                                dstart, scratch, (int64_t)blockIdx.y * gridDim.x + blockIdx.x,
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
 // (T R <= kPlanChunk): ranks, counts and the scan together, so the send
 // offsets and final positions need no chunk-count round trip. Grid (1, N).
 __global__ __launch_bounds__(kPlanThreads) void plan_count_local_kernel(
-    const int32_t* __restrict__ idx, int E, int64_t TR, PlanPtrs p,
+    const int32_t* __restrict__ idx, int E, int L, int64_t TR, PlanPtrs p,
     int32_t* __restrict__ status) {
   extern __shared__ int32_t lds[];
   constexpr int kWaves = kPlanThreads / kWave;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_local_kernel(
     pre[e] = 0;
   }
   __syncthreads();
-  send_tables<kPlanThreads>(e_of, rank_of, s, 0, E, TR, p, soff, pre, scratch, within_of);
+  send_tables<kPlanThreads>(e_of, rank_of, s, 0, E, L, TR, p, soff, pre, scratch, within_of);
 }
 
 bool fused_plan_fits(const Dims& d) {
@@ -281,13 +281,13 @@ hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& 
   if (e != hipSuccess) return e;
   if (d.nchunks == 1) {
     hipLaunchKernelGGL(plan_count_local_kernel, dim3(1, d.N), dim3(kPlanThreads),
-                       lds_count_local_bytes(d), stream, idx, d.E, d.TR, p, status);
+                       lds_count_local_bytes(d), stream, idx, d.E, d.L, d.TR, p, status);
     return hipGetLastError();
   }
   e = launch_count(d, idx, p, status, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_local_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
-                     lds_final_bytes(d), stream, idx, d.E, d.TR, d.nchunks, p);
+                     lds_final_bytes(d), stream, idx, d.E, d.L, d.TR, d.nchunks, p);
   return hipGetLastError();
 }
 

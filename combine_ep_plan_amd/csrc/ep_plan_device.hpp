@@ -290,12 +290,14 @@ __device__ __forceinline__ void source_sums(const int32_t* __restrict__ chunk_cn
 // Send side of the plan for the slots of block (c, s): cnt[s] and
 // send_off[s] (block c == 0), the final send positions and their inverse
 // (send_slot: the slot each send row holds, -1 for the rows past the last
-// one s fills). Returns each
-// slot's index among the rows s sends to its expert (-1 for a bad id).
+// one s fills), and send_seg: for each send row, its destination rank d and
+// index i inside the segment s -> d, as d * T R + i (-1 past the rows s
+// fills). Returns each slot's
+// index among the rows s sends to its expert (-1 for a bad id).
 template <int TPB>
 __device__ __forceinline__ void send_tables(const int* e_of, const int* rank_of, int s, int c,
-                                            int E, int64_t TR, const PlanPtrs& p, int32_t* soff,
-                                            const int32_t* pre, int32_t* scratch,
+                                            int E, int L, int64_t TR, const PlanPtrs& p,
+                                            int32_t* soff, const int32_t* pre, int32_t* scratch,
                                             int* within_of) {
   const int tid = threadIdx.x;
   if (c == 0)
@@ -303,7 +305,10 @@ __device__ __forceinline__ void send_tables(const int* e_of, const int* rank_of,
   block_exclusive_scan<TPB>(soff, E, scratch, &soff[E]);
   if (c == 0) {
     for (int e = tid; e <= E; e += TPB) p.send_off[(size_t)s * (E + 1) + e] = soff[e];
-    for (int64_t j = soff[E] + tid; j < TR; j += TPB) p.send_slot[(size_t)s * TR + j] = -1;
+    for (int64_t j = soff[E] + tid; j < TR; j += TPB) {
+      p.send_slot[(size_t)s * TR + j] = -1;
+      p.send_seg[(size_t)s * TR + j] = -1;
+    }
   }
 #pragma unroll
   for (int sub = 0; sub < (kPlanChunk / TPB); ++sub) {
@@ -316,8 +321,11 @@ __device__ __forceinline__ void send_tables(const int* e_of, const int* rank_of,
       continue;
     }
     within_of[sub] = pre[e] + rank_of[sub];
-    p.send_pos[(size_t)s * TR + i] = soff[e] + within_of[sub];
-    p.send_slot[(size_t)s * TR + soff[e] + within_of[sub]] = (int32_t)((size_t)s * TR + i);
+    const int pos = soff[e] + within_of[sub];
+    const int d = e / L;
+    p.send_pos[(size_t)s * TR + i] = pos;
+    p.send_slot[(size_t)s * TR + pos] = (int32_t)((size_t)s * TR + i);
+    p.send_seg[(size_t)s * TR + pos] = (int32_t)(d * TR + (pos - soff[d * L]));
   }
 }
 

@@ -120,6 +120,11 @@ typedef struct ep_plan_view {
                                      its send row s*T*R + send_pos and its
                                      grouped row d*cap + grp_pos; -1, -1 past
                                      the last delivered row */
+    int32_t *send_seg;  /* [N][T*R]  for send row p < send_off[s][E] of s:
+                                     d*T*R + i, where d is the destination
+                                     rank and i = p - send_off[s][dL] the
+                                     row's index in the segment s -> d;
+                                     -1 for p >= send_off[s][E] */
 } ep_plan_view;
 
 /* Worst-case receive rows N * T * max(R, E/N) ("Send and receive buffers");
@@ -161,7 +166,9 @@ EP_API int ep_plan_views(const ep_desc *d, void *plan_ws, ep_plan_view *v);
  *                     (each truncated to cap rows); -1 for j past the end;
  *   send_slot[s][p] = the slot (s*T + t)*R + k with send_pos[s][t][k] = p
  *                     (the inverse of send_pos); -1 for p >= send_off[s][E];
- *   recv_rows[j]    = (s*T*R + send_pos, comb_row) of the slot grp_slot[j].
+ *   recv_rows[j]    = (s*T*R + send_pos, comb_row) of the slot grp_slot[j];
+ *   send_seg[s][p]  = d*T*R + (p - send_off[s][dL]) for the rank d whose
+ *                     segment holds send row p; -1 for p >= send_off[s][E].
  * Slots with an id outside [0, E) get -1 and set EP_STATUS_BAD_EXPERT; rows
  * with grp_pos >= cap get -1 and set EP_STATUS_CAPACITY. status: device
  * int32, bits OR-ed in. Deterministic: equal inputs give equal bytes. */

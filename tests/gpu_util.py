@@ -10,7 +10,7 @@ import combine_ep_plan_amd as ep
 import ep_workloads as W
 
 PLAN_FIELDS = ("cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos",
-               "src_off", "comb_row", "grp_slot", "send_slot", "recv_rows")
+               "src_off", "comb_row", "grp_slot", "send_slot", "recv_rows", "send_seg")
 
 
 def note(msg: str) -> None:
@@ -54,7 +54,7 @@ def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
     shapes = {"cnt": (N, E), "send_off": (N, E + 1), "send_pos": (N, T, R),
               "recv_off": (N, N + 1), "grp_off": (N, L + 1), "grp_pos": (N, T, R),
               "src_off": (N, E), "comb_row": (N, T, R), "grp_slot": (N * T * R,),
-              "send_slot": (N, T * R), "recv_rows": (N * T * R, 2)}
+              "send_slot": (N, T * R), "recv_rows": (N * T * R, 2), "send_seg": (N, T * R)}
     v = ep.plan_views(d, b.plan_ws)
     base = b.plan_ws.data_ptr()
     ws = b.plan_ws.cpu().numpy()
@@ -67,8 +67,9 @@ def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
 
 
 def expected_plan_extras(p: dict, idx: np.ndarray, N: int, E: int, cap: int) -> dict:
-    """src_off, comb_row, grp_slot, send_slot and recv_rows from the
-    oracle's cnt, grp_pos and send_pos, by their definitions."""
+    """src_off, comb_row, grp_slot, send_slot, recv_rows and send_seg from
+    the oracle's cnt, grp_pos, send_pos and send_off and the routing ids, by
+    their definitions."""
     L = E // N
     cnt = p["cnt"].astype(np.int64)
     src_off = np.vstack([np.zeros((1, E), np.int64), np.cumsum(cnt, axis=0)[:-1]])
@@ -94,9 +95,16 @@ def expected_plan_extras(p: dict, idx: np.ndarray, N: int, E: int, cap: int) -> 
     gs = grp_slot[have]
     recv_rows[have, 0] = (gs // (T * R)) * T * R + sp.reshape(-1)[gs]
     recv_rows[have, 1] = comb.reshape(-1)[gs]
+    # send_seg: destination rank and index inside the segment s -> d
+    send_seg = np.full((N, T * R), -1, np.int64)
+    ids = idx.reshape(N, T * R).astype(np.int64)
+    for s in range(N):
+        n = int(p["send_off"][s, E])
+        dd = ids[s, send_slot[s, :n] - s * T * R] // L
+        send_seg[s, :n] = dd * T * R + (np.arange(n) - p["send_off"][s, dd * L])
     return {"src_off": src_off.astype(np.int32), "comb_row": comb.astype(np.int32),
             "grp_slot": grp_slot.astype(np.int32), "send_slot": send_slot.astype(np.int32),
-            "recv_rows": recv_rows.astype(np.int32)}
+            "recv_rows": recv_rows.astype(np.int32), "send_seg": send_seg.astype(np.int32)}
 
 
 def bf16_close(got: np.ndarray, want: np.ndarray, rel: float = 8e-3) -> np.ndarray:

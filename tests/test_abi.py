@@ -111,15 +111,15 @@ def test_plan_views_layout():
     v = ep.plan_views(d, base)
     N, E, L, NTR = 8, 256, 32, 8 * 4096 * 8
     names = ["cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos", "src_off",
-             "comb_row", "grp_slot", "send_slot", "recv_rows"]
+             "comb_row", "grp_slot", "send_slot", "recv_rows", "send_seg"]
     sizes = [N * E, N * (E + 1), NTR, N * (N + 1), N * (L + 1), NTR, N * E, NTR, NTR, NTR,
-             2 * NTR]
+             2 * NTR, NTR]
     ptrs = [getattr(v, n) for n in names]
     assert ptrs[0] == base
     for p, q, n in zip(ptrs, ptrs[1:], sizes):
         assert (p - base) % 256 == 0
         assert q - p >= 4 * n                      # no overlap
-    assert ep.plan_bytes(d) >= ptrs[-1] - base + 8 * NTR
+    assert ep.plan_bytes(d) >= ptrs[-1] - base + 4 * NTR
 
 
 def test_status_strings():
