@@ -105,6 +105,13 @@ EDGE_SHAPES = [
     W.Shape("max_experts", 2, 64, 64, 2048, 16),
     W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"),
     W.Shape("zipf_mid", 16, 64, 512, 128, 6, routing="zipf", expert="scale"),
+    # Sources above 4 MiB of token rows take the token-order sender: one pass
+    # of 14 chunks per lane, the two-plane fp8 form, and the general kernel
+    # (rows over 14 KB).
+    W.Shape("large_source_bf16", 2, 512, 4608, 16, 8, expert="scale"),
+    W.Shape("large_source_fp8", 2, 600, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128,
+            expert="dequant"),
+    W.Shape("large_source_wide_row", 2, 300, 8192, 4, 2),
 ]
 
 
