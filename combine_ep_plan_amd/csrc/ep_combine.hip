@@ -26,6 +26,8 @@ constexpr int kBlock = kWavesPerBlock * kWave;
 constexpr int kCombV = 7;          // 16-byte chunks (8 bf16) per lane per block
 constexpr int kCombWaves = 2;      // waves per output token
 constexpr int kCombRows = 2;       // expert rows in flight per wave
+constexpr int kPresumV = 1;        // presum_rows_kernel: chunks per lane per block
+constexpr int kPresumW = 14;       // and waves per token
 
 __device__ __forceinline__ int wave_index() {
   return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
@@ -144,6 +146,64 @@ __global__ __launch_bounds__(kBlock) void presum_kernel(const uint16_t* y, const
         fma_row(acc, v, wt[k]);
       }
       store_acc(acc, o, base, n16);
+    }
+  }
+}
+
+// Expert side with every expert row of a token in flight (R <= kPresumMaxR):
+// wave part of token tok owns column blocks of 64 x V chunks; per block it
+// loads the token's R rows, then for each group (leader k0, in k order) sums
+// w_k * y_k over the group's slots in k order with fused multiply-adds from
+// 0, rounds once to bf16 and stores the leader's partial row. The same
+// arithmetic as presum_kernel, so the same bits. Measured (whole partial-sum
+// combine, expert and source side): decode 258-267 us against 271 us with
+// presum_kernel, prefill 1609-1621 against 1701 us; 1 chunk per lane and 14
+// waves per token against 2 and 7: 258-263 against 264-267 us at decode. The
+// same shape for the source side was slower at prefill (1702-1708 us).
+constexpr int kPresumMaxR = 8;
+
+template <int V, int W>
+__global__ __launch_bounds__(kBlock) void presum_rows_kernel(const uint16_t* y, const float* w,
+                                                             const int32_t* comb_row,
+                                                             uint16_t* partial, int NT, int R,
+                                                             int H, int cap, int64_t rows_in) {
+  const int wv = wave_index();
+  const int tok = wv / W;
+  const int part = wv % W;
+  if (tok >= NT) return;
+  const int32_t* rows = comb_row + (size_t)tok * R;
+  const float* wt = w + (size_t)tok * R;
+  int rk[kPresumMaxR], dk[kPresumMaxR];
+  float wk[kPresumMaxR];
+#pragma unroll
+  for (int k = 0; k < kPresumMaxR; ++k) {
+    rk[k] = k < R ? rows[k] : -1;
+    wk[k] = k < R ? wt[k] : 0.0f;
+    dk[k] = slot_ok(rk[k], rows_in) ? rk[k] / cap : -1;
+  }
+  const int n16 = H / 8;
+  const u32x4* ybase = (const u32x4*)y;
+  for (int base = part * kWave * V; base < n16; base += W * kWave * V) {
+    RowRegs<V> v[kPresumMaxR];
+#pragma unroll
+    for (int k = 0; k < kPresumMaxR; ++k)
+      if (dk[k] >= 0) load_row16(v[k], ybase + (size_t)rk[k] * n16, base, n16);
+#pragma unroll
+    for (int k0 = 0; k0 < kPresumMaxR; ++k0) {
+      if (dk[k0] < 0) continue;
+      bool leader = true;
+#pragma unroll
+      for (int k2 = 0; k2 < k0; ++k2) leader = leader && dk[k2] != dk[k0];
+      if (!leader) continue;
+      float acc[V][8];
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+#pragma unroll
+      for (int k = k0; k < kPresumMaxR; ++k)
+        if (dk[k] == dk[k0]) fma_row(acc, v[k], wk[k]);
+      store_acc(acc, (u32x4*)(partial + ((size_t)tok * R + k0) * H), base, n16);
     }
   }
 }
@@ -278,8 +338,13 @@ hipError_t launch_combine_presum(const Dims& d, const uint16_t* y, const float* 
   if (d.NT == 0) return hipSuccess;
   const dim3 grid(blocks_for(d.NT * kCombWaves));
   const int64_t rows_in = (int64_t)d.N * d.cap;
-  hipLaunchKernelGGL(presum_kernel, grid, dim3(kBlock), 0, stream, y, w, p.comb_row, partial,
-                     (int)d.NT, d.R, d.H, (int)d.cap, rows_in);
+  if (d.R <= kPresumMaxR)
+    hipLaunchKernelGGL((presum_rows_kernel<kPresumV, kPresumW>), dim3(blocks_for(d.NT * kPresumW)),
+                       dim3(kBlock), 0, stream, y, w, p.comb_row, partial, (int)d.NT, d.R, d.H,
+                       (int)d.cap, rows_in);
+  else
+    hipLaunchKernelGGL(presum_kernel, grid, dim3(kBlock), 0, stream, y, w, p.comb_row, partial,
+                       (int)d.NT, d.R, d.H, (int)d.cap, rows_in);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(presum_final_kernel, grid, dim3(kBlock), 0, stream, partial, p.comb_row, out,
