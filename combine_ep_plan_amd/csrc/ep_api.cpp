@@ -217,7 +217,8 @@ int check_planes(const ep::Dims& d, const void* const* pl, int dev, const char* 
   DeviceScope scope(stream);                                             \
   if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device"); \
   {                                                                      \
-    const int rc_ = check_ptr(ws, scope.device(), "plan_ws");            \
+    int rc_ = check_ptr(ws, scope.device(), "plan_ws");                  \
+    if (rc_ == EP_OK) rc_ = check_aligned16(ws, "plan_ws");              \
     if (rc_ != EP_OK) return rc_;                                        \
   }                                                                      \
   const ep::PlanPtrs pp = plan_ptrs(dims, ws);

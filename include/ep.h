@@ -34,8 +34,10 @@
  *     row-major in the shapes given below. The library allocates nothing and
  *     keeps no state between calls; it is re-entrant.
  *   - Row buffers (payload planes, expert outputs, combined tokens, partial
- *     sums, KV pools) must start on a 16-byte boundary (EP_ERR_INVALID_ARG
- *     otherwise); they are moved with 16-byte vector accesses.
+ *     sums, KV pools) and the plan workspace must start on a 16-byte
+ *     boundary (EP_ERR_INVALID_ARG otherwise); rows are moved with 16-byte
+ *     vector accesses and the plan's row-pair table is read 8 bytes at a
+ *     time.
  *   - Work is enqueued on `stream` and the call returns without waiting.
  *     The device is taken from the stream (not from the calling thread);
  *     buffers on another device give EP_ERR_DEVICE_MISMATCH.

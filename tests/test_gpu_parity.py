@@ -368,3 +368,7 @@ def test_misaligned_row_buffers_are_rejected():
     out_raw = torch.empty(b.out.numel() + 8, dtype=torch.int16, device="cuda")
     with pytest.raises(ep.EPError):
         ep.combine(d, b.expert_out, b.weights, b.plan_ws, out_raw[4:4 + b.out.numel()])
+    ws_raw = torch.empty(b.plan_ws.numel() + 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ep.EPError) as e:
+        ep.plan(d, b.idx, ws_raw[4:4 + b.plan_ws.numel()], b.status)
+    assert e.value.code == ep.EP_ERR_INVALID_ARG and "plan_ws" in str(e.value)
