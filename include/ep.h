@@ -251,8 +251,9 @@ EP_API int ep_dispatch_quant(const ep_desc *d, const int32_t *topk_idx,
  * information, before the counts have been exchanged).
  *
  * Sender half. Uses only each source rank's own data: the send side of the
- * plan (cnt[s], send_off[s], send_pos[s], as ep_plan writes them; these
- * rows are the routing information the source publishes) and the pack, with
+ * plan (cnt[s], send_off[s], send_pos[s], send_slot[s], send_seg[s], as
+ * ep_plan writes them; these rows are the routing information the source
+ * publishes) and the pack, with
  * one change of destination: row i of the segment s -> d (the rows s sends
  * to the experts of rank d, which start at send_off[s][d L]) goes to
  * priv[p][(d N + s) P + i] when i < P = priv_rows, and to the send buffer
@@ -267,8 +268,9 @@ EP_API int ep_dispatch_send(const ep_desc *d, const int32_t *topk_idx,
                             hipStream_t stream);
 
 /* The sender half in two steps (ep_dispatch_send = send_plan, then
- * send_pack): send_plan writes cnt[s], send_off[s], send_pos[s] (the
- * routing information each source publishes) and flags bad ids in status;
+ * send_pack): send_plan writes cnt[s], send_off[s], send_pos[s],
+ * send_slot[s], send_seg[s] (the routing information each source
+ * publishes) and flags bad ids in status;
  * send_pack moves the rows (priv as for ep_dispatch_send). */
 EP_API int ep_dispatch_send_plan(const ep_desc *d, const int32_t *topk_idx,
                                  void *plan_ws, int32_t *status,
@@ -281,7 +283,7 @@ EP_API int ep_dispatch_send_pack(const ep_desc *d, const int32_t *topk_idx,
 /* Receiver half, after ep_dispatch_send on the same plan_ws (stream order
  * or an event). The exchange reads every source's published cnt row and
  * computes the receive side of the plan (src_off, recv_off, grp_off,
- * grp_pos, comb_row, grp_slot, capacity bit in status), then every
+ * grp_pos, comb_row, grp_slot, recv_rows, capacity bit in status), then every
  * delivered row is moved into the grouped layout from wherever the sender
  * put it (private region or send buffer). Afterwards plan_ws and grouped
  * are identical to those of ep_plan, ep_dispatch_pack, ep_dispatch_recv. */
