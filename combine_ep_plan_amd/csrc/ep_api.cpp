@@ -82,7 +82,9 @@ int derive(const ep_desc* d, ep::Dims* o) {
   }
   const int64_t nch = (o->TR + ep::kPlanChunk - 1) / ep::kPlanChunk;
   o->nchunks = (int)(nch > 0 ? nch : 1);
-  // Copy kernels launch one wave per 7 KB row segment.
+  // Bound on the copy grids: the row copies launch one wave per 1 KB piece
+  // of a row, at most 7x this count of 7 KB segments, so under 2^29 waves
+  // (int wave indices; grid.x below 2^27 blocks).
   const int64_t segs = (o->row[0] + 7167) / 7168;
   if (NTR * segs >= kMaxWaves)
     return fail(EP_ERR_UNSUPPORTED, "rows x row segments must be < 2^26");

@@ -11,17 +11,16 @@
 // Rows move as opaque bytes; lane l of a wave moves 16-byte chunks l, l+64,
 // ... and all chunks a wave holds are loaded before the first store. Row
 // indices are wave-uniform and live in scalar registers. Two shapes:
-//   - 1 KB pieces in output order (the sender in send order and the
-//     receiver in receive order): consecutive waves write consecutive 1 KB
-//     pieces, so the stores advance through memory as one front; measured
-//     on gfx950 this beats whole rows per wave for store-heavy copies (a
-//     fill writes 6.8 TB/s with 1 KB per wave against 5.3 TB/s with 14 KB).
-//     Each wave needs one table load to find its rows.
-//   - 7 KB row segments (the split receiver, the per-pair transfer and the
-//     unpack): one wave per 448-chunk segment (a 14 KB bf16 row at H = 7168
-//     is two waves), 6.4 TB/s for a plain copy against 5.8 TB/s with 14 KB
-//     per wave. The token-order sender (large sources, and the split
-//     sender) gives one wave a token pair and writes each row R times.
+//   - 1 KB pieces in output order (the sender in send order, the receiver in
+//     receive order, the staged transfer and unpack): consecutive waves
+//     write consecutive 1 KB pieces, so the stores advance through memory as
+//     one front; measured on gfx950 this beats whole rows per wave for
+//     store-heavy copies (a fill writes 6.8 TB/s with 1 KB per wave against
+//     5.3 TB/s with 14 KB). Each wave needs one or two table loads to find
+//     its rows.
+//   - whole rows per token pair (the token-order senders, for sources whose
+//     token rows do not fit an XCD's L2): one wave loads two token rows and
+//     writes each to its R send rows.
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 #include "ep_plan_device.hpp"
@@ -49,35 +48,6 @@ struct Planes {
 
 __device__ __forceinline__ int wave_index() {
   return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
-}
-
-// Segments a row of `row` bytes splits into (rows that are not a multiple
-// of 16 bytes are copied whole, 4 bytes per lane, by segment 0).
-__host__ __device__ __forceinline__ int row_segments(int64_t row) {
-  return (row & 15) == 0 ? (int)(((row >> 4) + kSeg - 1) / kSeg) : 1;
-}
-
-// Copy segment `seg` of one row with the whole wave (7 chunks per lane, or 1
-// when the segment holds at most 64 chunks, so that no store instruction
-// carries only clamped duplicates).
-__device__ __forceinline__ void wave_copy_segment(const uint8_t* src, uint8_t* dst, int64_t row,
-                                                  int seg) {
-  if ((row & 15) == 0) {
-    const int n16 = (int)(row >> 4);
-    const int base = seg * kSeg;
-    if (base >= n16) return;
-    if (n16 - base > kWave) {
-      RowRegs<kSegV> r;
-      load_row16(r, (const u32x4*)src, base, n16);
-      store_row16(r, (u32x4*)dst, base, n16);
-    } else {
-      RowRegs<1> r;
-      load_row16(r, (const u32x4*)src, base, n16);
-      store_row16(r, (u32x4*)dst, base, n16);
-    }
-  } else if (seg == 0) {
-    copy_row4((const uint32_t*)src, (uint32_t*)dst, row >> 2);
-  }
 }
 
 // Sender: one wave per pair of tokens. Both token rows are loaded (up to
@@ -426,6 +396,89 @@ __global__ __launch_bounds__(kBlock) void recv_rows_kernel(RecvArgs a) {
   if (w < a.pl[q].waves) recv_wave<SPLIT>(a, a.pl[q], q, w);
 }
 
+// The staged receive path, with the same 1 KB pieces. Send row g = s T R + p
+// is row i of the segment s -> d (send_seg[g] = d T R + i) and sits at row
+// recv_off[d][s] + i of d's receive buffer; rows at or beyond cap are not
+// there (dropped). One send_seg load per wave names the rank and the index.
+struct StagedArgs {
+  MovePlane pl[2];
+  const int32_t* send_seg;
+  const int32_t* recv_off;
+  const int2* recv_rows;
+  FastDiv tr_div;
+  int TR, N, NTR;
+  int64_t cap;
+};
+
+// Receive-buffer row (d cap + r) of send row g, or -1.
+__device__ __forceinline__ int64_t staged_row(const StagedArgs& a, int g) {
+  const int seg = a.send_seg[g];
+  if (seg < 0) return -1;
+  const int d = fast_div(seg, a.tr_div);
+  if (d >= a.N) return -1;
+  const int i = seg - d * a.TR;
+  const int s = fast_div(g, a.tr_div);
+  const int64_t r = (int64_t)a.recv_off[(size_t)d * (a.N + 1) + s] + i;
+  return r >= 0 && r < a.cap ? (int64_t)d * a.cap + r : -1;
+}
+
+// TRANSFER: the network write, in send order (wave w: piece of send row
+// w / per_row). Otherwise the receiver shuffle, in receive order (recv_rows).
+template <bool TRANSFER>
+__device__ __forceinline__ void staged_wave(const StagedArgs& a, const MovePlane& pl, int w) {
+  if (pl.pieces) {
+    const int j = wave_uniform(fast_div(w, pl.per_row_div));
+    const int base = (w - j * pl.per_row) * kWave;
+    int64_t from, to;
+    if (TRANSFER) {
+      from = j;
+      to = staged_row(a, j);
+    } else {
+      const int2 r = a.recv_rows[j];
+      const int g = wave_uniform(r.x);
+      if (g < 0 || g >= a.NTR || r.y < 0 || r.y >= (int64_t)a.N * a.cap) return;
+      from = staged_row(a, g);
+      to = wave_uniform(r.y);
+    }
+    if (from < 0 || to < 0) return;
+    const size_t row = (size_t)pl.n16 * 16;
+    RowRegs<1> v;
+    load_row16<1, true>(v, (const u32x4*)(pl.src + (size_t)from * row), base, pl.n16);
+    store_row16(v, (u32x4*)(pl.dst + (size_t)to * row), base, pl.n16);
+    return;
+  }
+  const int64_t c = (int64_t)w * kWave + lane_id();
+  if (c >= (int64_t)a.NTR * pl.per_row) return;
+  const int j = (int)(c / pl.per_row);
+  const int u = (int)(c - (int64_t)j * pl.per_row);
+  int64_t from, to;
+  if (TRANSFER) {
+    from = j;
+    to = staged_row(a, j);
+  } else {
+    const int2 r = a.recv_rows[j];
+    if (r.x < 0 || r.x >= a.NTR || r.y < 0 || r.y >= (int64_t)a.N * a.cap) return;
+    from = staged_row(a, r.x);
+    to = r.y;
+  }
+  if (from < 0 || to < 0) return;
+  const size_t f = (size_t)from * pl.per_row + u, t = (size_t)to * pl.per_row + u;
+  if (pl.unit == 16)
+    store_stream((u32x4*)pl.dst + t, load_stream((const u32x4*)pl.src + f));
+  else
+    __builtin_nontemporal_store(__builtin_nontemporal_load((const uint32_t*)pl.src + f),
+                                (uint32_t*)pl.dst + t);
+}
+
+template <bool TRANSFER>
+__global__ __launch_bounds__(kBlock) void staged_kernel(StagedArgs a) {
+  int b = blockIdx.x;
+  const int q = b < a.pl[0].blocks ? 0 : 1;
+  if (q) b -= a.pl[0].blocks;
+  const int w = b * kWavesPerBlock + (int)threadIdx.x / kWave;
+  if (w < a.pl[q].waves) staged_wave<TRANSFER>(a, a.pl[q], w);
+}
+
 // Chunks per lane for a single pass over a plane of `row` bytes: 14, 7 or 1;
 // 0 if the plane needs the general kernel.
 int pass_v(int64_t row) {
@@ -518,77 +571,6 @@ __global__ __launch_bounds__(kBlock) void pack_split_kernel(Planes pl, Split sp,
 }
 
 
-// The network write: send row i of source s lies in the segment of the rank
-// d with send_off[s][dL] <= i < send_off[s][(d+1)L] and lands in d's receive
-// buffer at recv_off[d][s] + (i - send_off[s][dL]).
-__global__ __launch_bounds__(kBlock) void transfer_kernel(Planes pl, const int32_t* __restrict__ send_off,
-                                                          const int32_t* __restrict__ recv_off,
-                                                          int N, int E, int L, int64_t TR,
-                                                          int64_t cap, int wps) {
-  const int w = wave_index();
-  const int g = w / wps;
-  const int seg = w % wps;
-  if (g >= (int64_t)N * TR) return;
-  const int s = (int)(g / TR);
-  const int i = (int)(g - (int64_t)s * TR);
-  const int32_t* so = send_off + (size_t)s * (E + 1);
-  if (i >= so[E]) return;
-  int lo = 0, hi = N - 1;  // largest d with so[d * L] <= i
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (so[mid * L] <= i) lo = mid; else hi = mid - 1;
-  }
-  const int d = lo;
-  const int64_t r = (int64_t)recv_off[(size_t)d * (N + 1) + s] + (i - so[d * L]);
-  if (r < 0 || r >= cap) return;
-  for (int q = 0; q < pl.planes; ++q) {
-    const int64_t row = pl.row[q];
-    wave_copy_segment(pl.src[q] + ((size_t)s * TR + i) * row,
-                      pl.dst[q] + ((size_t)d * cap + r) * row, row, seg);
-  }
-}
-
-// Receiver on a materialised receive buffer. Row r of rank d came from the
-// source s with recv_off[d][s] <= r < recv_off[d][s+1]; inside s's segment it
-// is send row send_off[s][dL] + (r - recv_off[d][s]), whose expert e gives
-// the grouped row grp_off[d][e - dL] + src_off[s][e] + (rank within e).
-__global__ __launch_bounds__(kBlock) void unpack_kernel(Planes pl, const int32_t* __restrict__ send_off,
-                                                        const int32_t* __restrict__ recv_off,
-                                                        const int32_t* __restrict__ grp_off,
-                                                        const int32_t* __restrict__ src_off,
-                                                        int N, int E, int L, int64_t cap,
-                                                        int wps) {
-  const int d = blockIdx.y;
-  const int w = wave_index();
-  const int r = w / wps;
-  const int seg = w % wps;
-  const int32_t* ro = recv_off + (size_t)d * (N + 1);
-  const int64_t lim = ro[N] < cap ? ro[N] : cap;
-  if (r >= lim) return;
-  int lo = 0, hi = N - 1;  // largest s with ro[s] <= r
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ro[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  const int s = lo;
-  const int32_t* so = send_off + (size_t)s * (E + 1);
-  const int i = so[d * L] + (r - ro[s]);
-  int elo = d * L, ehi = d * L + L - 1;  // largest e of rank d with so[e] <= i
-  while (elo < ehi) {
-    const int mid = (elo + ehi + 1) >> 1;
-    if (so[mid] <= i) elo = mid; else ehi = mid - 1;
-  }
-  const int e = elo;
-  const int64_t gpos = (int64_t)grp_off[(size_t)d * (L + 1) + (e - d * L)] +
-                       src_off[(size_t)s * E + e] + (i - so[e]);
-  if (gpos < 0 || gpos >= cap) return;
-  for (int q = 0; q < pl.planes; ++q) {
-    const int64_t row = pl.row[q];
-    wave_copy_segment(pl.src[q] + ((size_t)d * cap + r) * row,
-                      pl.dst[q] + ((size_t)d * cap + gpos) * row, row, seg);
-  }
-}
-
 // Plain copy with the same per-wave loop as the row copies (7 KB per wave).
 __global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4* src, u32x4* dst,
                                                             int64_t n16) {
@@ -616,12 +598,6 @@ unsigned blocks_for(int64_t waves) {
   return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
-// Waves per row: enough segments for the largest plane.
-int waves_per_row(const Dims& d) {
-  int w = 1;
-  for (int q = 0; q < d.planes; ++q) w = row_segments(d.row[q]) > w ? row_segments(d.row[q]) : w;
-  return w;
-}
 
 }  // namespace
 
@@ -852,25 +828,33 @@ hipError_t launch_recv_split(const Dims& d, const void* const send[2], void* con
   return launch_recv_rows(d, send, p, grouped, P > 0 ? &v : nullptr, stream);
 }
 
+template <bool TRANSFER>
+hipError_t launch_staged(const Dims& d, const void* const src[2], const PlanPtrs& p,
+                         void* const dst[2], hipStream_t stream) {
+  if (d.NTR == 0) return hipSuccess;
+  StagedArgs a{};
+  for (int q = 0; q < d.planes; ++q) a.pl[q] = move_plane(src[q], dst[q], d.row[q], d.NTR);
+  a.send_seg = p.send_seg;
+  a.recv_off = p.recv_off;
+  a.recv_rows = (const int2*)p.recv_rows;
+  a.tr_div = fast_div_of((uint32_t)d.TR);
+  a.TR = (int)d.TR;
+  a.N = d.N;
+  a.NTR = (int)d.NTR;
+  a.cap = d.cap;
+  hipLaunchKernelGGL(staged_kernel<TRANSFER>, dim3((unsigned)(a.pl[0].blocks + a.pl[1].blocks)),
+                     dim3(kBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_transfer(const Dims& d, const void* const send[2], const PlanPtrs& p,
                            void* const recv[2], hipStream_t stream) {
-  if (d.NTR == 0) return hipSuccess;
-  const int wps = waves_per_row(d);
-  hipLaunchKernelGGL(transfer_kernel, dim3(blocks_for(d.NTR * wps)), dim3(kBlock), 0, stream,
-                     make_planes(d, send, recv), p.send_off, p.recv_off, d.N, d.E, d.L, d.TR,
-                     d.cap, wps);
-  return hipGetLastError();
+  return launch_staged<true>(d, send, p, recv, stream);
 }
 
 hipError_t launch_unpack(const Dims& d, const void* const recv[2], const PlanPtrs& p,
                          void* const grouped[2], hipStream_t stream) {
-  const int64_t rows = d.cap < d.NTR ? d.cap : d.NTR;  // no rank holds more
-  if (rows == 0) return hipSuccess;
-  const int wps = waves_per_row(d);
-  hipLaunchKernelGGL(unpack_kernel, dim3(blocks_for(rows * wps), d.N), dim3(kBlock), 0, stream,
-                     make_planes(d, recv, grouped), p.send_off, p.recv_off, p.grp_off,
-                     p.src_off, d.N, d.E, d.L, d.cap, wps);
-  return hipGetLastError();
+  return launch_staged<false>(d, recv, p, grouped, stream);
 }
 
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
