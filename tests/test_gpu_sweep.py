@@ -1,7 +1,9 @@
 """Seeded sweep of random small shapes through the one-call dispatch, the
 stand-in expert, combine and the partial-sum combine, against the oracle:
 random N, experts per rank, R (including R > E / N with repeated ids), T
-(including 0), H, payload, invalid ids and tight capacities."""
+(including 0), H, payload, invalid ids and tight capacities. Each case also
+runs the staged receive (transfer, then unpack) and the split dispatch with
+a random number of private rows."""
 import gc
 
 import numpy as np
@@ -78,6 +80,42 @@ def test_sweep_against_oracle(seed):
     assert bf16_close(out, ref["out"]).all()
     want_partial, want_out = oracle.combine_presum(ref["y"], wl.weights, wl.idx, p)
     np.testing.assert_array_equal(pout.cpu().numpy().view(np.uint16), want_out)
+
+    # staged receive: the receive buffers as the oracle's per-pair write; the
+    # grouped layout too unless capacity overflowed (rows past cap never
+    # reach a receive buffer)
+    recv = [torch.zeros((N, cap, t.shape[2]), dtype=torch.uint8, device="cuda") for t in b.send]
+    staged = [torch.zeros_like(g) for g in b.grouped]
+    ep.dispatch_transfer(d, b.send, b.plan_ws, recv)
+    ep.dispatch_unpack(d, recv, b.plan_ws, staged)
+    torch.cuda.synchronize()
+    for q in range(len(wl.planes)):
+        rv, sg = recv[q].cpu().numpy(), staged[q].cpu().numpy()
+        for dd in range(N):
+            n = min(int(totals[dd]), cap)
+            np.testing.assert_array_equal(rv[dd, :n], ref["recv"][q][dd, :n], err_msg=f"recv {dd}")
+            if not p["status"] & 2:
+                np.testing.assert_array_equal(sg[dd, :n], ref["grouped"][q][dd, :n],
+                                              err_msg=f"staged grouped {dd}")
+    del recv, staged
+
+    # split dispatch with P private rows per (destination, source)
+    P = min(int(np.random.default_rng(2000 + seed).integers(0, 6)), sh.tokens * sh.topk)
+    ws2 = torch.empty_like(b.plan_ws)
+    send2 = [torch.zeros_like(t) for t in b.send]
+    grouped2 = [torch.zeros_like(g) for g in b.grouped]
+    priv = ep.priv_buffers(d, P)
+    st2 = torch.zeros_like(b.status)
+    ep.dispatch_send(d, b.idx, b.x, ws2, send2, priv, P, st2)
+    ep.dispatch_recv_split(d, send2, priv, P, ws2, grouped2, st2)
+    torch.cuda.synchronize()
+    assert int(st2.item()) == p["status"]
+    for q in range(len(wl.planes)):
+        g2 = grouped2[q].cpu().numpy()
+        for dd in range(N):
+            n = min(int(totals[dd]), cap)
+            np.testing.assert_array_equal(g2[dd, :n], ref["grouped"][q][dd, :n],
+                                          err_msg=f"split P={P} grouped {dd}")
     np.testing.assert_array_equal(partial.cpu().numpy().view(np.uint16), want_partial)
     del b
     gc.collect()
