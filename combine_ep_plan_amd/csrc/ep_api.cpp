@@ -165,9 +165,11 @@ class DeviceScope {
   hipError_t err_ = hipSuccess;
 };
 
-// A non-empty buffer must be device (or managed) memory of the stream's GPU;
-// an empty one (bytes == 0) is never touched and may be anything.
-int check_ptr(const void* p, int dev, const char* name, int64_t bytes = 1) {
+// A non-empty buffer must be device (or managed) memory of the stream's GPU
+// and, where the runtime reports the allocation's range, lie inside it for
+// all `bytes`; an empty one (bytes == 0) is never touched and may be
+// anything.
+int check_ptr(const void* p, int dev, const char* name, int64_t bytes) {
   if (bytes == 0) return EP_OK;
   if (!p) return fail(EP_ERR_INVALID_ARG, (std::string("null pointer: ") + name).c_str());
   hipPointerAttribute_t a;
@@ -182,6 +184,16 @@ int check_ptr(const void* p, int dev, const char* name, int64_t bytes = 1) {
   if (a.type == hipMemoryTypeDevice && a.device != dev)
     return fail(EP_ERR_DEVICE_MISMATCH,
                 (std::string("buffer on another device: ") + name).c_str());
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) == hipSuccess && base != nullptr) {
+    const uintptr_t end = (uintptr_t)base + size;
+    if ((uintptr_t)p < (uintptr_t)base || (uint64_t)bytes > end - (uintptr_t)p)
+      return fail(EP_ERR_INVALID_ARG,
+                  (std::string("buffer smaller than the call needs: ") + name).c_str());
+  } else {
+    (void)hipGetLastError();
+  }
   return EP_OK;
 }
 
@@ -219,7 +231,7 @@ int check_planes(const ep::Dims& d, const void* const* pl, int dev, const char* 
   DeviceScope scope(stream);                                             \
   if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device"); \
   {                                                                      \
-    int rc_ = check_ptr(ws, scope.device(), "plan_ws");                  \
+    int rc_ = check_ptr(ws, scope.device(), "plan_ws", (int64_t)layout_of(dims).bytes); \
     if (rc_ == EP_OK) rc_ = check_aligned16(ws, "plan_ws");              \
     if (rc_ != EP_OK) return rc_;                                        \
   }                                                                      \
@@ -289,8 +301,8 @@ int ep_plan_views(const ep_desc* d, void* plan_ws, ep_plan_view* v) {
 int ep_plan(const ep_desc* d, const int32_t* topk_idx, void* plan_ws, int32_t* status,
             hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
-  EP_CHECK(check_ptr(status, scope.device(), "status"));
-  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  EP_CHECK(check_ptr(status, scope.device(), "status", 4));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", 4 * dims.NTR));
   const hipError_t e = ep::launch_plan(dims, topk_idx, pp, status, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_plan");
   return EP_OK;
@@ -300,8 +312,8 @@ int ep_dispatch(const ep_desc* d, const int32_t* topk_idx, const void* const x[2
                 void* plan_ws, void* const send[2], void* const grouped[2], int32_t* status,
                 hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
-  EP_CHECK(check_ptr(status, scope.device(), "status"));
-  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  EP_CHECK(check_ptr(status, scope.device(), "status", 4));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", 4 * dims.NTR));
   EP_CHECK(check_planes(dims, (const void* const*)x, scope.device(), "x", dims.NT));
   EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
   EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
@@ -344,8 +356,8 @@ int ep_dispatch_quant(const ep_desc* d, const int32_t* topk_idx, const uint16_t*
     return fail(EP_ERR_INVALID_ARG, "ep_dispatch_quant needs the fp8 payload descriptor");
   if (dims.NT * (((int64_t)dims.H + 1023) / 1024) >= kMaxWaves)
     return fail(EP_ERR_UNSUPPORTED, "tokens x 1024-value row segments must be < 2^26");
-  EP_CHECK(check_ptr(status, scope.device(), "status"));
-  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  EP_CHECK(check_ptr(status, scope.device(), "status", 4));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", 4 * dims.NTR));
   EP_CHECK(check_ptr(x, scope.device(), "x", dims.NT * 2 * (int64_t)dims.H));
   EP_CHECK(check_aligned16(x, "x"));
   EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
@@ -395,8 +407,8 @@ int check_priv(const ep::Dims& d, void* const priv[2], int32_t P, int dev) {
 int ep_dispatch_send_plan(const ep_desc* d, const int32_t* topk_idx, void* plan_ws,
                           int32_t* status, hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
-  EP_CHECK(check_ptr(status, scope.device(), "status"));
-  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  EP_CHECK(check_ptr(status, scope.device(), "status", 4));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", 4 * dims.NTR));
   const hipError_t e = ep::launch_plan_local(dims, topk_idx, pp, status, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_dispatch_send_plan");
   return EP_OK;
@@ -406,7 +418,7 @@ int ep_dispatch_send_pack(const ep_desc* d, const int32_t* topk_idx, const void*
                           const void* plan_ws, void* const send[2], void* const priv[2],
                           int32_t priv_rows, hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
-  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+  EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", 4 * dims.NTR));
   EP_CHECK(check_planes(dims, (const void* const*)x, scope.device(), "x", dims.NT));
   EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
   EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
@@ -417,7 +429,7 @@ int ep_dispatch_send_pack(const ep_desc* d, const int32_t* topk_idx, const void*
 
 int ep_dispatch_recv_plan(const ep_desc* d, void* plan_ws, int32_t* status, hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
-  EP_CHECK(check_ptr(status, scope.device(), "status"));
+  EP_CHECK(check_ptr(status, scope.device(), "status", 4));
   const hipError_t e = ep::launch_plan_exchange(dims, pp, status, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_dispatch_recv_plan");
   return EP_OK;
@@ -441,8 +453,8 @@ int ep_dispatch_send(const ep_desc* d, const int32_t* topk_idx, const void* cons
   // Check everything before enqueueing the first half.
   {
     EP_PROLOGUE(d, stream, plan_ws);
-    EP_CHECK(check_ptr(status, scope.device(), "status"));
-    EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", dims.NTR));
+    EP_CHECK(check_ptr(status, scope.device(), "status", 4));
+    EP_CHECK(check_ptr(topk_idx, scope.device(), "topk_idx", 4 * dims.NTR));
     EP_CHECK(check_planes(dims, (const void* const*)x, scope.device(), "x", dims.NT));
     EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
     EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
@@ -458,7 +470,7 @@ int ep_dispatch_recv_split(const ep_desc* d, const void* const send[2], void* co
   // Check everything before enqueueing the first half.
   {
     EP_PROLOGUE(d, stream, plan_ws);
-    EP_CHECK(check_ptr(status, scope.device(), "status"));
+    EP_CHECK(check_ptr(status, scope.device(), "status", 4));
     EP_CHECK(check_planes(dims, (const void* const*)send, scope.device(), "send", dims.NTR));
     EP_CHECK(check_priv(dims, priv, priv_rows, scope.device()));
     EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped",
@@ -473,12 +485,12 @@ int ep_expert_stub(const ep_desc* d, const void* const grouped[2], const float* 
                    const void* plan_ws, uint16_t* expert_out, hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
   EP_CHECK(check_planes(dims, (const void* const*)grouped, scope.device(), "grouped", dims.N * dims.cap));
-  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap));
+  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap * 2 * dims.H));
   EP_CHECK(check_aligned16(expert_out, "expert_out"));
   if (alpha) {
     if (dims.payload != EP_PAYLOAD_BF16)
       return fail(EP_ERR_INVALID_ARG, "alpha applies to the bf16 payload only");
-    EP_CHECK(check_ptr(alpha, scope.device(), "alpha"));
+    EP_CHECK(check_ptr(alpha, scope.device(), "alpha", 4 * (int64_t)dims.E));
   }
   const hipError_t e = ep::launch_expert_stub(dims, grouped, alpha, pp, expert_out, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_expert_stub");
@@ -488,9 +500,9 @@ int ep_expert_stub(const ep_desc* d, const void* const grouped[2], const float* 
 int ep_combine(const ep_desc* d, const uint16_t* expert_out, const float* weights,
                const void* plan_ws, uint16_t* out, hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
-  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap));
-  EP_CHECK(check_ptr(out, scope.device(), "out", dims.NT));
-  EP_CHECK(check_ptr(weights, scope.device(), "weights", dims.NTR));
+  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap * 2 * dims.H));
+  EP_CHECK(check_ptr(out, scope.device(), "out", dims.NT * 2 * dims.H));
+  EP_CHECK(check_ptr(weights, scope.device(), "weights", 4 * dims.NTR));
   EP_CHECK(check_aligned16(expert_out, "expert_out"));
   EP_CHECK(check_aligned16(out, "out"));
   const hipError_t e = ep::launch_combine(dims, expert_out, weights, pp, out, stream);
@@ -501,10 +513,10 @@ int ep_combine(const ep_desc* d, const uint16_t* expert_out, const float* weight
 int ep_combine_presum(const ep_desc* d, const uint16_t* expert_out, const float* weights,
                       const void* plan_ws, uint16_t* partial, uint16_t* out, hipStream_t stream) {
   EP_PROLOGUE(d, stream, plan_ws);
-  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap));
-  EP_CHECK(check_ptr(partial, scope.device(), "partial", dims.NTR));
-  EP_CHECK(check_ptr(out, scope.device(), "out", dims.NT));
-  EP_CHECK(check_ptr(weights, scope.device(), "weights", dims.NTR));
+  EP_CHECK(check_ptr(expert_out, scope.device(), "expert_out", dims.N * dims.cap * 2 * dims.H));
+  EP_CHECK(check_ptr(partial, scope.device(), "partial", dims.NTR * 2 * dims.H));
+  EP_CHECK(check_ptr(out, scope.device(), "out", dims.NT * 2 * dims.H));
+  EP_CHECK(check_ptr(weights, scope.device(), "weights", 4 * dims.NTR));
   EP_CHECK(check_aligned16(expert_out, "expert_out"));
   EP_CHECK(check_aligned16(partial, "partial"));
   EP_CHECK(check_aligned16(out, "out"));
@@ -563,16 +575,16 @@ int kv_checks(int32_t ranks, const ep_kv_region* regions, int64_t m, int64_t tot
     return fail(EP_ERR_INVALID_ARG, "ep_kv_push: pools must be 16-byte aligned");
   const int64_t pieces = (total + ep::kv_piece_bytes() - 1) / ep::kv_piece_bytes();
   if (pieces >= kMaxWaves / ranks) return fail(EP_ERR_UNSUPPORTED, "ep_kv_push: request too large");
-  EP_CHECK(check_ptr(regions, dev, "regions", m));
+  EP_CHECK(check_ptr(regions, dev, "regions", m * (int64_t)sizeof(ep_kv_region)));
   EP_CHECK(check_ptr(src, dev, "src_pool", src_rank_bytes * ranks));
   EP_CHECK(check_ptr(dst, dev, "dst_pool", dst_rank_bytes * ranks));
-  EP_CHECK(check_ptr(notify, dev, "notify"));
-  EP_CHECK(check_ptr(status, dev, "status"));
+  EP_CHECK(check_ptr(notify, dev, "notify", 4));
+  EP_CHECK(check_ptr(status, dev, "status", 4));
   return EP_OK;
 }
 
-// Device memory of `dev`, or pinned host memory.
-int check_bounce(const void* p, int dev) {
+// Device memory of `dev` (at least `bytes` of it), or pinned host memory.
+int check_bounce(const void* p, int dev, int64_t bytes) {
   if (!p) return fail(EP_ERR_INVALID_ARG, "null pointer: bounce");
   if (((uintptr_t)p) & 15) return fail(EP_ERR_INVALID_ARG, "bounce must be 16-byte aligned");
   hipPointerAttribute_t a;
@@ -582,7 +594,7 @@ int check_bounce(const void* p, int dev) {
     return fail(EP_ERR_INVALID_ARG, "bounce is neither device nor pinned host memory");
   }
   if (a.type == hipMemoryTypeHost) return EP_OK;
-  return check_ptr(p, dev, "bounce");
+  return check_ptr(p, dev, "bounce", bytes);
 }
 
 }  // namespace
@@ -609,7 +621,7 @@ int ep_kv_push_staged(int32_t ranks, const ep_kv_region* regions, int64_t m, int
   EP_CHECK(kv_checks(ranks, regions, m, total, src, src_rank_bytes, dst, dst_rank_bytes, notify,
                      status, scope.device()));
   if (slots < 1 || slots > 64) return fail(EP_ERR_INVALID_ARG, "bounce_slots must be in [1, 64]");
-  EP_CHECK(check_bounce(bounce, scope.device()));
+  EP_CHECK(check_bounce(bounce, scope.device(), (int64_t)slots * 32768));
   const hipError_t e = ep::launch_kv_push_staged(ranks, regions, m, total, src, src_rank_bytes,
                                                  dst, dst_rank_bytes, bounce,
                                                  (int64_t)slots * 32768, notify, status, stream);
@@ -623,8 +635,8 @@ int ep_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) 
     return fail(EP_ERR_UNSUPPORTED, "copy too large");
   DeviceScope scope(stream);
   if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");
-  EP_CHECK(check_ptr(dst, scope.device(), "dst"));
-  EP_CHECK(check_ptr(src, scope.device(), "src"));
+  EP_CHECK(check_ptr(dst, scope.device(), "dst", (int64_t)bytes));
+  EP_CHECK(check_ptr(src, scope.device(), "src", (int64_t)bytes));
   const hipError_t e = ep::launch_probe_copy(dst, src, bytes, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_probe_copy");
   return EP_OK;

@@ -38,6 +38,10 @@
  *     boundary (EP_ERR_INVALID_ARG otherwise); rows are moved with 16-byte
  *     vector accesses and the plan's row-pair table is read 8 bytes at a
  *     time.
+ *   - A buffer that ends before the extent a call needs (per its shapes)
+ *     gives EP_ERR_INVALID_ARG when the runtime reports the allocation's
+ *     range (hipMemGetAddressRange); a sub-range of a larger allocation can
+ *     only be checked against that allocation's end.
  *   - Work is enqueued on `stream` and the call returns without waiting.
  *     The device is taken from the stream (not from the calling thread);
  *     buffers on another device give EP_ERR_DEVICE_MISMATCH.

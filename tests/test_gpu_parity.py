@@ -372,3 +372,36 @@ def test_misaligned_row_buffers_are_rejected():
     with pytest.raises(ep.EPError) as e:
         ep.plan(d, b.idx, ws_raw[4:4 + b.plan_ws.numel()], b.status)
     assert e.value.code == ep.EP_ERR_INVALID_ARG and "plan_ws" in str(e.value)
+
+
+def _alloc_range(ptr):
+    """(base, size) of the device allocation holding ptr, from the HIP
+    runtime torch has loaded."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    base, size = ctypes.c_void_p(), ctypes.c_size_t()
+    rc = hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), ctypes.c_void_p(ptr))
+    assert rc == 0, rc
+    return base.value, size.value
+
+
+def test_buffers_smaller_than_the_call_needs_are_rejected():
+    """A pointer whose required extent runs past the end of its allocation
+    fails validation (nothing is launched)."""
+    sh = W.CONFIGS["tiny"]
+    d = desc_of(sh)
+    b = ep.Buffers(d)
+    upload(b, W.make_workload(sh))
+    need = d.n_ranks * d.tokens * 2 * d.hidden                  # bytes of out
+    base, size = _alloc_range(b.out.data_ptr())
+    short = (base + size - need // 2) & ~15
+    with pytest.raises(ep.EPError) as e:
+        ep.combine(d, b.expert_out, b.weights, b.plan_ws, short)
+    assert e.value.code == ep.EP_ERR_INVALID_ARG and "smaller" in str(e.value)
+    wbase, wsize = _alloc_range(b.plan_ws.data_ptr())
+    short_ws = (wbase + wsize - ep.plan_bytes(d) // 2) & ~15
+    with pytest.raises(ep.EPError) as e:
+        ep.plan(d, b.idx, short_ws, b.status)
+    assert e.value.code == ep.EP_ERR_INVALID_ARG and "plan_ws" in str(e.value)
+    ep.plan(d, b.idx, b.plan_ws, b.status)                        # full sizes pass
+    torch.cuda.synchronize()
