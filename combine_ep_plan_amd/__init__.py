@@ -63,7 +63,7 @@ class Desc(ctypes.Structure):
 class PlanView(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos",
-        "src_off", "comb_row", "grp_slot", "send_slot", "recv_rows", "send_seg")]
+        "src_off", "comb_row", "grp_slot", "send_slot", "recv_rows", "send_seg", "win_list")]
 
 
 def _load() -> ctypes.CDLL:

@@ -82,6 +82,18 @@ int derive(const ep_desc* d, ep::Dims* o) {
   }
   const int64_t nch = (o->TR + ep::kPlanChunk - 1) / ep::kPlanChunk;
   o->nchunks = (int)(nch > 0 ? nch : 1);
+  // Windowed sender: windows of the largest power-of-two token count whose
+  // rows fit kGatherSourceBytes.
+  const int64_t tok_bytes = o->row[0] + o->row[1];
+  const int64_t src_bytes = (int64_t)d->tokens * tok_bytes;
+  o->win = 0;
+  o->nwin = 0;
+  if (src_bytes > ep::kGatherSourceBytes && src_bytes <= ep::kWindowSourceBytes) {
+    int64_t w = 1;
+    while (2 * w * tok_bytes <= ep::kGatherSourceBytes) w *= 2;
+    o->win = (int)w;
+    o->nwin = (int)((d->tokens + w - 1) / w);
+  }
   // Bound on the copy grids: the row copies launch one wave per 1 KB piece
   // of a row, at most 7x this count of 7 KB segments, so under 2^29 waves
   // (int wave indices; grid.x below 2^27 blocks).
@@ -93,12 +105,12 @@ int derive(const ep_desc* d, ep::Dims* o) {
 
 // Plan workspace: int32 arrays, each starting on a 256-byte boundary.
 struct Layout {
-  size_t off[13];
+  size_t off[14];
   size_t bytes;
 };
 
 Layout layout_of(const ep::Dims& d) {
-  const size_t n[13] = {
+  const size_t n[14] = {
       (size_t)d.N * d.E,                       // cnt
       (size_t)d.N * (d.E + 1),                 // send_off
       (size_t)d.NTR,                           // send_pos
@@ -112,10 +124,11 @@ Layout layout_of(const ep::Dims& d) {
       (size_t)d.NTR,                           // send_slot
       (size_t)2 * d.NTR,                       // recv_rows
       (size_t)d.NTR,                           // send_seg
+      (size_t)2 * d.N * d.nwin * d.win * d.R,  // win_list (windowed sender only)
   };
   Layout l{};
   size_t at = 0;
-  for (int i = 0; i < 13; ++i) {
+  for (int i = 0; i < 14; ++i) {
     l.off[i] = at;
     at += (n[i] * sizeof(int32_t) + 255) & ~(size_t)255;
   }
@@ -140,6 +153,7 @@ ep::PlanPtrs plan_ptrs(const ep::Dims& d, const void* ws) {
   p.send_slot = (int32_t*)(b + l.off[10]);
   p.recv_rows = (int32_t*)(b + l.off[11]);
   p.send_seg = (int32_t*)(b + l.off[12]);
+  p.win_list = d.win > 0 ? (int32_t*)(b + l.off[13]) : nullptr;
   return p;
 }
 
@@ -295,6 +309,7 @@ int ep_plan_views(const ep_desc* d, void* plan_ws, ep_plan_view* v) {
   v->send_slot = p.send_slot;
   v->recv_rows = p.recv_rows;
   v->send_seg = p.send_seg;
+  v->win_list = p.win_list;
   return EP_OK;
 }
 

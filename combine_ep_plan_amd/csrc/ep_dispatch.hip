@@ -265,6 +265,7 @@ __device__ __forceinline__ uint8_t* split_dst(const PrivRegions& v, int q, int g
 struct GatherArgs {
   MovePlane pl[2];
   const int32_t* send_slot;
+  const int2* win_list;  // windowed order for plane 0 (pieces), or null
   FastDiv r_div;
   int NT, NTR;
   PrivRegions split;
@@ -274,12 +275,21 @@ template <bool SPLIT>
 __device__ __forceinline__ void gather_wave(const GatherArgs& a, const MovePlane& pl, int q,
                                             int w) {
   if (pl.pieces) {
-    const int g = wave_uniform(fast_div(w, pl.per_row_div));  // send row
-    const int base = (w - g * pl.per_row) * kWave;
-    const int slot = wave_uniform(a.send_slot[g]);
-    if (slot < 0) return;  // a row its source does not fill
-    const int tok = fast_div(slot, a.r_div);
-    if (tok >= a.NT) return;
+    const int j = wave_uniform(fast_div(w, pl.per_row_div));  // send row or list entry
+    const int base = (w - j * pl.per_row) * kWave;
+    int g, tok;
+    if (a.win_list != nullptr && q == 0) {
+      const int2 e = a.win_list[j];
+      g = wave_uniform(e.x);
+      tok = wave_uniform(e.y);
+      if (g < 0 || g >= a.NTR || tok < 0 || tok >= a.NT) return;
+    } else {
+      g = j;
+      const int slot = wave_uniform(a.send_slot[g]);
+      if (slot < 0) return;  // a row its source does not fill
+      tok = fast_div(slot, a.r_div);
+      if (tok >= a.NT) return;
+    }
     const size_t row = (size_t)pl.n16 * 16;
     uint8_t* dst = pl.dst + (size_t)g * row;
     if (SPLIT) dst = split_dst(a.split, q, g, row, dst);
@@ -603,13 +613,16 @@ unsigned blocks_for(int64_t waves) {
 
 hipError_t launch_pack_gather(const Dims& d, const void* const x[2], const PlanPtrs& p,
                               void* const send[2], bool exchange, int32_t* status,
-                              hipStream_t stream, const PrivRegions* split = nullptr);
+                              hipStream_t stream, const PrivRegions* split = nullptr,
+                              bool windowed = false);
 bool gather_fits(const Dims& d);
 
 hipError_t launch_pack(const Dims& d, const void* const x[2], const PlanPtrs& p,
                        void* const send[2], hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
   if (gather_fits(d)) return launch_pack_gather(d, x, p, send, false, nullptr, stream);
+  if (d.win > 0)
+    return launch_pack_gather(d, x, p, send, false, nullptr, stream, nullptr, true);
   const dim3 grid(blocks_for((d.NT + 1) / 2));
   const Planes pl = make_planes(d, x, send);
   const int v0 = pass_v(d.row[0]);
@@ -667,12 +680,16 @@ hipError_t launch_pack_exchange_v(const Dims& d, const void* const x[2], const P
 
 // The send-order sender re-reads each token row R times and relies on an
 // XCD's 4 MB L2 holding the rows of the source it works on: used when one
-// source's token rows (all planes) take at most this many bytes. Measured
+// source's token rows (all planes) take at most kGatherSourceBytes. Measured
 // at H = 7168 (bf16) against the token-order sender, whole dispatch +
 // combine steps: 1.8 MB per source 90 vs 96 us (8 ranks) and 329 vs 352 us
 // (32 ranks); 3.7 MB 170 vs 182 us; 7.3 MB even; 14.7 MB 743 vs 698 us.
-constexpr int64_t kGatherSourceBytes = 4 << 20;
-
+// Larger sources take the windowed send order (d.win > 0: the rows of W
+// tokens at a time, W of them fitting kGatherSourceBytes) up to
+// kWindowSourceBytes: sender alone, 8 ranks x 1024 tokens 148-153 us
+// against 186 us in token order; 32 x 512 tokens 293-298 against 359 us.
+// Beyond that, and once the send buffers pass ~2 GB, the token-order
+// sender measured faster.
 bool gather_fits(const Dims& d) {
   int64_t bytes = 0;
   for (int q = 0; q < d.planes; ++q) bytes += d.row[q];
@@ -706,10 +723,16 @@ MovePlane move_plane(const void* src, void* dst, int64_t row, int64_t NTR) {
 
 hipError_t launch_pack_gather(const Dims& d, const void* const x[2], const PlanPtrs& p,
                               void* const send[2], bool exchange, int32_t* status,
-                              hipStream_t stream, const PrivRegions* split) {
+                              hipStream_t stream, const PrivRegions* split, bool windowed) {
   GatherArgs a{};
   if (split != nullptr) a.split = *split;
   for (int q = 0; q < d.planes; ++q) a.pl[q] = move_plane(x[q], send[q], d.row[q], d.NTR);
+  // Windowed order: plane 0's pieces walk the work list (one entry per slot
+  // of each window, padded); a plane too narrow for pieces keeps send order.
+  if (windowed && a.pl[0].pieces && p.win_list != nullptr) {
+    a.pl[0] = move_plane(x[0], send[0], d.row[0], (int64_t)d.N * d.nwin * d.win * d.R);
+    a.win_list = (const int2*)p.win_list;
+  }
   a.send_slot = p.send_slot;
   a.r_div = fast_div_of((uint32_t)d.R);
   a.NT = (int)d.NT;
@@ -756,7 +779,8 @@ hipError_t launch_recv(const Dims& d, const void* const send[2], const PlanPtrs&
 hipError_t launch_dispatch(const Dims& d, const int32_t* idx, const void* const x[2],
                            const PlanPtrs& p, void* const send[2], void* const grouped[2],
                            int32_t* status, hipStream_t stream) {
-  if (!(pack_exchange_fits(d) || (dispatch_fused_fits(d) && gather_fits(d))) || d.NT == 0) {
+  const bool gather = gather_fits(d) || d.win > 0;
+  if (!(pack_exchange_fits(d) || (dispatch_fused_fits(d) && gather)) || d.NT == 0) {
     hipError_t e = launch_plan(d, idx, p, status, stream);
     if (e == hipSuccess) e = launch_pack(d, x, p, send, stream);
     if (e == hipSuccess) e = launch_recv(d, send, p, grouped, stream);
@@ -764,8 +788,8 @@ hipError_t launch_dispatch(const Dims& d, const int32_t* idx, const void* const 
   }
   hipError_t e = launch_plan_local(d, idx, p, status, stream);
   if (e != hipSuccess) return e;
-  if (gather_fits(d)) {
-    e = launch_pack_gather(d, x, p, send, true, status, stream);
+  if (gather) {
+    e = launch_pack_gather(d, x, p, send, true, status, stream, nullptr, d.win > 0);
     if (e != hipSuccess) return e;
     return launch_recv(d, send, p, grouped, stream);
   }

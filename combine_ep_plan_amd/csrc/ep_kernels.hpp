@@ -20,12 +20,22 @@ struct Dims {
   int64_t NTR;       // slots over all ranks
   int64_t row[2];    // bytes per row of each payload plane (0 if absent)
   int nchunks;       // plan chunks per source
+  int win;           // tokens per window of the windowed sender (0: not used)
+  int nwin;          // windows per source
 };
+
+// Sender choice by the bytes of one source's token rows (all planes), from
+// gfx950 measurements (see the senders): send order up to kGatherSourceBytes
+// (the rows an XCD re-reads fit its 4 MB L2), windowed send order up to
+// kWindowSourceBytes with windows of at most kGatherSourceBytes, token order
+// beyond.
+constexpr int64_t kGatherSourceBytes = 4 << 20;
+constexpr int64_t kWindowSourceBytes = 16 << 20;
 
 // Plan workspace pointers (int32 arrays, see ep_plan_view).
 struct PlanPtrs {
   int32_t *cnt, *send_off, *send_pos, *recv_off, *grp_off, *grp_pos, *src_off,
-      *comb_row, *grp_slot, *chunk_cnt, *send_slot, *recv_rows, *send_seg;
+      *comb_row, *grp_slot, *chunk_cnt, *send_slot, *recv_rows, *send_seg, *win_list;
 };
 
 constexpr int kPlanThreads = 1024;
@@ -39,6 +49,8 @@ constexpr int64_t kFusedPlanSlots = 8192;
 
 hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                        int32_t* status, hipStream_t stream);
+// The windowed sender's work list (d.win > 0), from the send side of the plan.
+hipError_t launch_window_list(const Dims& d, const PlanPtrs& p, hipStream_t stream);
 // Split dispatch: the sender half's plan (no data of other ranks), the
 // receiver half's exchange, and the two data movers with private regions of
 // P rows per (destination, source) pair.

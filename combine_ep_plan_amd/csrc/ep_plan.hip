@@ -201,6 +201,62 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_local_kernel(
   send_tables<kPlanThreads>(e_of, rank_of, s, 0, E, L, TR, p, soff, pre, scratch, within_of);
 }
 
+// Work list of the windowed sender, block (w, s): the slots of source s's
+// tokens [w W, (w+1) W) ordered by their send row. A window's rows of one
+// expert are consecutive send rows (tokens ascend inside an expert's rows),
+// so a slot's place in the list is the window's rows of the experts before
+// its own (a histogram of the window, scanned) plus its send row minus the
+// first send row of its expert in the window. The list has W R entries per
+// window; the ones past the window's rows are (-1, -1).
+__global__ __launch_bounds__(kPlanThreads) void window_list_kernel(int E, int T, int R, int W,
+                                                                   int nwin, PlanPtrs p) {
+  extern __shared__ int32_t lds[];
+  int32_t* so = lds;                // [E+1] send_off[s]
+  int32_t* cnt = so + (E + 1);      // [E+1] rows per expert, then their exclusive prefix
+  int32_t* first = cnt + (E + 1);   // [E]   first send row of each expert in the window
+  int32_t* scratch = first + E;     // [kPlanThreads / 64]
+  const int s = blockIdx.y, w = blockIdx.x, tid = threadIdx.x;
+  const int64_t TR = (int64_t)T * R;
+  const int64_t lo = (int64_t)w * W * R;
+  const int64_t hi = lo + (int64_t)W * R < TR ? lo + (int64_t)W * R : TR;
+  for (int e = tid; e <= E; e += kPlanThreads) {
+    so[e] = p.send_off[(size_t)s * (E + 1) + e];
+    cnt[e] = 0;
+    if (e < E) first[e] = INT32_MAX;
+  }
+  __syncthreads();
+  auto expert_of = [&](int pos) {  // largest e with so[e] <= pos
+    int a = 0, b = E - 1;
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (so[mid] <= pos) a = mid; else b = mid - 1;
+    }
+    return a;
+  };
+  for (int64_t i = lo + tid; i < hi; i += kPlanThreads) {
+    const int pos = p.send_pos[(size_t)s * TR + i];
+    if (pos < 0 || pos >= so[E]) continue;
+    const int e = expert_of(pos);
+    atomicAdd(&cnt[e], 1);
+    atomicMin(&first[e], pos);
+  }
+  __syncthreads();
+  block_exclusive_scan<kPlanThreads>(cnt, E, scratch, &cnt[E]);
+  int2* list = (int2*)p.win_list + ((size_t)s * nwin + w) * W * R;
+  for (int64_t i = lo + tid; i < hi; i += kPlanThreads) {
+    const int pos = p.send_pos[(size_t)s * TR + i];
+    if (pos < 0 || pos >= so[E]) continue;
+    const int e = expert_of(pos);
+    list[cnt[e] + (pos - first[e])] =
+        make_int2((int32_t)((int64_t)s * TR + pos), (int32_t)((int64_t)s * T + i / R));
+  }
+  for (int64_t j = cnt[E] + tid; j < (int64_t)W * R; j += kPlanThreads) list[j] = make_int2(-1, -1);
+}
+
+size_t lds_window_bytes(const Dims& d) {
+  return sizeof(int32_t) * ((size_t)3 * (d.E + 1) + kPlanThreads / kWave);
+}
+
 bool fused_plan_fits(const Dims& d) {
   return d.NTR <= kFusedPlanSlots && d.E <= 1024 && d.N <= 1024;
 }
@@ -258,6 +314,13 @@ hipError_t launch_count(const Dims& d, const int32_t* idx, const PlanPtrs& p, in
 
 }  // namespace
 
+hipError_t launch_window_list(const Dims& d, const PlanPtrs& p, hipStream_t stream) {
+  if (d.win <= 0 || d.NT == 0) return hipSuccess;
+  hipLaunchKernelGGL(window_list_kernel, dim3(d.nwin, d.N), dim3(kPlanThreads),
+                     lds_window_bytes(d), stream, d.E, d.T, d.R, d.win, d.nwin, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                        int32_t* status, hipStream_t stream) {
   hipError_t e = allow_large_lds();
@@ -265,14 +328,16 @@ hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
   if (fused_plan_fits(d)) {
     hipLaunchKernelGGL(plan_fused_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
                        lds_fused_bytes(d), stream, idx, d.N, d.E, d.L, d.TR, d.cap, p, status);
-    return hipGetLastError();
+  } else {
+    e = launch_count(d, idx, p, status, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(plan_finalize_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
+                       lds_final_bytes(d), stream, idx, d.N, d.E, d.L, d.TR, d.nchunks, d.cap, p,
+                       status);
   }
-  e = launch_count(d, idx, p, status, stream);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_finalize_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
-                     lds_final_bytes(d), stream, idx, d.N, d.E, d.L, d.TR, d.nchunks, d.cap, p,
-                     status);
-  return hipGetLastError();
+  return launch_window_list(d, p, stream);
 }
 
 hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
@@ -282,13 +347,15 @@ hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& 
   if (d.nchunks == 1) {
     hipLaunchKernelGGL(plan_count_local_kernel, dim3(1, d.N), dim3(kPlanThreads),
                        lds_count_local_bytes(d), stream, idx, d.E, d.L, d.TR, p, status);
-    return hipGetLastError();
+  } else {
+    e = launch_count(d, idx, p, status, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(plan_local_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
+                       lds_final_bytes(d), stream, idx, d.E, d.L, d.TR, d.nchunks, p);
   }
-  e = launch_count(d, idx, p, status, stream);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_local_kernel, dim3(d.nchunks, d.N), dim3(kPlanThreads),
-                     lds_final_bytes(d), stream, idx, d.E, d.L, d.TR, d.nchunks, p);
-  return hipGetLastError();
+  return launch_window_list(d, p, stream);
 }
 
 hipError_t launch_plan_exchange(const Dims& d, const PlanPtrs& p, int32_t* status,

@@ -131,6 +131,15 @@ typedef struct ep_plan_view {
                                      rank and i = p - send_off[s][dL] the
                                      row's index in the segment s -> d;
                                      -1 for p >= send_off[s][E] */
+    int32_t *win_list;  /* [N][nwin][W*R][2] or NULL: the windowed sender's
+                                     work list, for sources of 4 to 16 MiB of
+                                     token rows. Window w of source s holds its
+                                     tokens [w W, (w+1) W); its entries are
+                                     the pairs (s*T*R + send_pos, s*T + t) of
+                                     the window's slots in send-row order,
+                                     then -1, -1. W is the largest power of two
+                                     with W * (row bytes of all planes)
+                                     <= 4 MiB; nwin = ceil(T / W). */
 } ep_plan_view;
 
 /* Worst-case receive rows N * T * max(R, E/N) ("Send and receive buffers");
@@ -174,7 +183,9 @@ EP_API int ep_plan_views(const ep_desc *d, void *plan_ws, ep_plan_view *v);
  *                     (the inverse of send_pos); -1 for p >= send_off[s][E];
  *   recv_rows[j]    = (s*T*R + send_pos, comb_row) of the slot grp_slot[j];
  *   send_seg[s][p]  = d*T*R + (p - send_off[s][dL]) for the rank d whose
- *                     segment holds send row p; -1 for p >= send_off[s][E].
+ *                     segment holds send row p; -1 for p >= send_off[s][E];
+ *   win_list        = the windowed sender's work list (see ep_plan_view),
+ *                     written only for sources of 4 to 16 MiB of token rows.
  * Slots with an id outside [0, E) get -1 and set EP_STATUS_BAD_EXPERT; rows
  * with grp_pos >= cap get -1 and set EP_STATUS_CAPACITY. status: device
  * int32, bits OR-ed in. Deterministic: equal inputs give equal bytes. */

@@ -10,7 +10,8 @@ import combine_ep_plan_amd as ep
 import ep_workloads as W
 
 PLAN_FIELDS = ("cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos",
-               "src_off", "comb_row", "grp_slot", "send_slot", "recv_rows", "send_seg")
+               "src_off", "comb_row", "grp_slot", "send_slot", "recv_rows", "send_seg",
+               "win_list")
 
 
 def note(msg: str) -> None:
@@ -47,19 +48,71 @@ def run_path(d: ep.Desc, b: ep.Buffers, wl: W.Workload, staged: bool = False,
     ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, stream)
 
 
+def window_of(T: int, tok_bytes: int):
+    """(W, nwin) of the windowed sender, by the rule the header states:
+    (0, 0) unless one source's token rows take more than 4 and at most
+    16 MiB; W is the largest power of two with W * tok_bytes <= 4 MiB."""
+    src = T * tok_bytes
+    if not (4 << 20 < src <= 16 << 20):
+        return 0, 0
+    w = 1
+    while 2 * w * tok_bytes <= 4 << 20:
+        w *= 2
+    return w, -(-T // w)
+
+
+def tok_bytes_of(d: ep.Desc) -> int:
+    return sum(ep.row_bytes(d, q) for q in range(ep.num_planes(d)))
+
+
+def expected_win_list(p: dict, N: int, T: int, R: int, tok_bytes: int):
+    """The windowed sender's work list from the oracle's send positions: per
+    window of W tokens, its slots in send-row order as (send row, token),
+    then (-1, -1); None when the sender is not windowed."""
+    W, nwin = window_of(T, tok_bytes)
+    if W == 0:
+        return None
+    TR = T * R
+    out = np.full((N, nwin, W * R, 2), -1, np.int64)
+    sp = p["send_pos"].reshape(N, TR).astype(np.int64)
+    for s in range(N):
+        for w in range(nwin):
+            lo, hi = w * W * R, min(TR, (w + 1) * W * R)
+            i = np.arange(lo, hi)
+            pos = sp[s, lo:hi]
+            ok = pos >= 0
+            i, pos = i[ok], pos[ok]
+            order = np.argsort(pos, kind="stable")
+            out[s, w, :len(order), 0] = s * TR + pos[order]
+            out[s, w, :len(order), 1] = s * T + i[order] // R
+    return out.reshape(-1, 2).astype(np.int32)
+
+
+def plan_fields(d: ep.Desc) -> tuple:
+    """The plan tables a descriptor has (the windowed list only when used)."""
+    if window_of(d.tokens, tok_bytes_of(d))[0]:
+        return PLAN_FIELDS
+    return tuple(f for f in PLAN_FIELDS if f != "win_list")
+
+
 def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
-    """Copy every plan table of the workspace to host numpy arrays."""
+    """Copy every plan table of the workspace to host numpy arrays (the
+    windowed sender's list only when the descriptor has one)."""
     N, T, E, R = d.n_ranks, d.tokens, d.n_experts, d.topk
     L = E // N
     shapes = {"cnt": (N, E), "send_off": (N, E + 1), "send_pos": (N, T, R),
               "recv_off": (N, N + 1), "grp_off": (N, L + 1), "grp_pos": (N, T, R),
               "src_off": (N, E), "comb_row": (N, T, R), "grp_slot": (N * T * R,),
               "send_slot": (N, T * R), "recv_rows": (N * T * R, 2), "send_seg": (N, T * R)}
+    W, nwin = window_of(T, tok_bytes_of(d))
+    shapes["win_list"] = (N * nwin * W * R, 2)
     v = ep.plan_views(d, b.plan_ws)
     base = b.plan_ws.data_ptr()
     ws = b.plan_ws.cpu().numpy()
     out = {}
     for f in PLAN_FIELDS:
+        if getattr(v, f) is None:
+            continue
         off = getattr(v, f) - base
         n = int(np.prod(shapes[f]))
         out[f] = ws[off:off + 4 * n].view(np.int32).reshape(shapes[f]).copy()

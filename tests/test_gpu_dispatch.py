@@ -10,7 +10,7 @@ import torch
 import combine_ep_plan_amd as ep
 import ep_workloads as W
 import oracle
-from gpu_util import PLAN_FIELDS, desc_of, expected_plan_extras, note, plan_arrays, upload
+from gpu_util import plan_fields, desc_of, expected_plan_extras, note, plan_arrays, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,7 @@ def compare(sh, wl, cap=0, with_oracle=True):
     torch.cuda.synchronize()
     assert int(b.status.item()) == ref_status
     got = plan_arrays(d, b)
-    for f in PLAN_FIELDS:
+    for f in plan_fields(d):
         np.testing.assert_array_equal(got[f], want[f], err_msg=f)
     so = want["send_off"]
     for q, (t, rt) in enumerate(zip(b.send, ref_send)):
@@ -88,10 +88,12 @@ SHAPES = [
     W.Shape("fp8_h7168", 4, 12, 7168, 16, 4, payload=W.PAYLOAD_FP8_B128, expert="dequant"),
     W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"),
     W.Shape("no_tokens", 2, 0, 64, 4, 2),
-    # over 4 MiB of token rows per source: the token-order sender with the
-    # exchange folded in (T R = 4096), and in the three-call form
+    # 4 to 16 MiB of token rows per source: the windowed sender with the
+    # exchange folded in (T R = 4096), and in the three-call form; over
+    # 16 MiB the token-order sender with the exchange folded in
     W.Shape("large_source_exchange", 2, 512, 4608, 16, 8),
     W.Shape("large_source_fp8", 2, 600, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128, expert="dequant"),
+    W.Shape("huge_source_exchange", 2, 2048, 4160, 4, 2),
 ]
 
 

@@ -9,7 +9,7 @@ import torch
 
 import combine_ep_plan_amd as ep
 import ep_workloads as W
-from gpu_util import PLAN_FIELDS, desc_of, note, plan_arrays, upload
+from gpu_util import plan_fields, desc_of, note, plan_arrays, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def test_graph_replays_equal_eager(name):
         torch.cuda.synchronize()
         assert int(b.status.item()) == 0
         got = plan_arrays(d, b)
-        for f in PLAN_FIELDS:
+        for f in plan_fields(d):
             np.testing.assert_array_equal(got[f], want_tables[f], err_msg=f"{f} replay {rep}")
         assert torch.equal(b.out, want_out), f"replay {rep}"
         if want_grouped is not None:

@@ -16,8 +16,8 @@ import torch
 import combine_ep_plan_amd as ep
 import ep_workloads as W
 import oracle
-from gpu_util import (bf16_close, desc_of, expected_plan_extras, note, plan_arrays,
-                      rows_of, run_path, upload)
+from gpu_util import (bf16_close, desc_of, expected_plan_extras, expected_win_list, note,
+                      plan_arrays, rows_of, run_path, tok_bytes_of, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,10 @@ def compare_full(sh, wl, cap=0, staged=False, check_closed_form=True):
         np.testing.assert_array_equal(got[f], p[f], err_msg=f)
     for f, v in expected_plan_extras(p, wl.idx, N, E, cap).items():
         np.testing.assert_array_equal(got[f], v, err_msg=f)
+    wlist = expected_win_list(p, N, T, R, tok_bytes_of(d))
+    assert (wlist is None) == ("win_list" not in got)
+    if wlist is not None:
+        np.testing.assert_array_equal(got["win_list"], wlist, err_msg="win_list")
     totals = p["recv_off"][:, N]
     for q in range(len(wl.planes)):
         send = b.send[q].cpu().numpy()
@@ -105,13 +109,18 @@ EDGE_SHAPES = [
     W.Shape("max_experts", 2, 64, 64, 2048, 16),
     W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"),
     W.Shape("zipf_mid", 16, 64, 512, 128, 6, routing="zipf", expert="scale"),
-    # Sources above 4 MiB of token rows take the token-order sender: one pass
-    # of 14 chunks per lane, the two-plane fp8 form, and the general kernel
-    # (rows over 14 KB).
+    # Sources of 4 to 16 MiB of token rows take the windowed sender (the last
+    # window partial for 600 and 300 tokens), larger ones the token-order
+    # sender: one pass of 14 chunks per lane, the two-plane fp8 form, and
+    # the general kernel (rows over 14 KB).
     W.Shape("large_source_bf16", 2, 512, 4608, 16, 8, expert="scale"),
     W.Shape("large_source_fp8", 2, 600, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128,
             expert="dequant"),
     W.Shape("large_source_wide_row", 2, 300, 8192, 4, 2),
+    W.Shape("huge_source_bf16", 2, 2400, 4096, 16, 8, expert="scale"),
+    W.Shape("huge_source_fp8", 2, 2400, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128,
+            expert="dequant"),
+    W.Shape("huge_source_wide_row", 2, 1100, 8192, 4, 2),
 ]
 
 
@@ -133,6 +142,21 @@ def _bad_and_tight():
     idx[1, 5, 2] = -3
     idx[3, 31, 1] = 1 << 20
     return sh, W.make_workload(sh, idx=idx)
+
+
+def test_windowed_sender_with_bad_ids_and_tight_capacity():
+    """Dropped slots leave gaps in a window's list; a tight capacity drops
+    rows on the receive side only."""
+    sh = W.Shape("window_bad", 2, 600, 4608, 16, 8, expert="scale", seed=5)
+    wl = W.make_workload(sh)
+    idx = wl.idx.copy()
+    rng = np.random.default_rng(7)
+    bad = rng.random(idx.shape) < 0.02
+    idx[bad] = rng.choice([-1, 16, 99], size=int(bad.sum()))
+    wl = W.make_workload(sh, idx=idx)
+    full = oracle.plan(2, 600, 16, 8, oracle.recv_bound(2, 600, 16, 8), idx)
+    cap = int(full["recv_off"][:, 2].max()) - 3
+    compare_full(sh, wl, cap=cap)
 
 
 def test_bad_expert_ids_are_dropped_and_flagged():

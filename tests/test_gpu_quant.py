@@ -148,7 +148,7 @@ def test_pack_quant_full_size(name):
 def test_dispatch_quant_equals_three_calls(sh):
     """ep_dispatch_quant == ep_plan + ep_dispatch_pack_quant + ep_dispatch_recv:
     plan tables, send planes and delivered grouped rows."""
-    from gpu_util import PLAN_FIELDS
+    from gpu_util import plan_fields
     wl = W.make_workload(sh)
     d = desc_of(sh)
     cap = ep.capacity(d)
@@ -177,7 +177,7 @@ def test_dispatch_quant_equals_three_calls(sh):
     torch.cuda.synchronize()
     assert int(b.status.item()) == 0
     got = plan_arrays(d, b)
-    for f in PLAN_FIELDS:
+    for f in plan_fields(d):
         np.testing.assert_array_equal(got[f], want[f], err_msg=f)
     for t, rt in zip(b.send, ref_send):
         assert torch.equal(t, rt)

@@ -15,7 +15,7 @@ import torch
 import combine_ep_plan_amd as ep
 import ep_workloads as W
 import oracle
-from gpu_util import (PLAN_FIELDS, bf16_close, desc_of, expected_plan_extras, note,
+from gpu_util import (plan_fields, bf16_close, desc_of, expected_plan_extras, note,
                       plan_arrays, run_path, upload)
 
 pytestmark = pytest.mark.gpu
@@ -59,7 +59,7 @@ def check_split(sh, wl, P, cap=0):
     torch.cuda.synchronize()
     assert int(b.status.item()) == int(ref_b.status.item())
     got, want = plan_arrays(d, b), plan_arrays(d, ref_b)
-    for f in PLAN_FIELDS:
+    for f in plan_fields(d):
         np.testing.assert_array_equal(got[f], want[f], err_msg=f)
     p = oracle.plan(N, T, E, R, cap, wl.idx)
     assert int(b.status.item()) == p["status"]
@@ -150,7 +150,7 @@ def test_independent_work_between_halves_on_another_stream():
 
     run_split(d, b, wl, 2, stream=sa, between=between)
     torch.cuda.synchronize()
-    for f in PLAN_FIELDS:
+    for f in plan_fields(d):
         np.testing.assert_array_equal(plan_arrays(d, b)[f], plan_arrays(d, ref_b)[f], err_msg=f)
     assert torch.equal(b.out, ref_b.out)
     assert torch.equal(res["c"], c_ref)
@@ -181,7 +181,7 @@ def test_two_micro_batches_interleaved():
     torch.cuda.synchronize()
     for b, rb in zip(bs, refs):
         assert int(b.status.item()) == 0
-        for f in PLAN_FIELDS:
+        for f in plan_fields(d):
             np.testing.assert_array_equal(plan_arrays(d, b)[f], plan_arrays(d, rb)[f], err_msg=f)
         assert torch.equal(b.out, rb.out)
 
@@ -226,7 +226,7 @@ def test_split_full_size(name, P):
     torch.cuda.synchronize()
     assert int(b.status.item()) == 0
     got = plan_arrays(d, b)
-    for f in PLAN_FIELDS:
+    for f in plan_fields(d):
         np.testing.assert_array_equal(got[f], want[f], err_msg=f)
     for g, rg in zip(b.grouped, ref_grouped):
         for dd in range(N):
@@ -282,7 +282,7 @@ def test_exchange_overlapped_with_pack_equals_unsplit(name, P):
     run_overlapped(d, b, wl, P, sa, sb)
     assert int(b.status.item()) == 0
     got = plan_arrays(d, b)
-    for f in PLAN_FIELDS:
+    for f in plan_fields(d):
         np.testing.assert_array_equal(got[f], want[f], err_msg=f)
     for g, rg in zip(b.grouped, ref_grouped):
         for dd in range(N):
