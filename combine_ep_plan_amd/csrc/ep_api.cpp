@@ -88,7 +88,8 @@ int derive(const ep_desc* d, ep::Dims* o) {
   const int64_t src_bytes = (int64_t)d->tokens * tok_bytes;
   o->win = 0;
   o->nwin = 0;
-  if (src_bytes > ep::kGatherSourceBytes && src_bytes <= ep::kWindowSourceBytes) {
+  if (src_bytes > ep::kGatherSourceBytes && src_bytes <= ep::kWindowSourceBytes &&
+      NTR * tok_bytes <= ep::kWindowSendBytes) {
     int64_t w = 1;
     while (2 * w * tok_bytes <= ep::kGatherSourceBytes) w *= 2;
     o->win = (int)w;

@@ -686,10 +686,11 @@ hipError_t launch_pack_exchange_v(const Dims& d, const void* const x[2], const P
 // (32 ranks); 3.7 MB 170 vs 182 us; 7.3 MB even; 14.7 MB 743 vs 698 us.
 // Larger sources take the windowed send order (d.win > 0: the rows of W
 // tokens at a time, W of them fitting kGatherSourceBytes) up to
-// kWindowSourceBytes: sender alone, 8 ranks x 1024 tokens 148-153 us
-// against 186 us in token order; 32 x 512 tokens 293-298 against 359 us.
-// Beyond that, and once the send buffers pass ~2 GB, the token-order
-// sender measured faster.
+// kWindowSourceBytes per source and kWindowSendBytes of send buffers:
+// sender alone, 8 ranks x 1024 tokens 148-153 us against 186 us in token
+// order; 32 x 512 tokens 293-298 against 359 us; 8 x 2048 tokens 298
+// against 360 us. With send buffers past ~2 GB (8 x 3072 tokens, 2.8 GB)
+// the token-order sender measured faster (637 against 707 us).
 bool gather_fits(const Dims& d) {
   int64_t bytes = 0;
   for (int q = 0; q < d.planes; ++q) bytes += d.row[q];

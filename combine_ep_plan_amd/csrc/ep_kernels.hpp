@@ -24,13 +24,15 @@ struct Dims {
   int nwin;          // windows per source
 };
 
-// Sender choice by the bytes of one source's token rows (all planes), from
-// gfx950 measurements (see the senders): send order up to kGatherSourceBytes
-// (the rows an XCD re-reads fit its 4 MB L2), windowed send order up to
-// kWindowSourceBytes with windows of at most kGatherSourceBytes, token order
-// beyond.
+// Sender choice by the bytes of one source's token rows (all planes) and of
+// all send buffers, from gfx950 measurements (see the senders): send order
+// up to kGatherSourceBytes per source (the rows an XCD re-reads fit its 4 MB
+// L2); windowed send order, windows of at most kGatherSourceBytes, up to
+// kWindowSourceBytes per source while the send buffers take at most
+// kWindowSendBytes; token order beyond.
 constexpr int64_t kGatherSourceBytes = 4 << 20;
-constexpr int64_t kWindowSourceBytes = 16 << 20;
+constexpr int64_t kWindowSourceBytes = 32 << 20;
+constexpr int64_t kWindowSendBytes = (int64_t)2 << 30;
 
 // Plan workspace pointers (int32 arrays, see ep_plan_view).
 struct PlanPtrs {
@@ -47,15 +49,17 @@ constexpr int kPlanChunk = kPlanThreads * kPlanSub;      // slots per block
 // costs more than the second launch.
 constexpr int64_t kFusedPlanSlots = 8192;
 
+// with_window: also build the windowed sender's work list (when the
+// descriptor has one); the quantising sender does not use it.
 hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
-                       int32_t* status, hipStream_t stream);
+                       int32_t* status, hipStream_t stream, bool with_window = true);
 // The windowed sender's work list (d.win > 0), from the send side of the plan.
 hipError_t launch_window_list(const Dims& d, const PlanPtrs& p, hipStream_t stream);
 // Split dispatch: the sender half's plan (no data of other ranks), the
 // receiver half's exchange, and the two data movers with private regions of
 // P rows per (destination, source) pair.
 hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
-                             int32_t* status, hipStream_t stream);
+                             int32_t* status, hipStream_t stream, bool with_window = true);
 hipError_t launch_plan_exchange(const Dims& d, const PlanPtrs& p, int32_t* status,
                                 hipStream_t stream);
 hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* const x[2],

@@ -322,7 +322,7 @@ hipError_t launch_window_list(const Dims& d, const PlanPtrs& p, hipStream_t stre
 }
 
 hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
-                       int32_t* status, hipStream_t stream) {
+                       int32_t* status, hipStream_t stream, bool with_window) {
   hipError_t e = allow_large_lds();
   if (e != hipSuccess) return e;
   if (fused_plan_fits(d)) {
@@ -336,12 +336,12 @@ hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                        status);
   }
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !with_window) return e;
   return launch_window_list(d, p, stream);
 }
 
 hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
-                             int32_t* status, hipStream_t stream) {
+                             int32_t* status, hipStream_t stream, bool with_window) {
   hipError_t e = allow_large_lds();
   if (e != hipSuccess) return e;
   if (d.nchunks == 1) {
@@ -354,7 +354,7 @@ hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& 
                        lds_final_bytes(d), stream, idx, d.E, d.L, d.TR, d.nchunks, p);
   }
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !with_window) return e;
   return launch_window_list(d, p, stream);
 }
 

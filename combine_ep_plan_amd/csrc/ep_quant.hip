@@ -220,12 +220,12 @@ hipError_t launch_dispatch_quant(const Dims& d, const int32_t* idx, const uint16
                                  const PlanPtrs& p, void* const send[2], void* const grouped[2],
                                  int32_t* status, hipStream_t stream) {
   if (!dispatch_fused_fits(d) || d.NT == 0) {
-    hipError_t e = launch_plan(d, idx, p, status, stream);
+    hipError_t e = launch_plan(d, idx, p, status, stream, false);
     if (e == hipSuccess) e = launch_pack_quant(d, x, p, send, stream);
     if (e == hipSuccess) e = launch_recv(d, send, p, grouped, stream);
     return e;
   }
-  hipError_t e = launch_plan_local(d, idx, p, status, stream);
+  hipError_t e = launch_plan_local(d, idx, p, status, stream, false);
   if (e != hipSuccess) return e;
   const int nseg = (d.H / 8 + kQSeg - 1) / kQSeg;
   if (nseg <= kTokWaves) {

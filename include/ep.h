@@ -132,8 +132,9 @@ typedef struct ep_plan_view {
                                      row's index in the segment s -> d;
                                      -1 for p >= send_off[s][E] */
     int32_t *win_list;  /* [N][nwin][W*R][2] or NULL: the windowed sender's
-                                     work list, for sources of 4 to 16 MiB of
-                                     token rows. Window w of source s holds its
+                                     work list, for sources of 4 to 32 MiB of
+                                     token rows while all send buffers take at
+                                     most 2 GiB. Window w of source s holds its
                                      tokens [w W, (w+1) W); its entries are
                                      the pairs (s*T*R + send_pos, s*T + t) of
                                      the window's slots in send-row order,
@@ -185,7 +186,7 @@ EP_API int ep_plan_views(const ep_desc *d, void *plan_ws, ep_plan_view *v);
  *   send_seg[s][p]  = d*T*R + (p - send_off[s][dL]) for the rank d whose
  *                     segment holds send row p; -1 for p >= send_off[s][E];
  *   win_list        = the windowed sender's work list (see ep_plan_view),
- *                     written only for sources of 4 to 16 MiB of token rows.
+ *                     written only when the descriptor has one.
  * Slots with an id outside [0, E) get -1 and set EP_STATUS_BAD_EXPERT; rows
  * with grp_pos >= cap get -1 and set EP_STATUS_CAPACITY. status: device
  * int32, bits OR-ed in. Deterministic: equal inputs give equal bytes. */
@@ -253,7 +254,8 @@ EP_API int ep_dispatch(const ep_desc *d, const int32_t *topk_idx,
 
 /* ep_dispatch with the quantising sender: ep_plan, ep_dispatch_pack_quant
  * and ep_dispatch_recv in one call (x: bf16 [N][T][H]; fp8 descriptor),
- * with the same results and the same launch saving. */
+ * with the same results and the same launch saving, except that win_list
+ * (the plain sender's work list) is not written. */
 EP_API int ep_dispatch_quant(const ep_desc *d, const int32_t *topk_idx,
                              const uint16_t *x, void *plan_ws,
                              void *const send[2], void *const grouped[2],

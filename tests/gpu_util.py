@@ -48,12 +48,13 @@ def run_path(d: ep.Desc, b: ep.Buffers, wl: W.Workload, staged: bool = False,
     ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, stream)
 
 
-def window_of(T: int, tok_bytes: int):
+def window_of(N: int, T: int, R: int, tok_bytes: int):
     """(W, nwin) of the windowed sender, by the rule the header states:
     (0, 0) unless one source's token rows take more than 4 and at most
-    16 MiB; W is the largest power of two with W * tok_bytes <= 4 MiB."""
+    32 MiB and all send buffers at most 2 GiB; W is the largest power of two
+    with W * tok_bytes <= 4 MiB."""
     src = T * tok_bytes
-    if not (4 << 20 < src <= 16 << 20):
+    if not (4 << 20 < src <= 32 << 20) or N * T * R * tok_bytes > 2 << 30:
         return 0, 0
     w = 1
     while 2 * w * tok_bytes <= 4 << 20:
@@ -69,7 +70,7 @@ def expected_win_list(p: dict, N: int, T: int, R: int, tok_bytes: int):
     """The windowed sender's work list from the oracle's send positions: per
     window of W tokens, its slots in send-row order as (send row, token),
     then (-1, -1); None when the sender is not windowed."""
-    W, nwin = window_of(T, tok_bytes)
+    W, nwin = window_of(N, T, R, tok_bytes)
     if W == 0:
         return None
     TR = T * R
@@ -90,7 +91,7 @@ def expected_win_list(p: dict, N: int, T: int, R: int, tok_bytes: int):
 
 def plan_fields(d: ep.Desc) -> tuple:
     """The plan tables a descriptor has (the windowed list only when used)."""
-    if window_of(d.tokens, tok_bytes_of(d))[0]:
+    if window_of(d.n_ranks, d.tokens, d.topk, tok_bytes_of(d))[0]:
         return PLAN_FIELDS
     return tuple(f for f in PLAN_FIELDS if f != "win_list")
 
@@ -104,7 +105,7 @@ def plan_arrays(d: ep.Desc, b: ep.Buffers) -> dict:
               "recv_off": (N, N + 1), "grp_off": (N, L + 1), "grp_pos": (N, T, R),
               "src_off": (N, E), "comb_row": (N, T, R), "grp_slot": (N * T * R,),
               "send_slot": (N, T * R), "recv_rows": (N * T * R, 2), "send_seg": (N, T * R)}
-    W, nwin = window_of(T, tok_bytes_of(d))
+    W, nwin = window_of(N, T, R, tok_bytes_of(d))
     shapes["win_list"] = (N * nwin * W * R, 2)
     v = ep.plan_views(d, b.plan_ws)
     base = b.plan_ws.data_ptr()

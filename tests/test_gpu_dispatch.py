@@ -88,12 +88,12 @@ SHAPES = [
     W.Shape("fp8_h7168", 4, 12, 7168, 16, 4, payload=W.PAYLOAD_FP8_B128, expert="dequant"),
     W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"),
     W.Shape("no_tokens", 2, 0, 64, 4, 2),
-    # 4 to 16 MiB of token rows per source: the windowed sender with the
+    # 4 to 32 MiB of token rows per source: the windowed sender with the
     # exchange folded in (T R = 4096), and in the three-call form; over
-    # 16 MiB the token-order sender with the exchange folded in
+    # 32 MiB the token-order sender with the exchange folded in
     W.Shape("large_source_exchange", 2, 512, 4608, 16, 8),
     W.Shape("large_source_fp8", 2, 600, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128, expert="dequant"),
-    W.Shape("huge_source_exchange", 2, 2048, 4160, 4, 2),
+    W.Shape("huge_source_exchange", 2, 4096, 4160, 4, 1),
 ]
 
 

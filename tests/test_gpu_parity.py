@@ -109,7 +109,7 @@ EDGE_SHAPES = [
     W.Shape("max_experts", 2, 64, 64, 2048, 16),
     W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"),
     W.Shape("zipf_mid", 16, 64, 512, 128, 6, routing="zipf", expert="scale"),
-    # Sources of 4 to 16 MiB of token rows take the windowed sender (the last
+    # Sources of 4 to 32 MiB of token rows take the windowed sender (the last
     # window partial for 600 and 300 tokens), larger ones the token-order
     # sender: one pass of 14 chunks per lane, the two-plane fp8 form, and
     # the general kernel (rows over 14 KB).
@@ -117,10 +117,10 @@ EDGE_SHAPES = [
     W.Shape("large_source_fp8", 2, 600, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128,
             expert="dequant"),
     W.Shape("large_source_wide_row", 2, 300, 8192, 4, 2),
-    W.Shape("huge_source_bf16", 2, 2400, 4096, 16, 8, expert="scale"),
-    W.Shape("huge_source_fp8", 2, 2400, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128,
+    W.Shape("huge_source_bf16", 2, 4200, 4096, 16, 4, expert="scale"),
+    W.Shape("huge_source_fp8", 2, 4600, 7168, 16, 4, payload=W.PAYLOAD_FP8_B128,
             expert="dequant"),
-    W.Shape("huge_source_wide_row", 2, 1100, 8192, 4, 2),
+    W.Shape("huge_source_wide_row", 2, 2100, 8192, 4, 2),
 ]
 
 

@@ -178,6 +178,8 @@ def test_dispatch_quant_equals_three_calls(sh):
     assert int(b.status.item()) == 0
     got = plan_arrays(d, b)
     for f in plan_fields(d):
+        if f == "win_list":   # the plain sender's list: not written here
+            continue
         np.testing.assert_array_equal(got[f], want[f], err_msg=f)
     for t, rt in zip(b.send, ref_send):
         assert torch.equal(t, rt)
