@@ -143,8 +143,16 @@ def test_pack_quant_full_size(name):
         assert bf16_close(out[i], want).all()
 
 
-@pytest.mark.parametrize("sh", QUANT_SHAPES + [W.CONFIGS["decode_fp8"], W.CONFIGS["prefill"]],
-                         ids=[s.name for s in QUANT_SHAPES] + ["decode_fp8", "prefill"])
+# 4.4 MB of token rows per source: a descriptor with a windowed plain
+# sender, whose list the quantising dispatch does not build
+WINDOWED_FP8 = W.Shape("q_window", 2, 600, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128,
+                       expert="dequant", seed=8)
+
+
+@pytest.mark.parametrize("sh", QUANT_SHAPES + [WINDOWED_FP8, W.CONFIGS["decode_fp8"],
+                                               W.CONFIGS["prefill"]],
+                         ids=[s.name for s in QUANT_SHAPES] + ["window", "decode_fp8",
+                                                                "prefill"])
 def test_dispatch_quant_equals_three_calls(sh):
     """ep_dispatch_quant == ep_plan + ep_dispatch_pack_quant + ep_dispatch_recv:
     plan tables, send planes and delivered grouped rows."""
@@ -186,3 +194,4 @@ def test_dispatch_quant_equals_three_calls(sh):
     for g, rg in zip(b.grouped, ref_grouped):
         for dd in range(N):
             assert torch.equal(g[dd, :rows[dd]], rg[dd]), f"grouped {dd}"
+
