@@ -836,9 +836,9 @@ hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* cons
                              hipStream_t stream) {
   if (d.NT == 0) return hipSuccess;
   if (P == 0) return launch_pack(d, x, p, send, stream);  // no private rows: the plain sender
-  if (gather_fits(d)) {
+  if (gather_fits(d) || d.win > 0) {
     const PrivRegions v = make_priv(d, priv, P, p);
-    return launch_pack_gather(d, x, p, send, false, nullptr, stream, &v);
+    return launch_pack_gather(d, x, p, send, false, nullptr, stream, &v, d.win > 0);
   }
   hipLaunchKernelGGL(pack_split_kernel, dim3(blocks_for((d.NT + 1) / 2)), dim3(kBlock), 0, stream,
                      make_planes(d, x, send), make_split(d, priv, P, p), idx, p.send_pos,

@@ -103,7 +103,8 @@ SPLIT_SHAPES = [
     (W.Shape("max_experts", 2, 64, 64, 2048, 16), 9),
     (W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"), 1),
     (W.Shape("no_tokens", 2, 0, 64, 4, 2), 0),
-    (W.Shape("large_source", 2, 512, 4608, 16, 8), 5),           # token-order split sender
+    (W.Shape("large_source", 2, 512, 4608, 16, 8), 5),           # windowed split sender
+    (W.Shape("huge_source", 2, 4200, 4096, 16, 4), 3),           # token-order split sender
 ]
 
 
