@@ -427,7 +427,7 @@ def main() -> int:
                     help="fp8 payloads: send pre-quantised rows with the plain sender "
                          "instead of quantising bf16 rows in the sender")
     ap.add_argument("--flushed-steps", type=int, default=20,
-                    help="extra steps, each after a 1 GiB copy that evicts the caches, "
+                    help="extra steps, each after a 1 GiB fill and a 1 GiB read that evict the caches, "
                          "timed one by one (reported beside the main figure)")
     ap.add_argument("--split", type=int, default=-1, metavar="P",
                     help="also measure the split dispatch with P private rows per "
@@ -631,12 +631,17 @@ def main() -> int:
     torch.cuda.synchronize()
     copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
-    # Cold-cache steps: before each one, a 1 GiB copy (outside the events)
-    # evicts what the previous step left in the L2s and the MALL; each step is
-    # timed alone between two events.
+    # Cold-cache steps: before each one (outside the events) a 1 GiB fill and
+    # a 1 GiB read with ordinary stores and loads evict what the previous step
+    # left in the L2s and the MALL. (The library's copy probe would not: its
+    # non-temporal accesses leave cached lines in place, and so do the
+    # receiver's and the combine's, which is why back-to-back steps find the
+    # previous sender's token rows still in each XCD's L2.) Each step is timed
+    # alone between two events.
     flushed = []
     for i in range(args.flushed_steps):
-        ep.probe_copy(dst, src, nbytes, sp)
+        dst.fill_(i & 0xff)
+        src.view(torch.int32).max()
         f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         f0.record(stream)
         step()
