@@ -117,6 +117,10 @@ EDGE_SHAPES = [
     W.Shape("large_source_fp8", 2, 600, 7168, 16, 8, payload=W.PAYLOAD_FP8_B128,
             expert="dequant"),
     W.Shape("large_source_wide_row", 2, 300, 8192, 4, 2),
+    # windowed with 2048 experts (the list kernel scans more entries than it
+    # has threads) and with skewed routing (experts empty inside a window)
+    W.Shape("large_source_max_experts", 2, 600, 4608, 2048, 8),
+    W.Shape("large_source_zipf", 4, 400, 7168, 64, 6, routing="zipf", expert="scale", seed=9),
     W.Shape("huge_source_bf16", 2, 4200, 4096, 16, 4, expert="scale"),
     W.Shape("huge_source_fp8", 2, 4600, 7168, 16, 4, payload=W.PAYLOAD_FP8_B128,
             expert="dequant"),
