@@ -243,8 +243,8 @@ EP_API int ep_dispatch_recv(const ep_desc *d, const void *const send[2],
 
 /* The whole dispatch in one call: ep_plan, ep_dispatch_pack and
  * ep_dispatch_recv, with identical results (plan_ws tables, send, grouped,
- * status). When a source's T R slots fit one plan chunk (4096) and E <= 512,
- * it takes three launches instead of four: the send side of the plan, then
+ * status). When a source's T R slots fit one plan chunk (4096), E <= 512 and
+ * N <= 1024, it takes three launches instead of four: the send side of the plan, then
  * the sender with the count exchange ("Send and receive buffers") done by
  * extra blocks of the same launch, then the receiver. */
 EP_API int ep_dispatch(const ep_desc *d, const int32_t *topk_idx,
@@ -362,8 +362,9 @@ EP_API int64_t ep_kv_plan(int64_t n_tokens, int64_t token_bytes,
  * r * dst_rank_bytes. regions: device array [n_regions] from ep_kv_plan;
  * total_bytes: their byte sum (a multiple of 16). notify: device int32 the
  * caller zeroes; each rank adds 1 once all its bytes are written (in stream
- * order after the copy), so the request has arrived when notify == ranks. A region that does not fit its pools (or is
- * not 16-byte aligned) is skipped and sets EP_STATUS_BAD_REGION in status. */
+ * order after the copy), so the request has arrived when notify == ranks.
+ * A region that does not fit its pools (or is not 16-byte aligned) is
+ * skipped and sets EP_STATUS_BAD_REGION in status. */
 EP_API int ep_kv_push(int32_t ranks, const ep_kv_region *regions,
                       int64_t n_regions, int64_t total_bytes,
                       const void *src_pool, int64_t src_rank_bytes,
@@ -423,8 +424,10 @@ EP_API int ep_combine_presum(const ep_desc *d, const uint16_t *expert_out,
                              hipStream_t stream);
 
 /* Copy `bytes` (a multiple of 16) from src to dst with the library's row
- * copy loop: a bandwidth reference for measurements, not part of the
- * method. */
+ * copy loop (non-temporal loads and stores, 7 KB per wave): a bandwidth
+ * reference for measurements, not part of the method. Its non-temporal
+ * accesses leave lines other kernels cached in place, so it does not serve
+ * to evict the caches. */
 EP_API int ep_probe_copy(void *dst, const void *src, size_t bytes,
                   hipStream_t stream);
 
