@@ -224,6 +224,13 @@ __device__ __forceinline__ int fast_div(int n, FastDiv f) {
 //   - the sender so takes 73 us against 99 us for the token-order sender
 //     (one wave per token pair, R stores per row); 2 KB and 7 KB pieces per
 //     wave took 76 and 78 us.
+// Those figures are for back-to-back steps, where each XCD's L2 still holds
+// token rows of the previous step (the receiver and the combine access
+// memory non-temporally and leave them). After a pass that evicts the
+// caches the token rows' first reads come from HBM: 119 us against 104 us
+// for the token-order sender, while whole steps (dispatch and combine) stay
+// ahead, 346 against 352 us. Extra waves that pre-read each source's rows
+// before its range recovered 14 us of that step but cost 6 us back to back.
 // The fp8 scale plane (rows of H/32 bytes) is too narrow for pieces: there
 // each lane moves one unit (16 bytes, or 4 when the row is not a multiple of
 // 16) of the plane's rows in address order, so every wave writes whole lines.
