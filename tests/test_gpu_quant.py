@@ -49,6 +49,11 @@ QUANT_SHAPES = [
             expert="dequant", seed=5),
     W.Shape("q_rank0", 8, 8, 512, 32, 8, routing="rank0", payload=W.PAYLOAD_FP8_B128,
             expert="dequant", seed=6),
+    # rows of more than 8 segments of 1024 values: the wave-per-segment
+    # senders instead of the workgroup-per-token one (ragged last segment)
+    W.Shape("q_wide", 3, 6, 8320, 12, 3, payload=W.PAYLOAD_FP8_B128, expert="dequant", seed=10),
+    W.Shape("q_wide16k", 2, 5, 16384, 8, 2, payload=W.PAYLOAD_FP8_B128, expert="dequant",
+            seed=11),
 ]
 
 
