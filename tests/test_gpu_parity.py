@@ -109,6 +109,9 @@ EDGE_SHAPES = [
     W.Shape("max_experts", 2, 64, 64, 2048, 16),
     W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"),
     W.Shape("zipf_mid", 16, 64, 512, 128, 6, routing="zipf", expert="scale"),
+    # 16800 tokens: the combine's many-token shape (7 waves per token), with
+    # ragged 400-byte rows and a multi-chunk plan, compared in full
+    W.Shape("many_tokens_ragged", 4, 4200, 200, 16, 3, expert="scale", seed=6),
     # Sources of 4 to 32 MiB of token rows take the windowed sender (the last
     # window partial for 600 and 300 tokens), larger ones the token-order
     # sender: one pass of 14 chunks per lane, the two-plane fp8 form, and
