@@ -136,3 +136,34 @@ def test_oracle_and_library_share_nothing():
         assert "oracle" not in text.lower(), f
     pkg = open(os.path.join(ROOT, "combine_ep_plan_amd", "__init__.py")).read()
     assert "import oracle" not in pkg and "from oracle" not in pkg
+
+
+# (N, T, H, R, payload) -> (W, nwin) by the rule the header states for the
+# windowed sender: more than 4 and at most 32 MiB of token rows per source,
+# all send buffers at most 2 GiB, W the largest power of two whose rows fit
+# 4 MiB. bf16 H = 2048 gives 4 KiB rows.
+WINDOW_CASES = [
+    ((2, 1024, 2048, 2, 0), (0, 0)),          # exactly 4 MiB per source
+    ((2, 1025, 2048, 2, 0), (1024, 2)),       # one row more
+    ((2, 8192, 2048, 2, 0), (1024, 8)),       # exactly 32 MiB
+    ((2, 8193, 2048, 2, 0), (0, 0)),          # one row more
+    ((63, 1025, 2048, 8, 0), (1024, 2)),      # send buffers just under 2 GiB
+    ((64, 1025, 2048, 8, 0), (0, 0)),         # just over
+    ((2, 600, 7168, 8, 1), (512, 2)),         # fp8: 7168 + 224 bytes per token
+]
+
+
+@pytest.mark.parametrize("args,want", WINDOW_CASES)
+def test_window_list_view_follows_the_stated_rule(args, want):
+    N, T, H, R, payload = args
+    d = ep.make_desc(N, T, H, 16 * N, R, payload)
+    base = 1 << 30
+    v = ep.plan_views(d, base)
+    W_, nwin = want
+    if W_ == 0:
+        assert not v.win_list
+        return
+    assert v.win_list and (v.win_list - base) % 256 == 0
+    NTR = N * T * R
+    assert v.win_list >= v.send_seg + 4 * NTR           # after the last table
+    assert ep.plan_bytes(d) >= v.win_list - base + 8 * N * nwin * W_ * R
