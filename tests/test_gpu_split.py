@@ -126,6 +126,23 @@ def test_split_bad_ids_and_capacity():
     assert int(b.status.item()) == ep.EP_STATUS_BAD_EXPERT | ep.EP_STATUS_CAPACITY
 
 
+def test_split_windowed_sender_with_bad_ids_and_tight_capacity():
+    """The windowed sender with private regions: dropped slots leave gaps in
+    the window lists, and rows past a tight capacity are dropped on the
+    receive side."""
+    sh = W.Shape("window_bad_split", 2, 600, 4608, 16, 8, expert="scale", seed=5)
+    wl = W.make_workload(sh)
+    idx = wl.idx.copy()
+    rng = np.random.default_rng(8)
+    bad = rng.random(idx.shape) < 0.02
+    idx[bad] = rng.choice([-1, 16, 99], size=int(bad.sum()))
+    wl = W.make_workload(sh, idx=idx)
+    full = oracle.plan(2, 600, 16, 8, oracle.recv_bound(2, 600, 16, 8), idx)
+    cap = int(full["recv_off"][:, 2].max()) - 3
+    d, b = check_split(sh, wl, 5, cap=cap)
+    assert int(b.status.item()) == ep.EP_STATUS_BAD_EXPERT | ep.EP_STATUS_CAPACITY
+
+
 def test_independent_work_between_halves_on_another_stream():
     """The sender half on stream A, a GEMM that does not depend on it on
     stream B while A goes on to the receiver half: same results."""
