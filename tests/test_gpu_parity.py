@@ -107,6 +107,7 @@ EDGE_SHAPES = [
     W.Shape("fp8_dword_scales", 2, 9, 256, 8, 2, payload=W.PAYLOAD_FP8_B128, expert="dequant"),
     W.Shape("fp8_h1024", 4, 12, 1024, 16, 4, payload=W.PAYLOAD_FP8_B128, expert="dequant"),
     W.Shape("max_experts", 2, 64, 64, 2048, 16),
+    W.Shape("max_topk", 2, 8, 64, 128, 64, expert="scale", seed=3),   # EP_MAX_TOPK
     W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"),
     W.Shape("zipf_mid", 16, 64, 512, 128, 6, routing="zipf", expert="scale"),
     # 16800 tokens: the combine's many-token shape (7 waves per token), with

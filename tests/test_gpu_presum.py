@@ -44,6 +44,7 @@ PRESUM_SHAPES = [
     W.Shape("rank0_repeated_ids", 8, 8, 64, 32, 8, routing="rank0"),
     W.Shape("few_ranks_many_choices", 2, 40, 512, 16, 6, expert="scale", seed=8),
     W.Shape("max_experts", 2, 64, 64, 2048, 16),
+    W.Shape("max_topk", 2, 8, 64, 128, 64, expert="scale", seed=3),
     W.Shape("many_ranks", 128, 4, 64, 128, 4, routing="zipf"),
     W.Shape("zipf_mid", 16, 64, 512, 128, 6, routing="zipf", expert="scale"),
     W.Shape("fp8_h1024", 4, 12, 1024, 16, 4, payload=W.PAYLOAD_FP8_B128, expert="dequant"),
