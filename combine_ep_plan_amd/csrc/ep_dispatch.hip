@@ -18,9 +18,10 @@
 //     store-heavy copies (a fill writes 6.8 TB/s with 1 KB per wave against
 //     5.3 TB/s with 14 KB). Each wave needs one or two table loads to find
 //     its rows.
-//   - whole rows per token pair (the token-order senders, for sources whose
-//     token rows do not fit an XCD's L2): one wave loads two token rows and
-//     writes each to its R send rows.
+//   - whole rows per token pair (the token-order senders, for sources of
+//     more than 32 MiB of token rows or send buffers of more than 2 GiB; in
+//     between, the send-order sender walks windows of tokens): one wave
+//     loads two token rows and writes each to its R send rows.
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 #include "ep_plan_device.hpp"
