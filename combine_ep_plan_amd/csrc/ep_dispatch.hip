@@ -441,7 +441,9 @@ __device__ __forceinline__ int64_t staged_row(const StagedArgs& a, int g) {
 }
 
 // TRANSFER: the network write, in send order (wave w: piece of send row
-// w / per_row). Otherwise the receiver shuffle, in receive order (recv_rows).
+// w / per_row). Otherwise the receiver shuffle, in receive order
+// (recv_rows); a delivered grouped row whose receive-buffer row was dropped
+// (at or beyond cap) is written as zeros, so it holds no stale bytes.
 template <bool TRANSFER>
 __device__ __forceinline__ void staged_wave(const StagedArgs& a, const MovePlane& pl, int w) {
   if (pl.pieces) {
@@ -458,10 +460,13 @@ __device__ __forceinline__ void staged_wave(const StagedArgs& a, const MovePlane
       from = staged_row(a, g);
       to = wave_uniform(r.y);
     }
-    if (from < 0 || to < 0) return;
+    if (to < 0 || (TRANSFER && from < 0)) return;
     const size_t row = (size_t)pl.n16 * 16;
     RowRegs<1> v;
-    load_row16<1, true>(v, (const u32x4*)(pl.src + (size_t)from * row), base, pl.n16);
+    if (from >= 0)
+      load_row16<1, true>(v, (const u32x4*)(pl.src + (size_t)from * row), base, pl.n16);
+    else
+      v.v[0] = u32x4{0u, 0u, 0u, 0u};
     store_row16(v, (u32x4*)(pl.dst + (size_t)to * row), base, pl.n16);
     return;
   }
@@ -479,8 +484,16 @@ __device__ __forceinline__ void staged_wave(const StagedArgs& a, const MovePlane
     from = staged_row(a, r.x);
     to = r.y;
   }
-  if (from < 0 || to < 0) return;
-  const size_t f = (size_t)from * pl.per_row + u, t = (size_t)to * pl.per_row + u;
+  if (to < 0 || (TRANSFER && from < 0)) return;
+  const size_t t = (size_t)to * pl.per_row + u;
+  if (from < 0) {
+    if (pl.unit == 16)
+      store_stream((u32x4*)pl.dst + t, u32x4{0u, 0u, 0u, 0u});
+    else
+      __builtin_nontemporal_store(0u, (uint32_t*)pl.dst + t);
+    return;
+  }
+  const size_t f = (size_t)from * pl.per_row + u;
   if (pl.unit == 16)
     store_stream((u32x4*)pl.dst + t, load_stream((const u32x4*)pl.src + f));
   else

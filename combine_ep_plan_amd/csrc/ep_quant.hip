@@ -87,9 +87,14 @@ __device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x
       v[2 * h] = bf16_lo(r.v[i][h]);
       v[2 * h + 1] = bf16_hi(r.v[i][h]);
     }
+    // amax over the block's magnitudes; a NaN never compares greater, so it
+    // is left out (an infinite value makes amax and the scale infinite).
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    for (int j = 0; j < 8; ++j) {
+      const float a = fabsf(v[j]);
+      amax = a > amax ? a : amax;
+    }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
     const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
@@ -97,9 +102,11 @@ __device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x
     uint32_t c[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float q = v[j] / scale;
-      q = fminf(fmaxf(q, -448.0f), 448.0f);
-      c[j] = f32_to_e4m3(q);
+      // A NaN quotient (a NaN value, or an infinite one over its infinite
+      // scale) is the NaN code 0x7F; it must not reach the clamp, which
+      // would turn it into -448.
+      const float q = v[j] / scale;
+      c[j] = __builtin_isnan(q) ? 0x7Fu : f32_to_e4m3(fminf(fmaxf(q, -448.0f), 448.0f));
     }
     packed[i][0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     packed[i][1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);

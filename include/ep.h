@@ -209,7 +209,10 @@ EP_API int ep_dispatch_pack(const ep_desc *d, const void *const x[2],
  * descriptor's payload must be EP_PAYLOAD_FP8_B128. Each token row is read
  * once and quantised per block of 128 values: scale = amax / 448 as a float
  * division (1 when amax is 0), code = OCP e4m3fn of x / scale (float
- * division), nearest even, clamped to +-448. send[0] (codes, [N][T*R][H])
+ * division), nearest even, clamped to +-448. NaN values are left out of
+ * amax and a NaN quotient gets the NaN code 0x7F; an infinite value makes
+ * its block's scale infinite, so its own code is 0x7F and the block's
+ * finite values get (signed) zero codes. send[0] (codes, [N][T*R][H])
  * and send[1] (fp32 scales, [N][T*R][H/128]) receive the token's planes at
  * each of its R send positions, exactly as ep_dispatch_pack would place a
  * pre-quantised row. */
@@ -227,7 +230,11 @@ EP_API int ep_dispatch_transfer(const ep_desc *d, const void *const send[2],
 /* Dispatch receiver on a materialised receive buffer: shuffle recv[p]
  * ([N][cap][row_p], as written by ep_dispatch_transfer) into the grouped
  * layout grouped[p] ([N][cap][row_p]; expert j of rank d owns rows
- * [grp_off[d][j], grp_off[d][j+1])). */
+ * [grp_off[d][j], grp_off[d][j+1])). Under EP_STATUS_CAPACITY the receive
+ * buffer lost the rows past cap in receive order (source, then segment
+ * row), while the grouped layout keeps rows below cap in grouped order;
+ * a grouped row below cap whose receive-buffer row was lost is written as
+ * zeros. */
 EP_API int ep_dispatch_unpack(const ep_desc *d, const void *const recv[2],
                        const void *plan_ws, void *const grouped[2],
                        hipStream_t stream);
@@ -236,7 +243,10 @@ EP_API int ep_dispatch_unpack(const ep_desc *d, const void *const recv[2],
  * rows straight from the sources' send buffers (the pattern of intra-node
  * peer-mapped buffers) into the grouped layout:
  * grouped[p][e / L][grp_pos[s][t][k]] = send[p][s][send_pos[s][t][k]].
- * Same result as ep_dispatch_transfer followed by ep_dispatch_unpack. */
+ * Same result as ep_dispatch_transfer followed by ep_dispatch_unpack when
+ * no rank receives more than cap rows; under EP_STATUS_CAPACITY this path
+ * delivers every row with grp_pos < cap, the staged path only those whose
+ * receive-buffer row also fits (zeros in the others). */
 EP_API int ep_dispatch_recv(const ep_desc *d, const void *const send[2],
                      const void *plan_ws, void *const grouped[2],
                      hipStream_t stream);

@@ -210,12 +210,13 @@ def transfer(send: np.ndarray, p: dict, recv_rows: int) -> np.ndarray:
     return recv
 
 
-def unpack(recv: np.ndarray, p: dict, rows: int) -> np.ndarray:
-    """receive buffers [N, recv_rows, row] -> grouped [N, rows, row]."""
+def unpack(recv: np.ndarray, p: dict, rows: int, fill: int = 0) -> np.ndarray:
+    """receive buffers [N, recv_rows, row] -> grouped [N, rows, row]; rows
+    the unpack does not write keep the byte `fill`."""
     N, recv_rows, row = recv.shape
     E = p["cnt"].shape[1]
     T, R = p["send_pos"].shape[1:]
-    grouped = np.zeros((N, rows, row), np.uint8)
+    grouped = np.full((N, rows, row), fill, np.uint8)
     lib().oracle_unpack(N, T, E, R, row, recv_rows, rows, _ptr(recv),
                         _ptr(p["cnt"]), _ptr(p["send_off"]), _ptr(p["recv_off"]),
                         _ptr(p["grp_off"]), _ptr(grouped))

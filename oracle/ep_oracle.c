@@ -126,6 +126,8 @@ uint8_t oracle_f32_to_e4m3(float v)
         return 0x7F;
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
     double a = fabs((double)v);
+    if (isinf(a))
+        return sign | 0x7E;            /* saturates like any finite overflow */
     uint8_t best = 0;
     double best_d = a;                 /* distance to code 0 (value 0) */
     for (int c = 1; c <= 0x7E; ++c) {
@@ -141,7 +143,12 @@ uint8_t oracle_f32_to_e4m3(float v)
 /* Block-scaled fp8 ("Evaluation": block-scaled fp8 dispatch), for one row of
  * H bf16 values: per block of 128, amax = max |x|, scale = amax / 448 in
  * float (1 when amax is 0), code = e4m3(x / scale) with the quotient formed
- * in float and clamped to +-448. codes: H bytes; scales: H/128 floats. */
+ * in float and clamped to +-448. codes: H bytes; scales: H/128 floats.
+ * Non-finite inputs (the page is silent; reading adopted): a NaN is never
+ * larger than amax, so it is left out of it, and its quotient is NaN, code
+ * 0x7F; an infinite value makes amax and the scale infinite, its own
+ * quotient inf/inf is NaN (0x7F) and the finite values of its block divide
+ * to signed zeros. */
 void oracle_quantize_b128(int H, const uint16_t *x, uint8_t *codes, float *scales)
 {
     for (int b = 0; b < H / 128; ++b) {
@@ -368,7 +375,11 @@ void oracle_transfer(int N, int T, int E, int R, int64_t row,
 /* Receiver: shuffle rows from the receive buffer into the grouped layout.
  * Source s's segment holds its rows for local experts j = 0..L-1 in turn;
  * they go to expert j's region after the rows of sources 0..s-1.
- * grouped: [N][cap][row]. */
+ * grouped: [N][cap][row]. A grouped row below cap whose receive-buffer row
+ * lies at or beyond recv_rows (the transfer dropped it: more rows arrived
+ * than the buffer holds) is written as zeros; the page is silent on what an
+ * overflowing receiver holds, and zeros make the slot add nothing to its
+ * token downstream. */
 void oracle_unpack(int N, int T, int E, int R, int64_t row,
                    int64_t recv_rows, int64_t cap, const uint8_t *recv,
                    const int32_t *cnt, const int32_t *send_off,
@@ -392,8 +403,12 @@ void oracle_unpack(int N, int T, int E, int R, int64_t row,
                 for (int64_t i = 0; i < cnt[(size_t)s * E + e]; ++i) {
                     int64_t src = seg + in_seg + i;
                     int64_t dst = g0 + i;
-                    if (dst >= cap || src >= recv_rows)
+                    if (dst >= cap)
                         continue;
+                    if (src >= recv_rows) {
+                        memset(grouped + ((size_t)d * cap + dst) * row, 0, (size_t)row);
+                        continue;
+                    }
                     memcpy(grouped + ((size_t)d * cap + dst) * row,
                            recv + ((size_t)d * recv_rows + src) * row,
                            (size_t)row);

@@ -168,6 +168,40 @@ def bf16_close(got: np.ndarray, want: np.ndarray, rel: float = 8e-3) -> np.ndarr
     return np.abs(g - o) <= rel * np.abs(o)
 
 
+def random_bf16(rng: np.random.Generator, shape, lo: int = -6, hi: int = 6) -> np.ndarray:
+    """bf16 bit patterns of random sign, exponent in [lo, hi], any mantissa:
+    expert rows whose terms cancel, as a grouped GEMM's outputs do."""
+    sign = rng.integers(0, 2, shape, dtype=np.uint32) << 15
+    expo = rng.integers(127 + lo, 127 + hi + 1, shape, dtype=np.uint32) << 7
+    mant = rng.integers(0, 128, shape, dtype=np.uint32)
+    return (sign | expo | mant).astype(np.uint16)
+
+
+def abs_term_sum(weights: np.ndarray, y_slots: np.ndarray) -> np.ndarray:
+    """sum_k |w_k| * |y_k| per output element, in float64: weights [..., R]
+    fp32, y_slots [..., R, H] bf16 bits of each slot's expert row (zero rows
+    for dropped slots). Returns [..., H]."""
+    w = np.abs(weights.astype(np.float64))
+    out = np.zeros(y_slots.shape[:-2] + y_slots.shape[-1:], np.float64)
+    for k in range(y_slots.shape[-2]):
+        out += w[..., k, None] * np.abs(W.bf16_bits_to_f32(y_slots[..., k, :]).astype(np.float64))
+    return out
+
+
+def combine_close(got: np.ndarray, want: np.ndarray, abs_sum: np.ndarray, R: int) -> np.ndarray:
+    """The combine's bar where the R terms may cancel:
+    |g - o| <= 8e-3 |o| + 2 R 2^-24 sum_k |w_k y_k| + 2^-133.
+    g sums in fp32 with one rounding per fused multiply-add (error at most
+    R 2^-24 sum_k |w_k y_k|), the oracle rounds the exact sum once; both then
+    round to bf16 (half an ulp, at most 2^-8 relative each, which the 8e-3
+    relative term covers) and 2^-133, the bf16 subnormal step, covers
+    results in the subnormal range. With terms of one sign the absolute part
+    is far below one ulp of |o| and the bar is the relative one."""
+    g = W.bf16_bits_to_f32(got).astype(np.float64)
+    o = W.bf16_bits_to_f32(want).astype(np.float64)
+    return np.abs(g - o) <= 8e-3 * np.abs(o) + 2.0 * R * 2.0 ** -24 * abs_sum + 2.0 ** -133
+
+
 def rows_of(t: torch.Tensor, d_idx: np.ndarray, r_idx: np.ndarray) -> np.ndarray:
     """Gather rows t[d, r] on the device, return them on the host."""
     dd = torch.from_numpy(d_idx.astype(np.int64)).to(t.device)

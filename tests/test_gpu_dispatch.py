@@ -117,4 +117,25 @@ def test_dispatch_bad_ids_and_capacity():
 
 @pytest.mark.parametrize("name", ["decode", "decode_zipf", "decode_fp8", "worst"])
 def test_dispatch_full_size(name):
-    compare(W.CONFIGS[name], W.make_workload(W.CONFIGS[name]), with_oracle=False)
+    """The benchmarked one-call dispatch at full size: equal to the three
+    calls, its plan tables equal to the oracle's, and every send row and
+    delivered grouped row equal to the token row the oracle's plan puts
+    there (compared on the device)."""
+    sh = W.CONFIGS[name]
+    wl = W.make_workload(sh)
+    b = compare(sh, wl)
+    N, T, E, R = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk
+    p = oracle.plan(N, T, E, R, ep.capacity(b.desc), wl.idx)
+    ss, tt, _ = np.unravel_index(np.arange(N * T * R), (N, T, R))
+    dd = wl.idx.reshape(-1) // (E // N)
+    for q in range(len(wl.planes)):
+        for lo in range(0, N * T * R, 8192):
+            sl = slice(lo, min(lo + 8192, N * T * R))
+            si = torch.from_numpy(ss[sl]).cuda()
+            ti = torch.from_numpy(tt[sl]).cuda()
+            want = b.x[q][si, ti]
+            spi = torch.from_numpy(p["send_pos"].reshape(-1)[sl].astype(np.int64)).cuda()
+            gpi = torch.from_numpy(p["grp_pos"].reshape(-1)[sl].astype(np.int64)).cuda()
+            di = torch.from_numpy(dd[sl].astype(np.int64)).cuda()
+            assert torch.equal(b.send[q][si, spi], want), f"send rows {lo}.."
+            assert torch.equal(b.grouped[q][di, gpi], want), f"grouped rows {lo}.."

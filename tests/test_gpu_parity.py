@@ -183,43 +183,73 @@ def test_capacity_overflow_drops_rows_and_flags():
     assert (ref["plan"]["grp_pos"] == -1).sum() >= 5
 
 
-def test_capacity_overflow_staged_path():
-    """Staged path under overflow: the receive buffer itself drops rows >= cap,
-    so compare with the oracle's transfer into a cap-row receive buffer."""
-    sh = W.Shape("tight_staged", 4, 32, 128, 16, 3, routing="zipf", seed=13)
+def _staged_overflow_idx(N, T, L):
+    """Routing whose rows lost by rank 0's receive buffer sit early in its
+    grouped order: sources 0 .. N-2 send every token to rank 0's expert 1,
+    the last source to its expert 0 (second choices go to other ranks)."""
+    idx = np.zeros((N, T, 2), np.int32)
+    idx[:, :, 0] = 1
+    idx[N - 1, :, 0] = 0
+    idx[:, :, 1] = L + (np.arange(N)[:, None] % (N - 1)) * L + np.arange(T)[None, :] % L
+    return idx
+
+
+STAGED_OVERFLOW = [
+    (W.Shape("tight_staged", 4, 32, 128, 16, 3, routing="zipf", expert="scale", seed=13), None),
+    (W.Shape("tight_staged_early", 4, 24, 256, 16, 2, expert="scale", seed=15), "early"),
+    (W.Shape("tight_staged_fp8", 4, 24, 256, 16, 2, payload=W.PAYLOAD_FP8_B128,
+             expert="dequant", seed=16), "early"),
+]
+
+
+@pytest.mark.parametrize("sh,routing", STAGED_OVERFLOW, ids=[c[0].name for c in STAGED_OVERFLOW])
+def test_capacity_overflow_staged_path(sh, routing):
+    """Staged path under overflow: the receive buffer keeps the first cap
+    rows of each rank in receive order and the unpack writes zeros into the
+    grouped rows whose receive row was lost. Receive buffers, grouped
+    layouts, expert outputs and the combine, compared in full with the
+    oracle's transfer into a cap-row receive buffer, its unpack, expert and
+    combine."""
+    N, T, E, R, H = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk, sh.hidden
     wl = W.make_workload(sh)
-    full = oracle.plan(4, 32, 16, 3, oracle.recv_bound(4, 32, 16, 3), wl.idx)
-    cap = int(full["recv_off"][:, 4].max()) - 4
+    if routing == "early":
+        wl = W.make_workload(sh, idx=_staged_overflow_idx(N, T, E // N))
+    full = oracle.plan(N, T, E, R, oracle.recv_bound(N, T, E, R), wl.idx)
+    cap = int(full["recv_off"][:, N].max()) - 4
     d = desc_of(sh, cap)
-    note(f"staged overflow cap={cap}")
+    note(f"staged overflow {sh.name} cap={cap}")
     b = ep.Buffers(d, staged=True)
     upload(b, wl)
+    for g in b.grouped:
+        g.fill_(0x5A)                             # stale bytes must not survive
     run_path(d, b, wl, staged=True)
     torch.cuda.synchronize()
-    p = oracle.plan(4, 32, 16, 3, cap, wl.idx)
-    send = oracle.dispatch_pack(wl.planes[0], p)
-    recv = oracle.transfer(send, p, cap)
-    grouped = oracle.unpack(recv, p, cap)
-    g = b.grouped[0].cpu().numpy()
-    r = b.recv[0].cpu().numpy()
-    totals = p["recv_off"][:, 4]
-    for dd in range(4):
-        n = min(int(totals[dd]), cap)
-        np.testing.assert_array_equal(r[dd, :n], recv[dd, :n])
-        # rows the receive buffer could not hold leave holes in the grouped
-        # layout; compare only rows whose source fitted
-        src_fitted = np.zeros(cap, bool)
-        for s in range(4):
-            for t in range(32):
-                for k in range(3):
-                    e = wl.idx[s, t, k]
-                    if e // 4 != dd or p["grp_pos"][s, t, k] < 0:
-                        continue
-                    seg_row = p["recv_off"][dd, s] + (p["send_pos"][s, t, k] - p["send_off"][s, dd * 4])
-                    if seg_row < cap:
-                        src_fitted[p["grp_pos"][s, t, k]] = True
-        np.testing.assert_array_equal(g[dd, :n][src_fitted[:n]], grouped[dd, :n][src_fitted[:n]])
-    assert int(b.status.item()) & ep.EP_STATUS_CAPACITY
+    p = oracle.plan(N, T, E, R, cap, wl.idx)
+    assert int(b.status.item()) == p["status"] and p["status"] & ep.EP_STATUS_CAPACITY
+    send = [oracle.dispatch_pack(pl, p) for pl in wl.planes]
+    recv = [oracle.transfer(sp, p, cap) for sp in send]
+    grouped = [oracle.unpack(r, p, cap) for r in recv]
+    y = oracle.expert_op(grouped, p, H, sh.payload, wl.alpha)
+    out = oracle.combine(y, wl.weights, wl.idx, p)
+    zero_rows = 0
+    for q in range(len(wl.planes)):
+        r_got = b.recv[q].cpu().numpy()
+        g_got = b.grouped[q].cpu().numpy()
+        for dd in range(N):
+            n = min(int(p["recv_off"][dd, N]), cap)
+            np.testing.assert_array_equal(r_got[dd, :n], recv[q][dd, :n], err_msg=f"recv {dd}")
+            np.testing.assert_array_equal(g_got[dd, :n], grouped[q][dd, :n],
+                                          err_msg=f"grouped {dd}")
+            if q == 0:
+                zero_rows += int((grouped[0][dd, :n] == 0).all(axis=1).sum())
+    if routing == "early":
+        assert zero_rows >= 4                     # lost receive rows below cap
+    y_got = b.expert_out.cpu().numpy().view(np.uint16)
+    for dd in range(N):
+        n = min(int(p["recv_off"][dd, N]), cap)
+        np.testing.assert_array_equal(y_got[dd, :n], y[dd, :n], err_msg=f"expert {dd}")
+    ok = bf16_close(b.out.cpu().numpy().view(np.uint16), out)
+    assert ok.all(), f"combine: {int((~ok).sum())} elements off"
 
 
 def test_deterministic_and_stream_independent():
@@ -271,7 +301,11 @@ def test_probe_copy():
 # Full-size workloads (the configurations of the benchmark and its siblings)
 # ---------------------------------------------------------------------------
 
-def compare_full_size(name, n_slots=3000, n_tokens=300):
+def compare_full_size(name, n_slots=3000, n_tokens=300, full_oracle=False):
+    """Plan tables in full, every send and delivered grouped row on the
+    device, sampled rows and tokens against the oracle one by one; with
+    full_oracle also the oracle's whole path (plan, pack, transfer, unpack,
+    expert, combine): every expert-output row and every output token."""
     sh = W.CONFIGS[name]
     N, T, E, R, H = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk, sh.hidden
     L = E // N
@@ -329,11 +363,21 @@ def compare_full_size(name, n_slots=3000, n_tokens=300):
         ys = [oracle.expert_row(row, int(ee), sh.payload, H, wl.alpha) for ee in wl.idx[ts[i], tt[i]]]
         want = oracle.combine_token(wl.weights[ts[i], tt[i]], ys)
         assert bf16_close(out[i], want).all(), (name, ts[i], tt[i])
+    if full_oracle:
+        ref = oracle.run(wl, cap=cap)
+        rows = ref["rows"]
+        y_got = b.expert_out[:, :rows].cpu().numpy().view(np.uint16)
+        for dd in range(N):
+            n = min(int(p["recv_off"][dd, N]), cap)
+            np.testing.assert_array_equal(y_got[dd, :n], ref["y"][dd, :n], err_msg=f"expert {dd}")
+        del y_got
+        ok = bf16_close(b.out.cpu().numpy().view(np.uint16), ref["out"])
+        assert ok.all(), f"{name} combine: {int((~ok).sum())} of {ok.size} elements off"
     return sh, wl, b
 
 
 def test_full_size_decode():
-    sh, wl, b = compare_full_size("decode")
+    sh, wl, b = compare_full_size("decode", full_oracle=True)
     # closed form up to two bf16 roundings: out ~= x * sum_k w_k alpha_k
     x = torch.from_numpy(W.bf16_bits_to_f32(wl.x_bf16)).cuda().double()
     f = torch.from_numpy((wl.weights.astype(np.float64) * wl.alpha[wl.idx]).sum(-1)).cuda()
@@ -346,7 +390,7 @@ def test_full_size_decode():
 
 
 def test_full_size_decode_zipf():
-    compare_full_size("decode_zipf")
+    compare_full_size("decode_zipf", full_oracle=True)
 
 
 def _unsign_zero(a):

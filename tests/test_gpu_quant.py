@@ -102,6 +102,35 @@ def test_pack_quant_zero_and_signed_blocks():
     np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.float32), osc)
 
 
+@pytest.mark.parametrize("H", [384, 8320], ids=["per_token_workgroup", "per_segment_waves"])
+def test_pack_quant_non_finite_blocks(H):
+    """NaN (quiet, signalling, negative) is left out of amax and codes 0x7F;
+    +-Inf makes its block's scale infinite, codes itself 0x7F and zeroes the
+    block's finite values with their signs. Both sender forms, bit for bit
+    against the oracle."""
+    sh = W.Shape(f"q_nonfinite_{H}", 2, 4, H, 4, 2, payload=W.PAYLOAD_FP8_B128,
+                 expert="dequant", seed=17)
+    wl = W.make_workload(sh)
+    xb = wl.x_bf16.copy()
+    xb[0, 0, 3] = 0x7FC0                 # quiet NaN
+    xb[0, 0, 200] = 0xFFC1               # negative NaN
+    xb[0, 1, 300] = 0x7F81               # signalling-NaN pattern
+    xb[1, 0, 130] = 0x7F80               # +Inf
+    xb[1, 1, 255] = 0xFF80               # -Inf
+    xb[1, 2, 0:128] = 0x7FC0             # all-NaN block: scale 1
+    xb[1, 3, 128:256] = 0x7F80           # all +Inf block
+    wl.x_bf16 = xb
+    codes, scales = oracle.quantize_b128(xb)
+    wl.planes = [codes, scales.view(np.uint8)]
+    note(f"quant non-finite H={H}")
+    d, b, _ = _run_quant_path(sh, wl)
+    p = oracle.plan(2, 4, 4, 2, ep.capacity(d), wl.idx)
+    oc, osc = oracle.dispatch_pack_quant(xb, p)
+    assert (oc == 0x7F).sum() >= 2 * (5 + 128 + 128)      # every slot's copies
+    np.testing.assert_array_equal(b.send[0].cpu().numpy(), oc)
+    np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
+
+
 def test_pack_quant_rejects_bf16_descriptor():
     sh = W.CONFIGS["tiny"]
     d = desc_of(sh)

@@ -72,6 +72,19 @@ MUTATIONS = {
                               "return ((int64_t)blocks[i / bs] * bs) * tok;"),
     "kv_copy_rank_stride": ("memcpy(dst + r * dst_rank_bytes + dst_off[j],",
                             "memcpy(dst + dst_off[j],"),
+    "e4m3_inf_not_saturated": ("    if (isinf(a))\n        return sign | 0x7E;", ""),
+    "quant_nan_in_amax": ("            if (a > amax)\n                amax = a;",
+                          "            if (!(a <= amax))\n                amax = a;"),
+    "quant_nan_not_nan_code": ("    if (isnan(v))\n        return 0x7F;\n    uint8_t sign",
+                               "    if (isnan(v))\n        return 0x00;\n    uint8_t sign"),
+    "quant_pack_source_offset_dropped": ("size_t row = (size_t)s * T * R + (size_t)p;",
+                                         "size_t row = (size_t)p;"),
+    "quant_pack_scale_row": ("memcpy(scales + row * (H / 128), qs,",
+                             "memcpy(scales + (size_t)p * (H / 128), qs,"),
+    "quant_pack_wrong_token": ("oracle_quantize_b128(H, x + ((size_t)s * T + t) * H, qc, qs);",
+                               "oracle_quantize_b128(H, x + ((size_t)s * T + (T - 1 - t)) * H, qc, qs);"),
+    "unpack_overflow_rows_left_stale": ("memset(grouped + ((size_t)d * cap + dst) * row, 0, (size_t)row);",
+                                        ";"),
     "quant_block_size": ("float a = fabsf(oracle_bf16_to_f32(x[b * 128 + i]));",
                          "float a = fabsf(oracle_bf16_to_f32(x[b * 128 + (i & 63)]));"),
 }
@@ -100,6 +113,10 @@ def _pin_checks():
         pins.test_f32_to_e4m3_matches_torch_including_ties,
         pins.test_quantize_b128_matches_generator_quantiser,
         pins.test_quantize_b128_roundtrip_error_bound,
+        pins.test_f32_to_e4m3_saturates_infinities,
+        pins.test_quantize_b128_non_finite_blocks,
+        pins.test_dispatch_pack_quant_is_quantise_then_place,
+        pins.test_staged_overflow_rows_are_source_rows_or_zeros,
         pins.test_presum_groups_by_rank_and_rounds_each_partial,
         pins.test_presum_adds_partials_in_slot_order,
         pins.test_presum_single_choice_is_the_rounded_product,

@@ -332,6 +332,47 @@ def test_grouped_rows_are_source_rows(name):
                                           wl.planes[0][s, t])
 
 
+def test_staged_overflow_rows_are_source_rows_or_zeros():
+    """A receive buffer of cap rows keeps the first cap rows of each
+    destination in receive order (source rank, then segment row); the
+    grouped rows below cap are the x rows their slots name (by a brute-force
+    walk of the receive order) when the slot's receive row fitted, else
+    zeros. Rows the unpack does not own keep the fill byte."""
+    # Rank 0 receives 18 rows: sources 0 and 1 send to its expert 1, source 2
+    # to its expert 0. With cap 16 the receive buffer loses source 2's last
+    # two rows, which the grouped order puts first (expert 0): rows 4 and 5
+    # must be zeros, while grouped rows 16 and 17 fall past cap.
+    sh = W.Shape("staged_tight", 3, 6, 16, 6, 2, seed=14)
+    idx = np.zeros((3, 6, 2), np.int32)
+    idx[0] = [1, 2]
+    idx[1] = [1, 4]
+    idx[2] = [0, 5]
+    wl = W.make_workload(sh, idx=idx)
+    cap = 16
+    p = oracle.plan(3, 6, 6, 2, cap, wl.idx)
+    send = oracle.dispatch_pack(wl.planes[0], p)
+    recv = oracle.transfer(send, p, cap)
+    grouped = oracle.unpack(recv, p, cap, fill=0xAB)
+    x = wl.planes[0]
+    for d in range(3):
+        # receive order: for each source, its slots for rank d in (expert, t, k) order
+        order = []
+        for s in range(3):
+            order += sorted((int(wl.idx[s, t, k]), t, k, s) for t in range(6) for k in range(2)
+                            if wl.idx[s, t, k] // 2 == d)
+        grp = sorted(order, key=lambda q: (q[0], q[3], q[1], q[2]))
+        fitted = {q for i, q in enumerate(order) if i < cap}
+        for r in range(cap):
+            if r >= len(grp):
+                assert (grouped[d, r] == 0xAB).all()
+                continue
+            e, t, k, s = grp[r]
+            want = x[s, t] if (e, t, k, s) in fitted else np.zeros_like(x[s, t])
+            np.testing.assert_array_equal(grouped[d, r], want, err_msg=f"{d} {r}")
+    assert p["status"] & oracle.STATUS_CAPACITY
+    assert (grouped[0, 4:6] == 0).all() and (grouped[0, :4] != 0).any(axis=1).all()
+
+
 @pytest.mark.parametrize("name", ["tiny", "tiny_zipf"])
 def test_combine_identity_closed_form(name):
     """Identity experts and weights summing to one give back x exactly."""
@@ -486,6 +527,97 @@ def test_quantize_b128_roundtrip_error_bound():
     assert (np.abs(deq - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal] * (1 + 1e-6)).all()
     sub = ~normal
     assert (np.abs(deq - x)[sub] <= 2.0 ** -10 * np.repeat(scales, 128, axis=-1)[sub] * (1 + 1e-6)).all()
+
+
+def test_f32_to_e4m3_saturates_infinities():
+    """e4m3fn has no infinity; like any magnitude past 448 it saturates."""
+    assert oracle.f32_to_e4m3(float("inf")) == 0x7E
+    assert oracle.f32_to_e4m3(float("-inf")) == 0xFE
+    assert oracle.f32_to_e4m3(float("nan")) == 0x7F
+    assert oracle.f32_to_e4m3(-float("nan")) == 0x7F
+
+
+BF16_NAN, BF16_NEG_NAN, BF16_SNAN, BF16_INF, BF16_NEG_INF = 0x7FC0, 0xFFC1, 0x7F81, 0x7F80, 0xFF80
+
+
+def test_quantize_b128_non_finite_blocks():
+    """NaN is left out of amax and codes 0x7F; an infinite value makes its
+    block's scale infinite, codes itself 0x7F and zeroes the block's finite
+    values (signed). Finite blocks beside them are untouched: they equal the
+    torch-cast quantiser of the workload generator."""
+    rng = np.random.default_rng(12)
+    xb = W.to_bf16_bits(rng.standard_normal((4, 512)).astype(np.float32))
+    clean = xb.copy()
+    xb[0, 3] = BF16_NAN
+    xb[0, 200] = BF16_NEG_NAN
+    xb[0, 300] = BF16_SNAN
+    xb[1, 130] = BF16_INF
+    xb[2, 511] = BF16_NEG_INF
+    xb[3, 0:128] = BF16_NAN                         # an all-NaN block: amax 0, scale 1
+    codes, scales = oracle.quantize_b128(xb)
+    # NaN positions and the infinities themselves
+    for r, c in [(0, 3), (0, 200), (0, 300), (1, 130), (2, 511)]:
+        assert codes[r, c] == 0x7F, (r, c)
+    assert (codes[3, :128] == 0x7F).all() and scales[3, 0] == 1.0
+    # NaN blocks: amax of the finite values, as if the NaN were a zero
+    no_nan = clean.copy()
+    no_nan[0, [3, 200, 300]] = 0
+    gc, gs = W.quantize_fp8_b128(no_nan)
+    keep = np.ones(512, bool)
+    keep[[3, 200, 300]] = False
+    np.testing.assert_array_equal(codes[0, keep], gc[0, keep])
+    np.testing.assert_array_equal(scales[0], gs[0])
+    # infinite blocks: scale inf, finite values to +-0 by sign
+    assert np.isinf(scales[1, 1]) and np.isinf(scales[2, 3])
+    for r, blk, skip in [(1, 1, 130), (2, 3, 511)]:
+        lo = 128 * blk
+        idx = [i for i in range(lo, lo + 128) if i != skip]
+        want = np.where(xb[r, idx] & 0x8000, 0x80, 0x00)
+        np.testing.assert_array_equal(codes[r, idx], want)
+    # the other blocks of those rows are the plain quantiser's
+    gc, gs = W.quantize_fp8_b128(clean)
+    for r, blk in [(1, 0), (1, 2), (1, 3), (2, 0), (2, 1), (2, 2)]:
+        sl = slice(128 * blk, 128 * blk + 128)
+        np.testing.assert_array_equal(codes[r, sl], gc[r, sl])
+        assert scales[r, blk] == gs[r, blk]
+
+
+def _send_rows_by_argsort(idx, E):
+    """(source, send row) -> token of that row, from numpy's stable argsort
+    of each source's expert ids (valid ids only), independent of the plan."""
+    N, T, R = idx.shape
+    out = {}
+    for s in range(N):
+        flat = idx[s].reshape(-1)
+        ok = np.nonzero((flat >= 0) & (flat < E))[0]
+        order = ok[np.argsort(flat[ok], kind="stable")]
+        for p, slot in enumerate(order):
+            out[(s, p)] = slot // R
+    return out
+
+
+def test_dispatch_pack_quant_is_quantise_then_place():
+    """The fused sender's planes: every send row p of source s holds the
+    torch-cast quantisation of the token that the stable argsort puts at p;
+    rows past the valid slots stay zero. Repeated and out-of-range ids."""
+    sh = W.Shape("pq", 3, 9, 384, 12, 3, payload=W.PAYLOAD_FP8_B128, expert="dequant", seed=13)
+    wl = W.make_workload(sh)
+    idx = wl.idx.copy()
+    idx[0, 2, 1] = idx[0, 2, 0]                      # repeated id within a token
+    idx[1, 4, 2] = 12                                # out of range: dropped
+    idx[2, 8, 0] = -1
+    p = oracle.plan(3, 9, 12, 3, oracle.recv_bound(3, 9, 12, 3), idx)
+    codes, scales = oracle.dispatch_pack_quant(wl.x_bf16, p)
+    gc, gs = W.quantize_fp8_b128(wl.x_bf16)
+    rows = _send_rows_by_argsort(idx, 12)
+    want_c = np.zeros_like(codes)
+    want_s = np.zeros_like(scales)
+    for (s, r), t in rows.items():
+        want_c[s, r] = gc[s, t]
+        want_s[s, r] = gs[s, t]
+    np.testing.assert_array_equal(codes, want_c)
+    np.testing.assert_array_equal(scales, want_s)
+    assert len(rows) == 3 * 9 * 3 - 2
 
 
 # ---------------------------------------------------------------------------
