@@ -27,6 +27,7 @@ EP_STATUS_CAPACITY = 2
 EP_STATUS_BAD_REGION = 4
 EP_PAYLOAD_BF16 = 0
 EP_PAYLOAD_FP8_B128 = 1
+EP_KV_STATIC_SLOTS = 64
 
 # Every entry point the C header declares (checked by the tests).
 EXPORTS = (
@@ -39,6 +40,7 @@ EXPORTS = (
     "ep_dispatch_send_pack", "ep_dispatch_recv_plan", "ep_dispatch_recv_pull",
     "ep_expert_stub", "ep_combine",
     "ep_combine_presum", "ep_kv_plan", "ep_kv_push", "ep_kv_push_staged",
+    "ep_kv_push_staged_static",
     "ep_probe_copy", "ep_status_string",
     "ep_last_error",
 )
@@ -105,6 +107,8 @@ def _load() -> ctypes.CDLL:
         "ep_kv_push": (ctypes.c_int, [ctypes.c_int32, P, I64, I64, P, I64, P, I64, P, P, P]),
         "ep_kv_push_staged": (ctypes.c_int, [ctypes.c_int32, P, I64, I64, P, I64, P, I64, P,
                                              ctypes.c_int32, P, P, P]),
+        "ep_kv_push_staged_static": (ctypes.c_int, [ctypes.c_int32, P, I64, I64, P, I64, P, I64,
+                                                    ctypes.c_int32, P, P, P]),
         "ep_probe_copy": (ctypes.c_int, [P, P, ctypes.c_size_t, P]),
         "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "ep_last_error": (ctypes.c_char_p, []),
@@ -343,6 +347,16 @@ def kv_push_staged(ranks: int, regions, n_regions: int, total_bytes: int, src_po
                                   int(dst_rank_bytes), _addr(bounce), int(bounce_slots),
                                   _addr(notify), _addr(status), _stream(stream)),
            "ep_kv_push_staged")
+
+
+def kv_push_staged_static(ranks: int, regions, n_regions: int, total_bytes: int, src_pool,
+                          src_rank_bytes: int, dst_pool, dst_rank_bytes: int, bounce_slots: int,
+                          notify, status, stream=None) -> None:
+    _check(_lib.ep_kv_push_staged_static(int(ranks), _addr(regions), int(n_regions),
+                                         int(total_bytes), _addr(src_pool), int(src_rank_bytes),
+                                         _addr(dst_pool), int(dst_rank_bytes), int(bounce_slots),
+                                         _addr(notify), _addr(status), _stream(stream)),
+           "ep_kv_push_staged_static")
 
 
 def probe_copy(dst, src, nbytes: int, stream=None) -> None:

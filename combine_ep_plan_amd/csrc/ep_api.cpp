@@ -636,12 +636,37 @@ int ep_kv_push_staged(int32_t ranks, const ep_kv_region* regions, int64_t m, int
   if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");
   EP_CHECK(kv_checks(ranks, regions, m, total, src, src_rank_bytes, dst, dst_rank_bytes, notify,
                      status, scope.device()));
-  if (slots < 1 || slots > 64) return fail(EP_ERR_INVALID_ARG, "bounce_slots must be in [1, 64]");
-  EP_CHECK(check_bounce(bounce, scope.device(), (int64_t)slots * 32768));
+  if (slots < 1 || slots > ep::kKvStaticSlots)
+    return fail(EP_ERR_INVALID_ARG, "bounce_slots must be in [1, 64]");
+  EP_CHECK(check_bounce(bounce, scope.device(), (int64_t)slots * ep::kKvSlotBytes));
   const hipError_t e = ep::launch_kv_push_staged(ranks, regions, m, total, src, src_rank_bytes,
                                                  dst, dst_rank_bytes, bounce,
-                                                 (int64_t)slots * 32768, notify, status, stream);
+                                                 (int64_t)slots * ep::kKvSlotBytes, notify, status,
+                                                 stream);
   if (e != hipSuccess) return fail_hip(e, "ep_kv_push_staged");
+  return EP_OK;
+}
+
+int ep_kv_push_staged_static(int32_t ranks, const ep_kv_region* regions, int64_t m,
+                             int64_t total, const void* src, int64_t src_rank_bytes, void* dst,
+                             int64_t dst_rank_bytes, int32_t slots, int32_t* notify,
+                             int32_t* status, hipStream_t stream) {
+  DeviceScope scope(stream);
+  if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");
+  EP_CHECK(kv_checks(ranks, regions, m, total, src, src_rank_bytes, dst, dst_rank_bytes, notify,
+                     status, scope.device()));
+  if (slots < 1 || slots > ep::kKvStaticSlots)
+    return fail(EP_ERR_INVALID_ARG,
+                "bounce_slots must be in [1, 64]: the library's static bounce area holds 64 "
+                "slots of 32 KiB");
+  // The stream's device is current here (DeviceScope), as the lookup needs.
+  void* bounce = nullptr;
+  hipError_t e = ep::kv_static_bounce(scope.device(), &bounce);
+  if (e != hipSuccess) return fail_hip(e, "ep_kv_push_staged_static: static bounce address");
+  e = ep::launch_kv_push_staged(ranks, regions, m, total, src, src_rank_bytes, dst,
+                                dst_rank_bytes, bounce, (int64_t)slots * ep::kKvSlotBytes, notify,
+                                status, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_kv_push_staged_static");
   return EP_OK;
 }
 

@@ -99,6 +99,12 @@ hipError_t launch_combine_presum(const Dims& d, const uint16_t* y, const float* 
                                  hipStream_t stream);
 // KV-block push (regions: device array of ep_kv_region).
 int64_t kv_piece_bytes();
+// The staged relay's bounce slots: 32 KiB each, at most 64 per round.
+constexpr int64_t kKvSlotBytes = 32768;
+constexpr int kKvStaticSlots = EP_KV_STATIC_SLOTS;
+// Device address of the library's static bounce slots on `dev` (the current
+// device), for the relay that allocates nothing.
+hipError_t kv_static_bounce(int dev, void** out);
 hipError_t launch_kv_push(int ranks, const ep_kv_region* reg, int64_t m, int64_t total,
                           const void* src, int64_t src_rank_bytes, void* dst,
                           int64_t dst_rank_bytes, int32_t* notify, int32_t* status,

@@ -15,10 +15,20 @@
 // one 7 KB piece of the stream for one rank, walking the (few) regions that
 // overlap the piece. Every region is checked against the pools before any
 // byte moves; a bad one is skipped and flagged.
+#include <mutex>
+
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 
 namespace ep {
+
+// Bounce slots of ep_kv_push_staged_static: the library's own device memory
+// for callers that cannot allocate, kKvStaticSlots slots of kKvSlotBytes.
+// Each GPU the library runs on holds its own copy until the process ends. In
+// host code the name stands for a host-side shadow, not a device address:
+// kernels get the address that kv_static_bounce looks up per device.
+static __device__ __align__(256) uint8_t scratch[kKvStaticSlots * kKvSlotBytes];
+
 namespace {
 
 constexpr int kWavesPerBlock = 4;
@@ -120,6 +130,26 @@ hipError_t notify_ranks(int ranks, int32_t* notify, hipStream_t stream) {
 }  // namespace
 
 int64_t kv_piece_bytes() { return kPiece; }
+
+// Device address of `scratch` on device `dev`, which must be the current
+// device. Looked up once per device (each device's copy lives at its own
+// address) and kept for the life of the process.
+hipError_t kv_static_bounce(int dev, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_kv_push(int ranks, const ep_kv_region* reg, int64_t m, int64_t total,
                           const void* src, int64_t src_rank_bytes, void* dst,

@@ -396,6 +396,27 @@ EP_API int ep_kv_push_staged(int32_t ranks, const ep_kv_region *regions,
                              int32_t *notify, int32_t *status,
                              hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * ep_kv_push_staged with its bounce slots in the library's own device
+ * memory instead of a caller buffer. That memory is one static array of
+ * EP_KV_STATIC_SLOTS slots of 32 KiB (2 MiB) per GPU the library runs on,
+ * held until the process ends. Arguments, result and completion counting
+ * are those of ep_kv_push_staged without `bounce`; bounce_slots must be in
+ * [1, EP_KV_STATIC_SLOTS], else EP_ERR_INVALID_ARG and nothing is enqueued.
+ * The call allocates nothing. The slots need no initialisation: every round
+ * writes the bytes it then reads. All calls on one GPU share its one array,
+ * which keeps the last call's bytes: calls that overlap on one GPU (two
+ * streams, or two threads without ordering between them) race and corrupt
+ * each other's transfers, so such calls must be ordered by the caller. */
+#define EP_KV_STATIC_SLOTS 64
+EP_API int ep_kv_push_staged_static(int32_t ranks, const ep_kv_region *regions,
+                                    int64_t n_regions, int64_t total_bytes,
+                                    const void *src_pool, int64_t src_rank_bytes,
+                                    void *dst_pool, int64_t dst_rank_bytes,
+                                    int32_t bounce_slots, int32_t *notify,
+                                    int32_t *status, hipStream_t stream);
+
 /* Stand-in for the grouped GEMM (outside the method; used by tests and the
  * benchmark to produce expert outputs). expert_out is bf16 [N][cap][H].
  * bf16 payload: y = x when alpha == NULL, else y = bf16(x * alpha[e]) with a
