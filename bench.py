@@ -97,15 +97,34 @@ def recorded_traffic(workload: str, stage: str):
     return k["traffic_bytes"]
 
 
+def cpu_host() -> dict:
+    """Host CPU of this run: the model name, the logical CPUs the OS reports
+    and the CPUs this process may run on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"nproc": os.cpu_count(), "cpus_allowed": affinity, "model": model}
+
+
 def cpu_baseline(sh, wl, budget_s: float, quant: bool) -> dict:
     """The oracle as it stands, single thread, on the same workload.
 
     With the quantising sender the oracle's quantiser (an exhaustive nearest
     code search per value) runs on the first `quant_ranks` source ranks only
     and its time is scaled by N / quant_ranks; the rest of the step runs on
-    the whole workload.
+    the whole workload. The last run's plan and combined tokens are kept for
+    the parity check of the benchmarked buffers.
     """
-    import numpy as np
     import oracle
 
     N, T, E, R, H = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk, sh.hidden
@@ -140,11 +159,184 @@ def cpu_baseline(sh, wl, budget_s: float, quant: bool) -> dict:
         out = oracle.combine(y, wl.weights, wl.idx, p)
         t_comb = time.perf_counter() - tc0
         times.append(t_plan + t_pack + t_recv + t_comb)
-        del send, recv, grouped, y, out
+        del send, recv, grouped, y
         if time.perf_counter() - t_begin >= budget_s or len(times) >= 50:
             break
     return {"seconds": times, "median_s": statistics.median(times), "runs": len(times),
-            "quant_ranks": quant_ranks if quant else None}
+            "quant_ranks": quant_ranks if quant else None, "plan": p, "out": out}
+
+
+class Flusher:
+    """Evicts the L2s and the MALL between timed steps: a 1 GiB fill and a
+    1 GiB read with ordinary stores and loads, outside the timed events. (The
+    library's copy probe would not do: its non-temporal accesses leave cached
+    lines in place, and so do the receiver's and the combine's, which is why
+    back-to-back steps find the previous sender's token rows still in each
+    XCD's L2.)"""
+
+    def __init__(self, torch):
+        self.a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        self.b = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
+
+    def __call__(self, i: int) -> None:
+        self.a.fill_(i & 0xFF)
+        self.b.max()
+
+
+def time_flushed(torch, stream, step, n: int, flush) -> list:
+    """n steps, each after a cache flush, each timed alone between two HIP
+    events on the step's stream (synchronised on both sides); µs."""
+    out = []
+    for i in range(n):
+        flush(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    return out
+
+
+def time_back_to_back(torch, stream, step, n: int) -> float:
+    """n steps queued back to back between two HIP events; µs per step."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def pcts(np, v) -> list:
+    return [round(float(np.percentile(v, q)), 2) for q in (10, 50, 90)]
+
+
+def bench_parity(ep, torch, np, d, b, sh, wl, quant: bool, oracle_out=None,
+                 n_tokens: int = 256, seed: int = 0) -> dict:
+    """Parity of the benchmarked buffers with the oracle, after the timed
+    steps:
+      - every plan table the oracle computes (cnt, send_off, send_pos,
+        recv_off, grp_off, grp_pos) and the status word, bit for bit;
+      - every send row and every delivered grouped row equal to the token
+        row the oracle's plan puts there (compared on the device);
+      - with the quantising sender, the send rows of sampled tokens equal to
+        the oracle's quantiser applied to their bf16 rows;
+      - out: every token against the oracle's whole-path result when given
+        (oracle_out), else sampled tokens against the oracle's per-token
+        combine; for identity and dequantising stand-ins also every token
+        against the closed form (weights summing to one give back the one
+        expert value exactly);
+      - combine bar: 8e-3 relative per element (the stand-in experts give
+        each token terms of one sign).
+    """
+    import oracle
+    import ep_workloads as W
+
+    N, T, E, R, H = sh.n_ranks, sh.tokens, sh.n_experts, sh.topk, sh.hidden
+    L = E // N
+    cap = ep.capacity(d)
+    p = oracle.plan(N, T, E, R, cap, wl.idx)
+    res = {}
+    # plan tables
+    v = ep.plan_views(d, b.plan_ws)
+    base = b.plan_ws.data_ptr()
+    ws = b.plan_ws.cpu().numpy()
+    bad_tables = []
+    for f in ("cnt", "send_off", "send_pos", "recv_off", "grp_off", "grp_pos"):
+        off = getattr(v, f) - base
+        got = ws[off:off + 4 * p[f].size].view(np.int32).reshape(p[f].shape)
+        if not np.array_equal(got, p[f]):
+            bad_tables.append(f)
+    status = int(b.status.item())
+    res["plan_tables"] = "bit-exact" if not bad_tables else "differ: " + ",".join(bad_tables)
+    res["status"] = status
+    # every send row and delivered grouped row, on the device
+    NTR = N * T * R
+    ss, tt, _ = np.unravel_index(np.arange(NTR), (N, T, R))
+    dd = wl.idx.reshape(-1) // L
+    sp, gp = p["send_pos"].reshape(-1), p["grp_pos"].reshape(-1)
+    bad_send = bad_grp = n_send = n_grp = 0
+    for q in range(len(b.x)):
+        for lo in range(0, NTR, 16384):
+            sl = slice(lo, min(lo + 16384, NTR))
+            ok_s = sp[sl] >= 0
+            ok_g = gp[sl] >= 0
+            si = torch.from_numpy(ss[sl]).cuda()
+            ti = torch.from_numpy(tt[sl]).cuda()
+            want = b.x[q][si, ti]
+            spi = torch.from_numpy(np.where(ok_s, sp[sl], 0).astype(np.int64)).cuda()
+            gpi = torch.from_numpy(np.where(ok_g, gp[sl], 0).astype(np.int64)).cuda()
+            di = torch.from_numpy(np.where(ok_g, dd[sl], 0).astype(np.int64)).cuda()
+            ms = torch.from_numpy(ok_s).cuda()
+            mg = torch.from_numpy(ok_g).cuda()
+            row_bad_s = (b.send[q][si, spi] != want).any(dim=-1) & ms
+            row_bad_g = (b.grouped[q][di, gpi] != want).any(dim=-1) & mg
+            bad_send += int(row_bad_s.sum().item())
+            bad_grp += int(row_bad_g.sum().item())
+            n_send += int(ok_s.sum())
+            n_grp += int(ok_g.sum())
+    res["send_rows_checked"] = n_send // len(b.x)
+    res["send_rows_bad"] = bad_send
+    res["grouped_rows_checked"] = n_grp // len(b.x)
+    res["grouped_rows_bad"] = bad_grp
+    rng = np.random.default_rng(seed)
+    if quant:
+        toks = rng.choice(N * T, size=min(N * T, 64), replace=False)
+        s_, t_ = np.unravel_index(toks, (N, T))
+        oc, osc = oracle.quantize_b128(wl.x_bf16[s_, t_])
+        k_ = rng.integers(0, R, size=len(toks))
+        rows = p["send_pos"][s_, t_, k_]
+        keep = rows >= 0
+        si = torch.from_numpy(s_[keep].astype(np.int64)).cuda()
+        ri = torch.from_numpy(rows[keep].astype(np.int64)).cuda()
+        gc = b.send[0][si, ri].cpu().numpy()
+        gs = b.send[1][si, ri].cpu().numpy().view(np.float32)
+        res["quantised_rows_checked"] = int(keep.sum())
+        res["quantised_rows_bad"] = int((gc != oc[keep]).any(-1).sum() +
+                                        (gs.view(np.uint32) != osc[keep].view(np.uint32)).any(-1).sum())
+    # combined tokens
+    out = b.out.cpu().numpy().view(np.uint16)
+
+    def close(g, o):
+        gf = W.bf16_bits_to_f32(g).astype(np.float64)
+        of = W.bf16_bits_to_f32(o).astype(np.float64)
+        return np.abs(gf - of) <= 8e-3 * np.abs(of)
+
+    if oracle_out is not None:
+        ok = close(out, oracle_out)
+        res["out_tokens_vs_oracle"] = N * T
+        res["out_elements_off"] = int((~ok).sum())
+    else:
+        toks = rng.choice(N * T, size=min(N * T, n_tokens), replace=False)
+        s_, t_ = np.unravel_index(toks, (N, T))
+        off = 0
+        for i in range(len(toks)):
+            row = [pl[s_[i], t_[i]] for pl in wl.planes]
+            ys = [oracle.expert_row(row, int(e), sh.payload, H, wl.alpha) if 0 <= e < E else None
+                  for e in wl.idx[s_[i], t_[i]]]
+            want = oracle.combine_token(wl.weights[s_[i], t_[i]], ys)
+            off += int((~close(out[s_[i], t_[i]], want)).sum())
+        res["out_tokens_vs_oracle"] = len(toks)
+        res["out_elements_off"] = off
+    if sh.expert in ("identity", "dequant") and status == 0:
+        g = b.out
+        if sh.expert == "identity":
+            want = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda()
+        else:
+            codes = b.x[0].view(torch.float8_e4m3fn).to(torch.float32)
+            scales = b.x[1].view(torch.float32).repeat_interleave(128, dim=-1)
+            want = (codes * scales).to(torch.bfloat16).view(torch.int16)
+        same = (g == want) | (((g & 0x7FFF) == 0) & ((want & 0x7FFF) == 0))   # +0 == -0
+        res["out_tokens_closed_form"] = N * T
+        res["out_tokens_closed_form_bad"] = int((~same.all(dim=-1)).sum().item())
+    res["pass"] = (not bad_tables and bad_send == 0 and bad_grp == 0
+                   and res.get("quantised_rows_bad", 0) == 0 and res["out_elements_off"] == 0
+                   and res.get("out_tokens_closed_form_bad", 0) == 0)
+    return res
 
 
 def measure_split(ep, torch, d, b, sh, P: int, steps: int, warmup: int) -> dict:
@@ -415,26 +607,114 @@ def measure_staged(ep, torch, d, sh, wl, steps: int, warmup: int) -> dict:
     return out
 
 
+def setup(ep, torch, np, W, name: str):
+    """Workload, caller-owned buffers, inputs in HBM and the stand-in
+    expert's output (computed once, outside any timing)."""
+    sh = W.CONFIGS[name]
+    wl = W.make_workload(sh)
+    d = ep.make_desc(sh.n_ranks, sh.tokens, sh.hidden, sh.n_experts, sh.topk, sh.payload)
+    b = ep.Buffers(d, device="cuda:0")
+    b.idx.copy_(torch.from_numpy(wl.idx))
+    b.weights.copy_(torch.from_numpy(wl.weights))
+    for q, plane in enumerate(wl.planes):
+        b.x[q].copy_(torch.from_numpy(plane))
+    alpha = torch.from_numpy(wl.alpha).cuda() if wl.alpha is not None else None
+    return sh, wl, d, b, alpha
+
+
+def describe(sh, W, quant: bool) -> str:
+    if sh.payload == W.PAYLOAD_BF16:
+        payload = "bf16"
+    elif quant:
+        payload = "fp8 e4m3 + fp32 scale per 128 values, quantised in the sender"
+    else:
+        payload = "fp8 e4m3 + fp32 scale per 128 values, pre-quantised"
+    return (f"{sh.name}: N={sh.n_ranks} virtual ranks, T={sh.tokens} tokens/rank, "
+            f"H={sh.hidden} bf16 tokens, dispatch payload {payload}, E={sh.n_experts} experts, "
+            f"top-{sh.topk} {sh.routing} routing, softmax weights, stand-in expert = {sh.expert}")
+
+
+# Per-config protocol: iterations, and whether a cache flush precedes each
+# step (the large workloads) or the steps run back to back (the tiny ones,
+# which are launch-bound and report microseconds only).
+CONFIG_PROTOCOL = {"tiny": (200, False), "tiny_zipf": (200, False), "decode": (100, True),
+                   "worst": (100, True), "prefill": (30, True), "decode_zipf": (100, True),
+                   "decode_fp8": (100, True)}
+
+
+def run_config(ep, torch, np, W, name: str, flush, warmup: int = 20) -> dict:
+    """One workload under its protocol: dispatch + combine steps timed on
+    the device, then the parity of its buffers with the oracle (the whole
+    oracle path for the tiny workloads, sampled tokens plus closed forms for
+    the others)."""
+    import oracle
+
+    steps, flushed = CONFIG_PROTOCOL[name]
+    sh, wl, d, b, alpha = setup(ep, torch, np, W, name)
+    quant = sh.payload == W.PAYLOAD_FP8_B128
+    x_bf16 = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda() if quant else None
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        if quant:
+            ep.dispatch_quant(d, b.idx, x_bf16, b.plan_ws, b.send, b.grouped, b.status, sp)
+        else:
+            ep.dispatch(d, b.idx, b.x, b.plan_ws, b.send, b.grouped, b.status, sp)
+        ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, sp)
+
+    b.status.zero_()
+    step()
+    ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out, sp)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    row_d = sum(ep.row_bytes(d, q) for q in range(ep.num_planes(d)))
+    ab = algorithmic_bytes(sh, row_d, quant)
+    res = {"workload": describe(sh, W, quant), "steps": steps, "warmup": warmup,
+           "step_form": ("ep_dispatch_quant" if quant else "ep_dispatch") + " then ep_combine",
+           "algorithmic_bytes_per_step": ab["step"]}
+    b2b = time_back_to_back(torch, stream, step, steps)
+    if flushed:
+        ts = time_flushed(torch, stream, step, steps, flush)
+        us = statistics.median(ts)
+        res.update(flushed=True, us_p10_p50_p90=pcts(np, ts),
+                   us_mean=round(statistics.mean(ts), 2), back_to_back_us=round(b2b, 2))
+    else:
+        us = b2b
+        res.update(flushed=False, us_back_to_back=round(b2b, 2))
+    res["effective_GBps"] = round(ab["step"] / us / 1e3, 1)
+    res["frac_of_hbm_peak"] = round(ab["step"] / us / 1e3 / HBM_PEAK_GBPS, 4)
+    if name in ("tiny", "tiny_zipf"):
+        ref = oracle.run(wl, cap=ep.capacity(d))
+        res["parity"] = bench_parity(ep, torch, np, d, b, sh, wl, quant, oracle_out=ref["out"])
+    else:
+        res["parity"] = bench_parity(ep, torch, np, d, b, sh, wl, quant)
+    del b, x_bf16
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=100,
+                    help="timed steps of the headline workload, each after a cache flush")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode")
+    ap.add_argument("--configs", default="tiny,tiny_zipf,prefill,worst",
+                    help="further workloads measured under their own protocol and reported "
+                         "in the line's 'configs' object ('' for none)")
     ap.add_argument("--sample-every", type=int, default=10,
-                    help="record per-stage events on every n-th timed step")
+                    help="record per-stage events on every n-th back-to-back step")
     ap.add_argument("--prequantized", action="store_true",
                     help="fp8 payloads: send pre-quantised rows with the plain sender "
                          "instead of quantising bf16 rows in the sender")
-    ap.add_argument("--flushed-steps", type=int, default=20,
-                    help="extra steps, each after a 1 GiB fill and a 1 GiB read that evict the caches, "
-                         "timed one by one (reported beside the main figure)")
     ap.add_argument("--split", type=int, default=-1, metavar="P",
                     help="also measure the split dispatch with P private rows per "
                          "(destination, source) pair, alone and overlapped with a "
                          "shared-expert stand-in on a second stream")
     ap.add_argument("--graph", action="store_true",
-                    help="capture the timed steps as one HIP graph and replay it (removes "
+                    help="capture K steps as one HIP graph and replay it (removes "
                          "launch overhead; matters for launch-bound small workloads)")
     ap.add_argument("--staged", action="store_true",
                     help="also time the materialised network write + unpack against the "
@@ -444,7 +724,8 @@ def main() -> int:
     ap.add_argument("--kv", action="store_true",
                     help="also measure the KV-block push (merged, per-block, staged)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
-                    help="seconds of oracle CPU work for the baseline (0 = skip)")
+                    help="seconds of oracle CPU work for the baseline (0 = skip; the parity "
+                         "check then runs the oracle once)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the EP group's ranks are virtual ranks on one "
@@ -458,20 +739,13 @@ def main() -> int:
     import ep_workloads as W
 
     torch.cuda.set_device(0)
-    sh = W.CONFIGS[args.config]
-    wl = W.make_workload(sh)
-    d = ep.make_desc(sh.n_ranks, sh.tokens, sh.hidden, sh.n_experts, sh.topk, sh.payload)
-    b = ep.Buffers(d, device="cuda:0")
-    b.idx.copy_(torch.from_numpy(wl.idx))
-    b.weights.copy_(torch.from_numpy(wl.weights))
-    for q, plane in enumerate(wl.planes):
-        b.x[q].copy_(torch.from_numpy(plane))
-    alpha = torch.from_numpy(wl.alpha).cuda() if wl.alpha is not None else None
+    sh, wl, d, b, alpha = setup(ep, torch, np, W, args.config)
     quant = sh.payload == W.PAYLOAD_FP8_B128 and not args.prequantized
     x_bf16 = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda() if quant else None
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     row_d = sum(ep.row_bytes(d, q) for q in range(ep.num_planes(d)))
+    flush = Flusher(torch)
 
     def pack():
         if quant:
@@ -480,6 +754,7 @@ def main() -> int:
             ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)
 
     # expert outputs once (outside timing)
+    b.status.zero_()
     ep.plan(d, b.idx, b.plan_ws, b.status, sp)
     pack()
     ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp)
@@ -506,7 +781,7 @@ def main() -> int:
         if ev is not None:
             ev[4].record(stream)
 
-    def fused_step(ev=None):
+    def step(ev=None):
         """ep_dispatch / ep_dispatch_quant (plan + pack + receive, the count
         exchange folded into the sender launch) and ep_combine."""
         if ev is not None:
@@ -521,26 +796,34 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
 
-    # A step is the one-call dispatch and the combine.
-    step = fused_step
-    n_ev = 3
     for _ in range(args.warmup):
         step()
-    # Events only on every `sample_every`-th step: an event record between
-    # two kernels costs a few microseconds of GPU time.
+    torch.cuda.synchronize()
+
+    # Back to back: K steps queued between two events (events on every
+    # `sample_every`-th step split dispatch from combine: an event record
+    # between two kernels costs a few microseconds of GPU time).
     sampled = list(range(0, args.steps, args.sample_every))
-    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for i in sampled}
+    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
         step(events.get(i))
     t_end.record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    steps_ms = [ev[0].elapsed_time(ev[-1]) for ev in events.values()]
+    b2b_us = t_start.elapsed_time(t_end) * 1e3 / args.steps
+    steps_us = [ev[0].elapsed_time(ev[-1]) * 1e3 for ev in events.values()]
     dispatch_call_us = statistics.mean(ev[0].elapsed_time(ev[1]) for ev in events.values()) * 1e3
+
+    # The timed region: K steps, each after a cache flush (outside its
+    # events), as a model layer finds the caches after other kernels ran.
+    t0 = time.perf_counter()
+    flushed = time_flushed(torch, stream, step, args.steps, flush)
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    us_per_step = statistics.mean(flushed)
+    ms_per_step = us_per_step / 1e3
+    status_after = int(b.status.item())
 
     graph_step_us = None
     if args.graph:
@@ -567,9 +850,8 @@ def main() -> int:
         torch.cuda.synchronize()
         graph_step_us = g0.elapsed_time(g1) * 1e3 / args.steps
         del graph
-    # Per-stage times (and the dominant kernel's) from the four separate
-    # calls, after the timed region; the receiver kernel is the same launch
-    # in both forms of the step.
+    # Per-stage times from the four separate calls, after the timed region;
+    # the receiver kernel is the same launch in both forms of the step.
     stage_names = ["plan", "pack", "recv", "combine"]
     per = {n: [] for n in stage_names}
     stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -583,8 +865,6 @@ def main() -> int:
     for ev in stage_ev:
         for j, n in enumerate(stage_names):
             per[n].append(ev[j].elapsed_time(ev[j + 1]))
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
     ab = algorithmic_bytes(sh, row_d, quant)
     eff = ab["step"] / (ms_per_step * 1e-3) / 1e9
 
@@ -619,36 +899,18 @@ def main() -> int:
 
     # copy ceiling of this GPU with the library's own row-copy loop (context)
     nbytes = 1 << 30
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
-    dst = torch.empty_like(src)
+    csrc = flush.a
+    cdst = torch.empty_like(csrc)
     for _ in range(3):
-        ep.probe_copy(dst, src, nbytes, sp)
+        ep.probe_copy(cdst, csrc, nbytes, sp)
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record(stream)
     for _ in range(10):
-        ep.probe_copy(dst, src, nbytes, sp)
+        ep.probe_copy(cdst, csrc, nbytes, sp)
     c1.record(stream)
     torch.cuda.synchronize()
     copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-
-    # Cold-cache steps: before each one (outside the events) a 1 GiB fill and
-    # a 1 GiB read with ordinary stores and loads evict what the previous step
-    # left in the L2s and the MALL. (The library's copy probe would not: its
-    # non-temporal accesses leave cached lines in place, and so do the
-    # receiver's and the combine's, which is why back-to-back steps find the
-    # previous sender's token rows still in each XCD's L2.) Each step is timed
-    # alone between two events.
-    flushed = []
-    for i in range(args.flushed_steps):
-        dst.fill_(i & 0xff)
-        src.view(torch.int32).max()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        step()
-        f1.record(stream)
-        torch.cuda.synchronize()
-        flushed.append(f0.elapsed_time(f1) * 1e3)
-    del src, dst
+    del cdst
 
     split = None
     if args.split >= 0:
@@ -666,9 +928,15 @@ def main() -> int:
     if args.kv:
         kv = measure_kv(ep, torch, np, W)
 
+    # The oracle: timed as the CPU baseline, and its result is what the
+    # benchmarked buffers are compared with (the last step's plan tables,
+    # send and grouped rows, and every combined token).
+    import oracle
     cpu = None
     if args.cpu_budget > 0:
         base = cpu_baseline(sh, wl, args.cpu_budget, quant)
+        oracle_out = base["out"]
+        host = cpu_host()
         sample = (f"the whole {sh.name} workload, {base['runs']} run(s) of the plain-C "
                   f"oracle (plan, pack, per-pair transfer, unpack, combine; stand-in "
                   f"expert not timed), median {base['median_s']:.3f} s")
@@ -682,14 +950,19 @@ def main() -> int:
             "kind": "oracle",
             "sample": sample,
             "us_per_step": base["median_s"] * 1e6,
+            "threads": 1,
+            "host_nproc": host["nproc"],
+            "host_cpus_allowed": host["cpus_allowed"],
+            "host_cpu_model": host["model"],
         }
-
-    if sh.payload == W.PAYLOAD_BF16:
-        payload_name = "bf16"
-    elif quant:
-        payload_name = "fp8 e4m3 + fp32 scale per 128 values, quantised in the sender"
+        del base
     else:
-        payload_name = "fp8 e4m3 + fp32 scale per 128 values, pre-quantised"
+        oracle_out = oracle.run(wl, cap=ep.capacity(d))["out"]
+    # the plan, send rows and grouped rows of the last four-call pass (equal
+    # by construction to the timed steps'), the combine of the last one
+    parity = bench_parity(ep, torch, np, d, b, sh, wl, quant, oracle_out=oracle_out)
+    parity["status_after_timed_steps"] = status_after
+
     traffic = recorded_traffic(args.config, "pack_quant" if dom == "pack" and quant else dom)
     res = {
         "metric": METRIC,
@@ -706,15 +979,18 @@ def main() -> int:
         "accumulate": "f32",
         "data": "synthetic",
         "config": {
-            "workload": (f"{sh.name}: N={sh.n_ranks} virtual ranks, T={sh.tokens} tokens/rank, "
-                         f"H={sh.hidden} bf16 tokens, dispatch payload {payload_name}, "
-                         f"E={sh.n_experts} experts, top-{sh.topk} {sh.routing} routing, "
-                         f"softmax weights, stand-in expert = {sh.expert}"),
+            "workload": describe(sh, W, quant),
             "parallelism": "ep (virtual ranks on one GPU)",
             "global_batch": sh.n_ranks * sh.tokens,
         },
-        "us_per_dispatch_combine": round(ms_per_step * 1e3, 2),
-        "us_per_virtual_rank": round(ms_per_step * 1e3 / sh.n_ranks, 3),
+        "timing": ("each of the K timed steps follows a 1 GiB fill and a 1 GiB read that "
+                   "evict the L2s and the MALL, and is timed alone between two HIP events; "
+                   "value and ms_per_step use the mean of the K steps"),
+        "us_per_dispatch_combine": round(us_per_step, 2),
+        "us_p10_p50_p90": pcts(np, flushed),
+        "back_to_back_us_per_step": round(b2b_us, 2),
+        "back_to_back_frac_of_hbm_peak": round(ab["step"] / b2b_us / 1e3 / HBM_PEAK_GBPS, 4),
+        "us_per_virtual_rank": round(us_per_step / sh.n_ranks, 3),
         "expert_stand_in_us": round(expert_us, 2),
         "frac_of_hbm_peak": round(eff / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": ab["step"],
@@ -725,12 +1001,8 @@ def main() -> int:
             "graph_from": "the K steps captured as one HIP graph, one replay between two events"}
            if graph_step_us is not None else {}),
         "stages_us": {n: round(statistics.mean(per[n]) * 1e3, 2) for n in stage_names},
-        "stages_from": "the four separate calls, sampled after the timed steps",
-        "instrumented_step_us_p10_p50_p90": [round(float(np.percentile(steps_ms, q)) * 1e3, 2)
-                                             for q in (10, 50, 90)],
-        "instrumented_steps": len(steps_ms),
-        "cold_cache_step_us_p10_p50_p90": ([round(float(np.percentile(flushed, q)), 2)
-                                            for q in (10, 50, 90)] if flushed else None),
+        "stages_from": "the four separate calls, back to back, after the timed steps",
+        "instrumented_step_us_p10_p50_p90": pcts(np, steps_us),
         "wall_ms": round(wall_ms, 3),
         "roofline": {
             "kernel": f"ep_dispatch_{dom}" if dom in ("pack", "recv") else f"ep_{dom}",
@@ -747,6 +1019,7 @@ def main() -> int:
             "avg_us_from": "20 launches back to back between two HIP events on the launch stream",
         },
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "parity": parity,
         "cpu_baseline": cpu,
     }
     if split is not None:
@@ -757,6 +1030,19 @@ def main() -> int:
         res["kv_push"] = kv
     if staged is not None:
         res["staged_receive"] = staged
+
+    # the other workloads, each under its own protocol, after freeing this one
+    names = [n for n in args.configs.split(",") if n and n != args.config]
+    if names:
+        del b, x_bf16, alpha
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        res["configs"] = {}
+        for n in names:
+            res["configs"][n] = run_config(ep, torch, np, W, n, flush)
+            gc.collect()
+            torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
     return 0
 
