@@ -956,8 +956,10 @@ def main() -> int:
             "host_cpu_model": host["model"],
         }
         del base
-    else:
+    elif sh.n_ranks * sh.tokens * sh.hidden <= 1 << 25:
         oracle_out = oracle.run(wl, cap=ep.capacity(d))["out"]
+    else:
+        oracle_out = None     # sampled tokens and closed forms (bench_parity)
     # the plan, send rows and grouped rows of the last four-call pass (equal
     # by construction to the timed steps'), the combine of the last one
     parity = bench_parity(ep, torch, np, d, b, sh, wl, quant, oracle_out=oracle_out)

@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""Turn rocprofv3 outputs of bench.py runs into the summaries under profiles/.
+
+Two summaries per workload:
+
+  trace    rocprofv3 --kernel-trace --stats of one bench.py run ->
+           profiles/<workload>_kernel_trace.md (calls and durations per kernel)
+  traffic  two rocprofv3 --pmc runs of the same bench.py command, FETCH_SIZE
+           in one and WRITE_SIZE in the other (one counter per run) ->
+           profiles/<workload>_hbm_traffic.md and profiles/traffic_<workload>.json
+
+Traffic calibration: bench.py's copy-ceiling leg launches the library's copy
+probe on 1 GiB (1 GiB read, 1 GiB written per launch); each counter's reading
+for that launch gives the factor that turns the counter into bytes. The JSON
+records, per stage, the source hash of the kernels it was measured on;
+bench.py only reports the traffic while the built kernels still hash the same.
+
+Usage (after the rocprofv3 runs, whose commands the summaries quote):
+  python3 bench_profiles.py trace WORKLOAD STATS_CSV "BENCH_ARGS"
+  python3 bench_profiles.py traffic WORKLOAD FETCH_CSV WRITE_CSV STATS_CSV "BENCH_ARGS"
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import json
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Kernels of each stage (the first one present is the stage's kernel; the
+# plan stage sums its kernels).
+STAGE_KERNELS = {
+    "plan": [["plan_count_kernel", "plan_finalize_kernel"], ["plan_fused_kernel"]],
+    "plan_local": [["plan_count_local_kernel"]],
+    "pack": [["pack_gather_kernel<false, false>"], ["pack_fast1_kernel<14>"],
+             ["pack_fast2_kernel<7, 1>"], ["pack_kernel"]],
+    "pack_exchange": [["pack_gather_kernel<true, false>"], ["pack_exchange_kernel<14, 0>"]],
+    "pack_quant": [["pack_quant_tok_kernel<false>"], ["pack_quant_kernel"]],
+    "pack_quant_exchange": [["pack_quant_tok_kernel<true>"], ["pack_quant_exchange_kernel"]],
+    "recv": [["recv_rows_kernel<false>"]],
+    "combine": [["combine_kernel<7, 2, 2>"], ["combine_kernel<2, 7, 2>"]],
+}
+COPY_KERNEL = "probe_copy_kernel"
+
+
+def short(name: str) -> str:
+    n = name.replace("void ", "").replace("ep::(anonymous namespace)::", "")
+    m = re.match(r"([\w:]+(<[^()]*>)?)", n)
+    return m.group(1) if m else n[:60]
+
+
+def command(args: str, extra: str) -> str:
+    return ("cd /tmp && export TMPDIR=/tmp && rocprofv3 " + extra +
+            " --output-format csv -d <out> -o run -- python3 /root/repo/bench.py " + args).strip()
+
+
+def read_stats(path: str):
+    rows = list(csv.DictReader(open(path)))
+    return rows, {short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
+
+
+def trace(workload: str, stats_csv: str, args: str) -> str:
+    rows, _ = read_stats(stats_csv)
+    out = [f"# Kernel trace: {workload} workload", "",
+           "Command (MI355X, one GPU):", "", "```",
+           command(args, "--kernel-trace --stats"), "```", "",
+           "rocprofv3 kernel statistics over every dispatch of the run: warm-up, back-to-back",
+           "and flushed steps, the per-stage loop of four separate calls, the dominant kernel's",
+           "20 launches, the stand-in expert, the copy probe and the torch kernels that evict",
+           "the caches between flushed steps.", "",
+           "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    path = os.path.join(PROFILES, f"{workload}_kernel_trace.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    return path
+
+
+def counter_means(path: str) -> dict:
+    """Mean counter value per dispatch, per kernel."""
+    agg = collections.defaultdict(list)
+    per = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(path)):
+        i = int(r["Dispatch_Id"])
+        per[i] += float(r["Counter_Value"])
+        names[i] = short(r["Kernel_Name"])
+    for i, v in per.items():
+        agg[names[i]].append(v)
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def traffic(workload: str, fetch_csv: str, write_csv: str, stats_csv: str, args: str):
+    import bench
+    import ep_workloads as W
+
+    fetch = counter_means(fetch_csv)
+    write = counter_means(write_csv)
+    _, avg = read_stats(stats_csv)
+    copy_kib = (1 << 30) / 1024
+    ff = copy_kib / fetch[COPY_KERNEL]
+    wf = copy_kib / write[COPY_KERNEL]
+    sh = W.CONFIGS[workload]
+    quant = sh.payload == W.PAYLOAD_FP8_B128 and "--prequantized" not in args
+    row_d = 2 * sh.hidden if sh.payload == W.PAYLOAD_BF16 else sh.hidden + 4 * (sh.hidden // 128)
+    ab = bench.algorithmic_bytes(sh, row_d, quant)["stages"]
+    alg = dict(ab)
+    alg["plan_local"] = ab["plan"]
+    alg["pack_exchange"] = ab["pack"]
+    alg["pack_quant"] = ab["pack"]
+    alg["pack_quant_exchange"] = ab["pack"]
+    rec = {"workload": workload, "bench_args": args, "fetch_factor": round(ff, 4),
+           "write_factor": round(wf, 4),
+           "calibration": "probe_copy_kernel, 1 GiB read + 1 GiB written per launch",
+           "stages": {}}
+    md = [f"# HBM traffic per launch: {workload} workload", "",
+          "Commands (MI355X, one GPU), one counter per run, then this summary:", "", "```",
+          command(args, "--pmc FETCH_SIZE"), command(args, "--pmc WRITE_SIZE"),
+          command(args, "--kernel-trace --stats"),
+          f"python3 bench_profiles.py traffic {workload} <fetch csv> <write csv> <stats csv> "
+          f"\"{args}\"", "```", "",
+          "Calibration against the copy probe of the same run (1 GiB read, 1 GiB written per "
+          f"launch): FETCH_SIZE reads {1 / ff:.3f}x the true bytes (factor {ff:.4f}), WRITE_SIZE "
+          f"{1 / wf:.3f}x (factor {wf:.4f}). Counter values are means over every launch of the "
+          "kernel in the run (warm and flushed alike); durations are the kernel trace's means.", "",
+          "| stage | kernel | FETCH KiB (raw) | WRITE KiB (raw) | calibrated traffic bytes | "
+          "algorithmic bytes | traffic / algorithmic | avg us (trace) | algorithmic GB/s |",
+          "|---|---|---|---|---|---|---|---|---|"]
+    for stage, options in STAGE_KERNELS.items():
+        ks = next((o for o in options if all(k in fetch and k in write for k in o)), None)
+        if ks is None:
+            continue
+        if stage in ("pack", "pack_exchange") and quant:
+            continue
+        fk = sum(fetch[k] for k in ks)
+        wk = sum(write[k] for k in ks)
+        t = int(fk * 1024 * ff + wk * 1024 * wf)
+        us = sum(avg.get(k, float("nan")) for k in ks)
+        a = alg[stage]
+        rec["stages"][stage] = {
+            "kernels": ks, "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+            "traffic_bytes": t, "algorithmic_bytes": a,
+            "traffic_over_algorithmic": round(t / a, 4), "avg_us": round(us, 2),
+            "sources": bench.STAGE_SOURCES[stage],
+            "source_sha256_16": bench.kernel_source_hash(bench.STAGE_SOURCES[stage])}
+        md.append(f"| {stage} | {' + '.join(ks)} | {fk:.1f} | {wk:.1f} | {t} | {a} | "
+                  f"{t / a:.4f} | {us:.2f} | {a / us / 1e3:.1f} |")
+    md += ["",
+           "The plan stages' algorithmic bytes count only the routing ids; their traffic "
+           "includes the plan tables they write (and, for plan_local, the token rows it "
+           "touches for the sender).",
+           "traffic_" + workload + ".json holds these figures with a source hash per stage; "
+           "bench.py reports a stage's traffic only while its kernels hash the same."]
+    p_md = os.path.join(PROFILES, f"{workload}_hbm_traffic.md")
+    p_js = os.path.join(PROFILES, f"traffic_{workload}.json")
+    with open(p_md, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    with open(p_js, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return p_md, p_js
+
+
+def main(argv) -> int:
+    if len(argv) >= 4 and argv[0] == "trace":
+        print(trace(argv[1], argv[2], argv[3]))
+        return 0
+    if len(argv) >= 6 and argv[0] == "traffic":
+        print(*traffic(argv[1], argv[2], argv[3], argv[4], argv[5]))
+        return 0
+    print(__doc__, file=sys.stderr)
+    return 2
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

@@ -34,6 +34,13 @@ constexpr int64_t kGatherSourceBytes = 4 << 20;
 constexpr int64_t kWindowSourceBytes = 32 << 20;
 constexpr int64_t kWindowSendBytes = (int64_t)2 << 30;
 
+// Token rows the send-side plan launch touches for the sender (per plane:
+// base pointer, or null, and one source's bytes).
+struct RowTouch {
+  const uint8_t* src[2];
+  int64_t bytes[2];
+};
+
 // Plan workspace pointers (int32 arrays, see ep_plan_view).
 struct PlanPtrs {
   int32_t *cnt, *send_off, *send_pos, *recv_off, *grp_off, *grp_pos, *src_off,
@@ -58,8 +65,13 @@ hipError_t launch_window_list(const Dims& d, const PlanPtrs& p, hipStream_t stre
 // Split dispatch: the sender half's plan (no data of other ranks), the
 // receiver half's exchange, and the two data movers with private regions of
 // P rows per (destination, source) pair.
+// touch_x (optional, plane pointers of the token rows): the send-side plan
+// launch, when it is one launch (d.nchunks == 1), also reads one dword of
+// every 128-byte line of the token rows, so that the sender that follows
+// finds them in the memory-side cache instead of HBM.
 hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
-                             int32_t* status, hipStream_t stream, bool with_window = true);
+                             int32_t* status, hipStream_t stream, bool with_window = true,
+                             const void* const* touch_x = nullptr);
 hipError_t launch_plan_exchange(const Dims& d, const PlanPtrs& p, int32_t* status,
                                 hipStream_t stream);
 hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* const x[2],

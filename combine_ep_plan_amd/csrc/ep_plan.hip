@@ -175,12 +175,47 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
                                (int64_t)gridDim.x * gridDim.y);
 }
 
+// Block x of source s touches lines [x * kTouchLines, (x + 1) * kTouchLines)
+// of s's token rows in each plane: one dword of each 128-byte line with an
+// ordinary load, which brings the line into the memory-side cache (MALL).
+// The values are only held until they arrive. Two lines per thread spread
+// the touch over about one block per CU at decode scale; with eight per
+// thread (a quarter of the blocks) the flushed decode step took 340 against
+// 330 us, with one 330 us.
+constexpr int kTouchPerThread = 2;
+constexpr int64_t kTouchLines = (int64_t)kPlanThreads * kTouchPerThread;
+
+__device__ __forceinline__ void touch_rows(const RowTouch& t, int s, int x) {
+  uint32_t acc = 0;
+  for (int q = 0; q < 2; ++q) {
+    if (t.src[q] == nullptr) continue;
+    const int64_t bytes = t.bytes[q];
+    const uint8_t* base = t.src[q] + (size_t)s * bytes;
+    uint32_t v[kTouchPerThread];
+#pragma unroll
+    for (int k = 0; k < kTouchPerThread; ++k) {
+      const int64_t line = (int64_t)x * kTouchLines + (int64_t)k * kPlanThreads + threadIdx.x;
+      const int64_t off = line * 128 < bytes ? line * 128 : 0;
+      v[k] = *(const uint32_t*)(base + off);
+    }
+#pragma unroll
+    for (int k = 0; k < kTouchPerThread; ++k) acc ^= v[k];
+  }
+  asm volatile("" ::"v"(acc));
+}
+
 // Send side of the plan in one launch when a source's slots fit one chunk
 // (T R <= kPlanChunk): ranks, counts and the scan together, so the send
-// offsets and final positions need no chunk-count round trip. Grid (1, N).
+// offsets and final positions need no chunk-count round trip. Grid
+// (1 + touch blocks, N): block (0, s) plans source s; blocks (x > 0, s)
+// touch s's token rows for the sender that follows (see RowTouch).
 __global__ __launch_bounds__(kPlanThreads) void plan_count_local_kernel(
     const int32_t* __restrict__ idx, int E, int L, int64_t TR, PlanPtrs p,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ status, RowTouch touch) {
+  if (blockIdx.x > 0) {  // block-uniform
+    touch_rows(touch, (int)blockIdx.y, (int)blockIdx.x - 1);
+    return;
+  }
   extern __shared__ int32_t lds[];
   constexpr int kWaves = kPlanThreads / kWave;
   int32_t* soff = lds;                        // [E+1]
@@ -341,12 +376,25 @@ hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
 }
 
 hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
-                             int32_t* status, hipStream_t stream, bool with_window) {
+                             int32_t* status, hipStream_t stream, bool with_window,
+                             const void* const* touch_x) {
   hipError_t e = allow_large_lds();
   if (e != hipSuccess) return e;
   if (d.nchunks == 1) {
-    hipLaunchKernelGGL(plan_count_local_kernel, dim3(1, d.N), dim3(kPlanThreads),
-                       lds_count_local_bytes(d), stream, idx, d.E, d.L, d.TR, p, status);
+    RowTouch t{};
+    int touch_blocks = 0;
+    if (touch_x != nullptr && d.T > 0) {
+      int64_t lines = 0;
+      for (int q = 0; q < d.planes; ++q) {
+        t.src[q] = (const uint8_t*)touch_x[q];
+        t.bytes[q] = (int64_t)d.T * d.row[q];
+        const int64_t lq = (t.bytes[q] + 127) / 128;
+        lines = lq > lines ? lq : lines;
+      }
+      touch_blocks = (int)((lines + kTouchLines - 1) / kTouchLines);
+    }
+    hipLaunchKernelGGL(plan_count_local_kernel, dim3(1 + touch_blocks, d.N), dim3(kPlanThreads),
+                       lds_count_local_bytes(d), stream, idx, d.E, d.L, d.TR, p, status, t);
   } else {
     e = launch_count(d, idx, p, status, stream);
     if (e != hipSuccess) return e;
