@@ -607,6 +607,94 @@ def measure_staged(ep, torch, d, sh, wl, steps: int, warmup: int) -> dict:
     return out
 
 
+def measure_probe(ep, torch, np, W, names, flush) -> dict:
+    """Kernel-level probe behind the design's sender and copy figures (and
+    the counter summaries under profiles/, which run it under rocprofv3):
+      - per workload, steps of the four separate calls (ep_plan, the sender
+        -- ep_dispatch_pack, or the quantising sender for fp8 workloads --,
+        ep_dispatch_recv, ep_combine) with an event between stages: 3
+        untimed, then 5 back to back, 5 each after a cache flush, and 5 each
+        after a cache flush followed by a read of the token rows (torch max,
+        ordinary loads); the median per stage (us);
+      - the library's copy probe on 0.5, 1, 2 and 3 GiB, 3 launches each,
+        each launch alone between two HIP events."""
+    import gc
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    res = {}
+    stage_names = ("plan", "sender", "recv", "combine")
+    for name in names:
+        sh, wl, d, b, alpha = setup(ep, torch, np, W, name)
+        quant = sh.payload == W.PAYLOAD_FP8_B128
+        xq = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda() if quant else None
+        xs = xq if quant else b.x[0]
+
+        def step(ev=None):
+            calls = (lambda: ep.plan(d, b.idx, b.plan_ws, b.status, sp),
+                     (lambda: ep.dispatch_pack_quant(d, xq, b.plan_ws, b.send, sp)) if quant
+                     else (lambda: ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)),
+                     lambda: ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp),
+                     lambda: ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, sp))
+            for j, c in enumerate(calls):
+                if ev is not None:
+                    ev[j].record(stream)
+                c()
+            if ev is not None:
+                ev[4].record(stream)
+
+        def phase(pre):
+            per = []
+            for i in range(5):
+                if pre is not None:
+                    pre(i)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                step(ev)
+                if pre is not None:
+                    torch.cuda.synchronize()
+                per.append(ev)
+            torch.cuda.synchronize()
+            return {n: round(float(np.median([e[j].elapsed_time(e[j + 1]) * 1e3 for e in per])), 2)
+                    for j, n in enumerate(stage_names)}
+
+        b.status.zero_()
+        step()
+        ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out, sp)
+        step()
+        step()
+        torch.cuda.synchronize()
+        row_d = sum(ep.row_bytes(d, q) for q in range(ep.num_planes(d)))
+        res[name] = {
+            "sender": "ep_dispatch_pack_quant" if quant else "ep_dispatch_pack",
+            "algorithmic_bytes": algorithmic_bytes(sh, row_d, quant)["stages"],
+            "back_to_back_us": phase(None),
+            "after_flush_us": phase(flush),
+            "after_flush_and_token_read_us": phase(
+                lambda i: (flush(i), xs.view(torch.int32).max())),
+        }
+        del b, xq, xs
+        gc.collect()
+        torch.cuda.empty_cache()
+    copies = {}
+    for gib in (0.5, 1, 2, 3):
+        n = int(gib * (1 << 30))
+        src = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ep.probe_copy(dst, src, n, sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(round(e0.elapsed_time(e1) * 1e3, 2))
+        copies[f"{gib:g}GiB"] = {"us": ts, "TBps": [round(2 * n / t / 1e6, 3) for t in ts]}
+        del src, dst
+        torch.cuda.empty_cache()
+    res["copy_probe"] = copies
+    return res
+
+
 def setup(ep, torch, np, W, name: str):
     """Workload, caller-owned buffers, inputs in HBM and the stand-in
     expert's output (computed once, outside any timing)."""
@@ -723,6 +811,10 @@ def main() -> int:
                     help="also measure the combine with partial sums on the expert side")
     ap.add_argument("--kv", action="store_true",
                     help="also measure the KV-block push (merged, per-block, staged)")
+    ap.add_argument("--probe", default="", metavar="WORKLOADS",
+                    help="only run the kernel-level probe (the sender back to back, after a "
+                         "cache flush, and after a flush plus a read of the token rows, for "
+                         "each listed workload; the copy probe at 0.5-3 GiB) and print it")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0 = skip; the parity "
                          "check then runs the oracle once)")
@@ -739,6 +831,11 @@ def main() -> int:
     import ep_workloads as W
 
     torch.cuda.set_device(0)
+    if args.probe:
+        probe = measure_probe(ep, torch, np, W, [n for n in args.probe.split(",") if n],
+                              Flusher(torch))
+        print(json.dumps({"probe": probe}), flush=True)
+        return 0
     sh, wl, d, b, alpha = setup(ep, torch, np, W, args.config)
     quant = sh.payload == W.PAYLOAD_FP8_B128 and not args.prequantized
     x_bf16 = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda() if quant else None

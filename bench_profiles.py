@@ -15,9 +15,14 @@ for that launch gives the factor that turns the counter into bytes. The JSON
 records, per stage, the source hash of the kernels it was measured on;
 bench.py only reports the traffic while the built kernels still hash the same.
 
+A third summary tabulates counter runs of `bench.py --probe` (the senders
+back to back, after a cache flush and after a flush plus a read of the token
+rows; the copy probe at 0.5-3 GiB).
+
 Usage (after the rocprofv3 runs, whose commands the summaries quote):
   python3 bench_profiles.py trace WORKLOAD STATS_CSV "BENCH_ARGS"
   python3 bench_profiles.py traffic WORKLOAD FETCH_CSV WRITE_CSV STATS_CSV "BENCH_ARGS"
+  python3 bench_profiles.py probe TITLE WORKLOADS TIMING_JSON COUNTER_CSV...
 """
 from __future__ import annotations
 
@@ -65,10 +70,14 @@ def read_stats(path: str):
 
 
 def trace(workload: str, stats_csv: str, args: str) -> str:
+    """Kernel statistics of one run; with the per-dispatch trace beside the
+    statistics file, also grouped by kernel and grid size, which tells the
+    workloads of one run apart (each launches its kernels on its own grid)."""
     rows, _ = read_stats(stats_csv)
-    out = [f"# Kernel trace: {workload} workload", "",
-           "Command (MI355X, one GPU):", "", "```",
-           command(args, "--kernel-trace --stats"), "```", "",
+    out = [f"# Kernel trace: {workload}", "",
+           "Command (MI355X, one GPU), then this summary:", "", "```",
+           command(args, "--kernel-trace --stats"),
+           f"python3 bench_profiles.py trace {workload} <stats csv> \"{args}\"", "```", "",
            "rocprofv3 kernel statistics over every dispatch of the run: warm-up, back-to-back",
            "and flushed steps, the per-stage loop of four separate calls, the dominant kernel's",
            "20 launches, the stand-in expert, the copy probe and the torch kernels that evict",
@@ -78,6 +87,24 @@ def trace(workload: str, stats_csv: str, args: str) -> str:
         out.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.1f}% |")
+    per_dispatch = os.path.join(os.path.dirname(stats_csv),
+                                os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    if os.path.exists(per_dispatch):
+        groups = collections.OrderedDict()
+        for r in csv.DictReader(open(per_dispatch)):
+            name = short(r["Kernel_Name"])
+            if not name.startswith(("plan_", "pack_", "recv_", "combine_", "expert_", "presum",
+                                    "kv_", "staged_", "window_", "probe_")):
+                continue
+            key = (name, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+            t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault(key, []).append(t)
+        out += ["", "The library's kernels by launch grid (threads), in order of first launch:", "",
+                "| kernel | grid threads | calls | avg us | min us | max us |",
+                "|---|---|---|---|---|---|"]
+        for (name, grid), ts in groups.items():
+            out.append(f"| {name} | {grid} | {len(ts)} | {sum(ts) / len(ts):.2f} | "
+                       f"{min(ts):.2f} | {max(ts):.2f} |")
     path = os.path.join(PROFILES, f"{workload}_kernel_trace.md")
     with open(path, "w") as fh:
         fh.write("\n".join(out) + "\n")
@@ -168,12 +195,92 @@ def traffic(workload: str, fetch_csv: str, write_csv: str, stats_csv: str, args:
     return p_md, p_js
 
 
+SENDER_KERNELS = ("pack_gather_kernel<false, false>", "pack_fast1_kernel<14>",
+                  "pack_fast2_kernel<7, 1>", "pack_kernel", "pack_quant_tok_kernel<false>",
+                  "pack_quant_kernel")
+
+
+def probe(title: str, workloads: str, timing_json: str, counter_csvs: list) -> str:
+    """Counter summary of `bench.py --probe WORKLOADS` runs: per workload the
+    sender launches in the probe's order (3 untimed steps, 5 back to back, 5
+    after a cache flush, 5 after a flush and a read of the token rows), then
+    the copy probe (3 launches each of 0.5, 1, 2, 3 GiB); per phase the mean of
+    each counter over the sender's launches, beside the event timings of an
+    unprofiled run."""
+    names = [n for n in workloads.split(",") if n]
+    with open(timing_json) as fh:
+        timing = json.loads(fh.read().strip().splitlines()[-1])["probe"]
+    phases = [("back to back", 3, 8), ("after flush", 8, 13), ("after flush + token read", 13, 18)]
+    table = collections.defaultdict(dict)   # (row label) -> counter -> value
+    counters = []
+    for path in counter_csvs:
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        kname = {}
+        for r in csv.DictReader(open(path)):
+            i = int(r["Dispatch_Id"])
+            per[i][r["Counter_Name"]] += float(r["Counter_Value"])
+            kname[i] = short(r["Kernel_Name"])
+        ids = sorted(per)
+        senders = [i for i in ids if kname[i] in SENDER_KERNELS]
+        copies = [i for i in ids if kname[i] == COPY_KERNEL]
+        cn = sorted({c for i in ids for c in per[i]})
+        counters += [c for c in cn if c not in counters]
+        for w, name in enumerate(names):
+            mine = senders[18 * w:18 * (w + 1)]
+            for label, a, b in phases:
+                for c in cn:
+                    v = [per[i][c] for i in mine[a:b]]
+                    table[(name, label)][c] = sum(v) / len(v)
+        for j, gib in enumerate(("0.5GiB", "1GiB", "2GiB", "3GiB")):
+            for c in cn:
+                v = [per[i][c] for i in copies[3 * j:3 * j + 3]]
+                table[("copy " + gib, "")][c] = sum(v) / len(v)
+    head = ["# " + title, "", "Commands (MI355X, one GPU): the event timings come from the first "
+            "run; each counter set from its own rocprofv3 run of the same probe; then this "
+            "summary.", "", "```", f"python3 /root/repo/bench.py --probe {workloads}"]
+    for c in counter_csvs:
+        sets = sorted({r["Counter_Name"] for r in csv.DictReader(open(c))})
+        head.append(command(f"--probe {workloads}", "--pmc " + " ".join(sets)))
+    head += [f"python3 bench_profiles.py probe \"{title}\" {workloads} <timing json> "
+             "<counter csv> ...", "```", "",
+             "Event timings (us, median of 5 steps of the four separate calls, each stage "
+             "between two events):", "",
+             "| workload | stage | algorithmic bytes | back to back | after flush | "
+             "after flush + token read |", "|---|---|---|---|---|---|"]
+    for name in names:
+        t = timing[name]
+        for st, key in (("plan", "plan"), ("sender", "pack"), ("recv", "recv"),
+                        ("combine", "combine")):
+            label = t["sender"] if st == "sender" else st
+            head.append(f"| {name} | {label} | {t['algorithmic_bytes'][key]} | "
+                        f"{t['back_to_back_us'][st]} | {t['after_flush_us'][st]} | "
+                        f"{t['after_flush_and_token_read_us'][st]} |")
+    head += ["", "Copy probe (each launch alone; read + write bytes):", "",
+             "| size | us (3 launches) | TB/s |", "|---|---|---|"]
+    for gib, c in timing["copy_probe"].items():
+        head.append(f"| {gib} | {c['us']} | {c['TBps']} |")
+    head += ["", "Counters, mean per launch (the `_sum` counters summed over instances):", "",
+             "| launches | " + " | ".join(counters) + " |",
+             "|---|" + "---|" * len(counters)]
+    for (w, label), vals in table.items():
+        row = f"{w} {label}".strip()
+        head.append(f"| {row} | " + " | ".join(f"{vals.get(c, float('nan')):.4g}"
+                                                for c in counters) + " |")
+    path = os.path.join(PROFILES, title.lower().replace(" ", "_").replace(",", "") + ".md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(head) + "\n")
+    return path
+
+
 def main(argv) -> int:
     if len(argv) >= 4 and argv[0] == "trace":
         print(trace(argv[1], argv[2], argv[3]))
         return 0
     if len(argv) >= 6 and argv[0] == "traffic":
         print(*traffic(argv[1], argv[2], argv[3], argv[4], argv[5]))
+        return 0
+    if len(argv) >= 5 and argv[0] == "probe":
+        print(probe(argv[1], argv[2], argv[3], argv[4:]))
         return 0
     print(__doc__, file=sys.stderr)
     return 2

@@ -131,6 +131,43 @@ def test_pack_quant_non_finite_blocks(H):
     np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
 
 
+def _e4m3_grid():
+    """Non-negative e4m3 values and the midpoints between neighbours."""
+    vals = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    mids = (vals[:-1].astype(np.float64) + vals[1:]) / 2
+    return np.concatenate([vals, mids.astype(np.float32)])
+
+
+@pytest.mark.parametrize("H", [1024, 8320], ids=["per_token_workgroup", "per_segment_waves"])
+def test_pack_quant_exact_ties_and_grid(H):
+    """Blocks whose scale is a power of two (amax = 448 * 2^k): every
+    quotient is exact, so values placed on e4m3 codes, on the midpoints
+    between them (ties, nearest even) and in the subnormal range test the
+    encoder's rounding decisions one by one; random blocks around them."""
+    rng = np.random.default_rng(41)
+    sh = W.Shape(f"q_ties_{H}", 2, 4, H, 4, 2, payload=W.PAYLOAD_FP8_B128, expert="dequant",
+                 seed=18)
+    wl = W.make_workload(sh)
+    grid = _e4m3_grid()
+    x = W.bf16_bits_to_f32(wl.x_bf16).copy().reshape(-1, 128)
+    for b in range(0, x.shape[0], 2):                     # every other block
+        k = int(rng.integers(-20, 12))
+        vals = rng.choice(grid, size=128) * rng.choice([-1.0, 1.0], size=128)
+        vals[0] = 448.0
+        x[b] = (vals * 2.0 ** k).astype(np.float32)
+    xb = W.to_bf16_bits(x.reshape(wl.x_bf16.shape))
+    assert (W.bf16_bits_to_f32(xb).reshape(-1, 128)[::2] == x[::2]).all()   # exact in bf16
+    wl.x_bf16 = xb
+    codes, scales = oracle.quantize_b128(xb)
+    wl.planes = [codes, scales.view(np.uint8)]
+    note(f"quant ties H={H}")
+    d, b, _ = _run_quant_path(sh, wl)
+    p = oracle.plan(2, 4, 4, 2, ep.capacity(d), wl.idx)
+    oc, osc = oracle.dispatch_pack_quant(xb, p)
+    np.testing.assert_array_equal(b.send[0].cpu().numpy(), oc)
+    np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
+
+
 def test_pack_quant_rejects_bf16_descriptor():
     sh = W.CONFIGS["tiny"]
     d = desc_of(sh)
