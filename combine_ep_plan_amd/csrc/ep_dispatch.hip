@@ -818,7 +818,15 @@ hipError_t launch_dispatch(const Dims& d, const int32_t* idx, const void* const 
   // (back to back, where the rows are in the MALL already, 319.4 against
   // 323.5 us; the all-to-one workload 669 against 643 us, back to back 625
   // against 637 us).
-  hipError_t e = launch_plan_local(d, idx, p, status, stream, true, gather_fits(d) ? x : nullptr);
+  RowTouch touch{};
+  int64_t touch_bytes = 0;
+  for (int q = 0; q < d.planes; ++q) {
+    touch.src[q] = (const uint8_t*)x[q];
+    touch.bytes[q] = (int64_t)d.T * d.row[q];
+    touch_bytes += d.N * touch.bytes[q];
+  }
+  const bool do_touch = gather_fits(d) && touch_bytes <= kTouchMaxBytes;
+  hipError_t e = launch_plan_local(d, idx, p, status, stream, true, do_touch ? &touch : nullptr);
   if (e != hipSuccess) return e;
   if (gather) {
     e = launch_pack_gather(d, x, p, send, true, status, stream, nullptr, d.win > 0);

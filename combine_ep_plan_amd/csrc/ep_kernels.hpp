@@ -34,6 +34,11 @@ constexpr int64_t kGatherSourceBytes = 4 << 20;
 constexpr int64_t kWindowSourceBytes = 32 << 20;
 constexpr int64_t kWindowSendBytes = (int64_t)2 << 30;
 
+// Token rows the dispatch touches into the memory-side cache (MALL) at
+// most, over all sources: beyond about half of its 256 MB they would evict
+// each other before the sender reads them.
+constexpr int64_t kTouchMaxBytes = (int64_t)128 << 20;
+
 // Token rows the send-side plan launch touches for the sender (per plane:
 // base pointer, or null, and one source's bytes).
 struct RowTouch {
@@ -65,13 +70,13 @@ hipError_t launch_window_list(const Dims& d, const PlanPtrs& p, hipStream_t stre
 // Split dispatch: the sender half's plan (no data of other ranks), the
 // receiver half's exchange, and the two data movers with private regions of
 // P rows per (destination, source) pair.
-// touch_x (optional, plane pointers of the token rows): the send-side plan
-// launch, when it is one launch (d.nchunks == 1), also reads one dword of
-// every 128-byte line of the token rows, so that the sender that follows
+// touch (optional, the token rows the sender reads, per source): the
+// send-side plan launch, when it is one launch (d.nchunks == 1), also reads
+// one dword of every 128-byte line of them, so that the sender that follows
 // finds them in the memory-side cache instead of HBM.
 hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                              int32_t* status, hipStream_t stream, bool with_window = true,
-                             const void* const* touch_x = nullptr);
+                             const RowTouch* touch = nullptr);
 hipError_t launch_plan_exchange(const Dims& d, const PlanPtrs& p, int32_t* status,
                                 hipStream_t stream);
 hipError_t launch_pack_split(const Dims& d, const int32_t* idx, const void* const x[2],

@@ -377,17 +377,17 @@ hipError_t launch_plan(const Dims& d, const int32_t* idx, const PlanPtrs& p,
 
 hipError_t launch_plan_local(const Dims& d, const int32_t* idx, const PlanPtrs& p,
                              int32_t* status, hipStream_t stream, bool with_window,
-                             const void* const* touch_x) {
+                             const RowTouch* touch) {
   hipError_t e = allow_large_lds();
   if (e != hipSuccess) return e;
   if (d.nchunks == 1) {
     RowTouch t{};
     int touch_blocks = 0;
-    if (touch_x != nullptr && d.T > 0) {
+    if (touch != nullptr && d.T > 0) {
+      t = *touch;
       int64_t lines = 0;
-      for (int q = 0; q < d.planes; ++q) {
-        t.src[q] = (const uint8_t*)touch_x[q];
-        t.bytes[q] = (int64_t)d.T * d.row[q];
+      for (int q = 0; q < 2; ++q) {
+        if (t.src[q] == nullptr) continue;
         const int64_t lq = (t.bytes[q] + 127) / 128;
         lines = lq > lines ? lq : lines;
       }

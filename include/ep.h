@@ -257,10 +257,10 @@ EP_API int ep_dispatch_recv(const ep_desc *d, const void *const send[2],
  * N <= 1024, it takes three launches instead of four: the send side of the plan, then
  * the sender with the count exchange ("Send and receive buffers") done by
  * extra blocks of the same launch, then the receiver. When, in addition, one
- * source's token rows take at most 4 MiB (the send-order sender), extra
- * blocks of the plan launch read one dword of every 128-byte line of x, so
- * that the sender's first reads of each row find it in the memory-side
- * cache; x is only read. */
+ * source's token rows take at most 4 MiB (the send-order sender) and all of
+ * x at most 128 MiB, extra blocks of the plan launch read one dword of every
+ * 128-byte line of x, so that the sender's first reads of each row find it
+ * in the memory-side cache; x is only read. */
 EP_API int ep_dispatch(const ep_desc *d, const int32_t *topk_idx,
                        const void *const x[2], void *plan_ws,
                        void *const send[2], void *const grouped[2],
