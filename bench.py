@@ -695,6 +695,126 @@ def measure_probe(ep, torch, np, W, names, flush) -> dict:
     return res
 
 
+def measure_sender_probe(ep, torch, np, W, flush) -> dict:
+    """What limits the quantising sender on the prefill workload, through the
+    public calls only (the figures of the design's sender section):
+      - the fused sender (ep_dispatch_pack_quant) on the whole workload;
+      - quantise once: the same call on a descriptor with one row per token
+        whose ids all name expert 0, so that its send buffer is the quantised
+        token rows in token order (a staging area);
+      - the plain sender (ep_dispatch_pack, send order over windows for this
+        descriptor) from pre-quantised rows: the generator's planes, back to
+        back (their rows in the memory-side cache) and after a flush, and the
+        staging rows right after the staging call wrote them;
+      - one source sent alone (a descriptor with N = 1 and that source's
+        ids): back to back, after a flush, and after a flush followed by a
+        read of its token rows;
+      - that source with 1, 2 or 4 rows per token (E = 32 R experts, uniform
+        distinct ids drawn from a fixed seed): the time of the token reads and
+        the quantisation against that of the extra rows.
+    Each figure is the median of 5 launches, each timed alone between two
+    HIP events. The byte-equality checks compare the two-pass and
+    per-source send buffers with the fused sender's."""
+    import gc
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    sh = W.CONFIGS["prefill"]
+    wl = W.make_workload(sh)
+    N, T, H, E, R = sh.n_ranks, sh.tokens, sh.hidden, sh.n_experts, sh.topk
+    F8 = ep.EP_PAYLOAD_FP8_B128
+    u8 = torch.uint8
+    d = ep.make_desc(N, T, H, E, R, F8)
+    rows = [ep.row_bytes(d, q) for q in range(2)]
+    idx = torch.from_numpy(wl.idx).cuda()
+    x = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda()
+    xq = [torch.from_numpy(pl).cuda() for pl in wl.planes]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = torch.empty(ep.plan_bytes(d), dtype=u8, device="cuda")
+    send = [torch.empty((N, T * R, r), dtype=u8, device="cuda") for r in rows]
+    ep.plan(d, idx, plan, status, sp)
+    ds = ep.make_desc(N, T, H, N, 1, F8)
+    plan_s = torch.empty(ep.plan_bytes(ds), dtype=u8, device="cuda")
+    ep.plan(ds, torch.zeros((N, T, 1), dtype=torch.int32, device="cuda"), plan_s, status, sp)
+    stg = [torch.empty((N, T, r), dtype=u8, device="cuda") for r in rows]
+
+    def timed(fns, pre=None, reps=5):
+        out = [[] for _ in fns]
+        for i in range(reps):
+            if pre is not None:
+                pre(i)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for j, fn in enumerate(fns):
+                fn()
+                ev[j + 1].record(stream)
+            torch.cuda.synchronize()
+            for j in range(len(fns)):
+                out[j].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+        return [round(float(np.median(o)), 1) for o in out]
+
+    fused = lambda: ep.dispatch_pack_quant(d, x, plan, send, sp)
+    stage = lambda: ep.dispatch_pack_quant(ds, x, plan_s, stg, sp)
+    copy_stg = lambda: ep.dispatch_pack(d, stg, plan, send, sp)
+    copy_gen = lambda: ep.dispatch_pack(d, xq, plan, send, sp)
+    fused()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in send]
+    for t in send:
+        t.zero_()
+    stage()
+    copy_stg()
+    torch.cuda.synchronize()
+    res = {"workload": describe(sh, W, True), "status": int(status.item()),
+           "windowed_plain_sender": bool(ep.plan_views(d, plan).win_list),
+           "staging_equals_generator_planes": all(torch.equal(a, c) for a, c in zip(stg, xq)),
+           "two_pass_send_equals_fused": all(torch.equal(a, c) for a, c in zip(send, ref))}
+    res["fused_us"] = {"back_to_back": timed([fused, fused])[1], "after_flush": timed([fused], flush)[0]}
+    res["staging_pass_us"] = {"back_to_back": timed([stage, stage])[1],
+                              "after_flush": timed([stage], flush)[0]}
+    res["plain_sender_us"] = {
+        "generator_planes_back_to_back": timed([copy_gen, copy_gen])[1],
+        "generator_planes_after_flush": timed([copy_gen], flush)[0],
+        "staging_rows_right_after_the_staging_call": timed([stage, copy_stg])[1],
+        "staging_rows_after_flush": timed([copy_stg], flush)[0]}
+    del stg, plan_s
+    gc.collect()
+    # one source alone
+    d1 = ep.make_desc(1, T, H, E, R, F8)
+    plan1 = torch.empty(ep.plan_bytes(d1), dtype=u8, device="cuda")
+    ep.plan(d1, idx[0:1].contiguous(), plan1, status, sp)
+    x0 = x[0:1]
+    send1 = [t[0:1] for t in send]
+    one = lambda: ep.dispatch_pack_quant(d1, x0, plan1, send1, sp)
+    for t in send:
+        t.zero_()
+    one()
+    torch.cuda.synchronize()
+    res["one_source_send_equals_fused"] = all(torch.equal(a[0], c[0]) for a, c in zip(send, ref))
+    res["one_source_us"] = {
+        "back_to_back": timed([one, one])[1],
+        "after_flush": timed([one], flush)[0],
+        "after_flush_and_token_read": timed([lambda: x0.view(torch.int32).max(), one], flush)[1]}
+    rng = np.random.default_rng(7)
+    rsweep = {}
+    for r in (1, 2, 4, R):
+        e_r = 32 * r
+        dr = ep.make_desc(1, T, H, e_r, r, F8)
+        ids = np.argsort(rng.random((1, T, e_r)), axis=-1, kind="stable")[..., :r].astype(np.int32)
+        plan_r = torch.empty(ep.plan_bytes(dr), dtype=u8, device="cuda")
+        ep.plan(dr, torch.from_numpy(ids).cuda(), plan_r, status, sp)
+        send_r = [torch.empty((1, T * r, ep.row_bytes(dr, q)), dtype=u8, device="cuda") for q in range(2)]
+        fn = lambda: ep.dispatch_pack_quant(dr, x0, plan_r, send_r, sp)
+        fn()
+        rsweep[f"R={r},E={e_r}"] = {"back_to_back": timed([fn, fn])[1]}
+        del send_r, plan_r
+    res["one_source_rows_per_token_us"] = rsweep
+    torch.cuda.synchronize()
+    res["status_after"] = int(status.item())
+    return res
+
+
 def setup(ep, torch, np, W, name: str):
     """Workload, caller-owned buffers, inputs in HBM and the stand-in
     expert's output (computed once, outside any timing)."""
@@ -815,6 +935,9 @@ def main() -> int:
                     help="only run the kernel-level probe (the sender back to back, after a "
                          "cache flush, and after a flush plus a read of the token rows, for "
                          "each listed workload; the copy probe at 0.5-3 GiB) and print it")
+    ap.add_argument("--sender-probe", action="store_true",
+                    help="measure what limits the quantising sender on the prefill workload "
+                         "(public calls only) and print one JSON line")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0 = skip; the parity "
                          "check then runs the oracle once)")
@@ -835,6 +958,10 @@ def main() -> int:
         probe = measure_probe(ep, torch, np, W, [n for n in args.probe.split(",") if n],
                               Flusher(torch))
         print(json.dumps({"probe": probe}), flush=True)
+        return 0
+    if args.sender_probe:
+        print(json.dumps({"sender_probe": measure_sender_probe(ep, torch, np, W, Flusher(torch))}),
+              flush=True)
         return 0
     sh, wl, d, b, alpha = setup(ep, torch, np, W, args.config)
     quant = sh.payload == W.PAYLOAD_FP8_B128 and not args.prequantized

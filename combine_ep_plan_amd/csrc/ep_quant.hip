@@ -10,10 +10,10 @@
 //
 // One wave per 1024-value segment of a token row. Lane l holds 16-byte chunks
 // l and l+64 of the segment (8 bf16 each); the 16 lanes 16g .. 16g+15 of one
-// step hold one 128-value block, so the block's amax is a 16-lane
-// xor-shuffle reduction. Scale and quotient
-// are IEEE fp32 divisions (the same operations a CPU reference performs), so
-// the integer codes are decided in the same precision everywhere.
+// step hold one 128-value block, so the block's amax is a reduction over one
+// DPP row. The scale is the IEEE fp32 division amax / 448. The codes are
+// those of the IEEE fp32 quotient x / scale (the operation a CPU reference
+// performs), obtained without a division per value (quantise_step).
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
 #include "ep_plan_device.hpp"
@@ -55,6 +55,83 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
   return sign | code;
 }
 
+// Codes and scale of one step (8 values per lane, 16 lanes per block).
+//
+// Fast path: y = 1 / scale once per block (IEEE division), then per value
+// q0 = |x| y and one correction q = q0 + (|x| - scale q0) y (two FMAs; the
+// residual is exact), clamped to 448, signed by x, and encoded by the
+// hardware conversion, which equals f32_to_e4m3 on every |q| <= 448. For a
+// bf16 x and a bf16 block amax of at least 2^-96 this q gives the same e4m3
+// code as the IEEE quotient x / scale: checked for every such pair (532.7 M
+// of them) by tests/test_fp8_reciprocal.py, which runs these same operations
+// on the CPU. Everything else takes the exact path below for the whole wave:
+// a smaller nonzero amax, an infinite amax, or a NaN anywhere in the step.
+//
+// Exact path: amax with NaN left out (a NaN never compares greater; an
+// infinite value makes amax and the scale infinite), IEEE division per
+// value, the software encoder; a NaN quotient (a NaN value, or an infinite
+// one over its infinite scale) is the NaN code 0x7F, kept from the clamp,
+// which would turn it into -448.
+__device__ __forceinline__ void quantise_step(const u32x4& r, uint32_t packed[2], float& scale_out) {
+  float v[8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    v[2 * h] = bf16_lo(r[h]);
+    v[2 * h + 1] = bf16_hi(r[h]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  // Over the block's 16 lanes (one DPP row): the maximum of non-negative
+  // floats is the maximum of their bit patterns, and a NaN stays the largest.
+  uint32_t ab = __float_as_uint(amax);
+  ab = max(ab, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ab, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  ab = max(ab, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ab, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  ab = max(ab, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ab, 0x141, 0xF, 0xF, false));  // half-row mirror
+  ab = max(ab, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ab, 0x140, 0xF, 0xF, false));  // row mirror
+  amax = __uint_as_float(ab);
+  float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const float y = 1.0f / scale;
+  uint32_t qmax = 0;
+  float q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float a = fabsf(v[j]);
+    const float q0 = a * y;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-scale, q0, a), y, q0);
+    qmax = max(qmax, __float_as_uint(q1));
+    q[j] = __builtin_copysignf(fminf(q1, 448.0f), v[j]);
+  }
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
+  packed[0] = (uint32_t)w0;
+  packed[1] = (uint32_t)w1;
+  const bool exact = (amax > 0.0f && amax < 0x1p-96f) || !(amax < __builtin_inff()) ||
+                     qmax > 0x7f800000u;
+  if (ballot(exact)) {  // wave-uniform: the shuffles below need every lane
+    amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = fabsf(v[j]);
+      amax = a > amax ? a : amax;
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float qq = v[j] / scale;
+      c[j] = __builtin_isnan(qq) ? 0x7Fu : f32_to_e4m3(fminf(fmaxf(qq, -448.0f), 448.0f));
+    }
+    packed[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    packed[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  }
+  scale_out = scale;
+}
+
 // The sender's work for wave w (token w / nseg, segment w % nseg). With
 // ROW_SCALES the wave also writes its blocks' scales to the R send rows;
 // otherwise it leaves them in tok_scale (LDS, indexed by block) for the
@@ -80,37 +157,7 @@ __device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x
   uint32_t packed[kQV][2];
   float sc[kQV];
 #pragma unroll
-  for (int i = 0; i < kQV; ++i) {
-    float v[8];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      v[2 * h] = bf16_lo(r.v[i][h]);
-      v[2 * h + 1] = bf16_hi(r.v[i][h]);
-    }
-    // amax over the block's magnitudes; a NaN never compares greater, so it
-    // is left out (an infinite value makes amax and the scale infinite).
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float a = fabsf(v[j]);
-      amax = a > amax ? a : amax;
-    }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-    sc[i] = scale;
-    uint32_t c[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // A NaN quotient (a NaN value, or an infinite one over its infinite
-      // scale) is the NaN code 0x7F; it must not reach the clamp, which
-      // would turn it into -448.
-      const float q = v[j] / scale;
-      c[j] = __builtin_isnan(q) ? 0x7Fu : f32_to_e4m3(fminf(fmaxf(q, -448.0f), 448.0f));
-    }
-    packed[i][0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    packed[i][1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-  }
+  for (int i = 0; i < kQV; ++i) quantise_step(r.v[i], packed[i], sc[i]);
   // Lane b < kQBlocks collects the scale of block b of this segment: block b
   // was computed in step b / 4 by lane group b % 4.
   float my_scale = 0.0f;

@@ -1,9 +1,12 @@
 """Sender with fused block-fp8 quantisation, against the CPU oracle.
 
-Codes and scales are integers and fp32 values decided by IEEE fp32
-divisions on both sides, so the send planes must match bit for bit; the
-rest of the fp8 path (receive, dequantising expert, combine) follows the
-parity bar of the bf16 path.
+Codes and scales are integers and fp32 values: the scale is an IEEE fp32
+division on both sides, and the codes are those of the IEEE fp32 quotient
+(the oracle divides; the sender reaches the same codes through a reciprocal
+and one FMA correction, exact for bf16 inputs by tests/test_fp8_reciprocal.py,
+falling back to the division outside that range). So the send planes must
+match bit for bit; the rest of the fp8 path (receive, dequantising expert,
+combine) follows the parity bar of the bf16 path.
 """
 import gc
 
@@ -163,6 +166,39 @@ def test_pack_quant_exact_ties_and_grid(H):
     note(f"quant ties H={H}")
     d, b, _ = _run_quant_path(sh, wl)
     p = oracle.plan(2, 4, 4, 2, ep.capacity(d), wl.idx)
+    oc, osc = oracle.dispatch_pack_quant(xb, p)
+    np.testing.assert_array_equal(b.send[0].cpu().numpy(), oc)
+    np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
+
+
+@pytest.mark.parametrize("H", [1024, 8320], ids=["per_token_workgroup", "per_segment_waves"])
+def test_pack_quant_wide_dynamic_range(H):
+    """Blocks scaled by 2^k over the whole bf16 range, k from -135 to 120,
+    with many blocks whose amax lies around 2^-96, where the sender switches
+    between the reciprocal form and the division (a wave takes the division
+    for all its blocks when any of them needs it), and bf16 subnormal values
+    inside normal blocks. Bit for bit against the oracle."""
+    rng = np.random.default_rng(43)
+    sh = W.Shape(f"q_range_{H}", 2, 8, H, 4, 2, payload=W.PAYLOAD_FP8_B128, expert="dequant",
+                 seed=19)
+    wl = W.make_workload(sh)
+    x = W.bf16_bits_to_f32(wl.x_bf16).astype(np.float64).reshape(-1, 128)
+    nb = x.shape[0]
+    k = rng.integers(-135, 121, size=nb)
+    near = rng.random(nb) < 0.4
+    k[near] = rng.integers(-99, -93, size=int(near.sum()))    # amax around 2^-96
+    x = x * np.exp2(k.astype(np.float64))[:, None]
+    tiny = rng.random(x.shape) < 0.02
+    x[tiny] *= 2.0 ** -40                                    # some values far below their amax
+    xb = W.to_bf16_bits(x.astype(np.float32).reshape(wl.x_bf16.shape))
+    wl.x_bf16 = xb
+    codes, scales = oracle.quantize_b128(xb)
+    wl.planes = [codes, scales.view(np.uint8)]
+    amax = np.abs(W.bf16_bits_to_f32(xb).reshape(-1, 128)).max(1)
+    assert (amax < 2.0 ** -96).sum() > 10 and (amax >= 2.0 ** -96).sum() > 10
+    note(f"quant wide range H={H}")
+    d, b, _ = _run_quant_path(sh, wl)
+    p = oracle.plan(2, 8, 4, 2, ep.capacity(d), wl.idx)
     oc, osc = oracle.dispatch_pack_quant(xb, p)
     np.testing.assert_array_equal(b.send[0].cpu().numpy(), oc)
     np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
