@@ -60,7 +60,8 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
 // Fast path: y = 1 / scale once per block (IEEE division), then per value
 // q0 = |x| y and one correction q = q0 + (|x| - scale q0) y (two FMAs; the
 // residual is exact), clamped to 448, signed by x, and encoded by the
-// hardware conversion, which equals f32_to_e4m3 on every |q| <= 448. For a
+// hardware conversion, which equals f32_to_e4m3 on every |q| <= 448
+// (tests/test_gpu_fp8_convert.py checks every such fp32 value). For a
 // bf16 x and a bf16 block amax of at least 2^-96 this q gives the same e4m3
 // code as the IEEE quotient x / scale: checked for every such pair (532.7 M
 // of them) by tests/test_fp8_reciprocal.py, which runs these same operations
