@@ -63,7 +63,7 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
 // hardware conversion, which equals f32_to_e4m3 on every |q| <= 448
 // (tests/test_gpu_fp8_convert.py checks every such fp32 value). For a
 // bf16 x and a bf16 block amax of at least 2^-96 this q gives the same e4m3
-// code as the IEEE quotient x / scale: checked for every such pair (532.7 M
+// code as the IEEE quotient x / scale: checked for every such pair (524.8 M
 // of them) by tests/test_fp8_reciprocal.py, which runs these same operations
 // on the CPU. Everything else takes the exact path below for the whole wave:
 // a smaller nonzero amax, an infinite amax, or a NaN anywhere in the step.
