@@ -204,6 +204,62 @@ def test_pack_quant_wide_dynamic_range(H):
     np.testing.assert_array_equal(b.send[1].cpu().numpy().view(np.uint32), osc.view(np.uint32))
 
 
+def test_dispatch_quant_many_chunks_bad_ids_and_tight_capacity():
+    """Sources of several plan chunks, with out-of-range ids and a capacity
+    below what most ranks receive: the one-call quantising dispatch gives
+    the status bits, plan tables, filled send rows and delivered grouped
+    rows of the three-call form."""
+    from gpu_util import plan_fields
+    sh = W.Shape("q_chunks_tight", 4, 1500, 1024, 16, 4, payload=W.PAYLOAD_FP8_B128,
+                 expert="dequant", seed=23)
+    wl = W.make_workload(sh)
+    idx = wl.idx.copy()
+    idx[0, 5, 1] = 16
+    idx[3, 1499, 0] = -1
+    idx[2, 700, 3] = 99
+    wl.idx = idx
+    N, T, R = sh.n_ranks, sh.tokens, sh.topk
+    assert T * R > 4096                              # more than one plan chunk per source
+    cap = (N * T * R) // N - 200                     # below the average per rank
+    d = desc_of(sh, cap)
+    note("dispatch_quant many chunks, bad ids, tight capacity")
+    x = torch.from_numpy(wl.x_bf16.view(np.int16)).cuda()
+    ref = ep.Buffers(d)
+    ref.idx.copy_(torch.from_numpy(idx))
+    ref.status.zero_()
+    ep.plan(d, ref.idx, ref.plan_ws, ref.status)
+    ep.dispatch_pack_quant(d, x, ref.plan_ws, ref.send)
+    ep.dispatch_recv(d, ref.send, ref.plan_ws, ref.grouped)
+    torch.cuda.synchronize()
+    want = plan_arrays(d, ref)
+    want_status = int(ref.status.item())
+    assert want_status == ep.EP_STATUS_BAD_EXPERT | ep.EP_STATUS_CAPACITY
+    b = ep.Buffers(d)
+    b.idx.copy_(torch.from_numpy(idx))
+    b.plan_ws.fill_(0x3C)
+    b.status.zero_()
+    ep.dispatch_quant(d, b.idx, x, b.plan_ws, b.send, b.grouped, b.status)
+    torch.cuda.synchronize()
+    assert int(b.status.item()) == want_status
+    got = plan_arrays(d, b)
+    for f in plan_fields(d):
+        if f == "win_list":
+            continue
+        np.testing.assert_array_equal(got[f], want[f], err_msg=f)
+    # the rows each source fills (rows past them are left untouched)
+    filled = want["send_off"][:, -1]
+    assert int(filled.sum()) == N * T * R - 3        # the three out-of-range slots are dropped
+    for t, rt in zip(b.send, ref.send):
+        for s in range(N):
+            n = int(filled[s])
+            assert torch.equal(t[s, :n], rt[s, :n]), f"send {s}"
+    totals = want["recv_off"][:, N]
+    for g, rg in zip(b.grouped, ref.grouped):
+        for dd in range(N):
+            n = min(int(totals[dd]), cap)
+            assert torch.equal(g[dd, :n], rg[dd, :n]), f"grouped {dd}"
+
+
 def test_pack_quant_rejects_bf16_descriptor():
     sh = W.CONFIGS["tiny"]
     d = desc_of(sh)
