@@ -850,6 +850,53 @@ CONFIG_PROTOCOL = {"tiny": (200, False), "tiny_zipf": (200, False), "decode": (1
                    "decode_fp8": (100, True)}
 
 
+def dominant_roofline(ep, torch, d, b, sh, quant, x_bf16, ab, workload, stream) -> dict:
+    """The roofline object of a workload's dominant kernel (the stage with
+    the largest algorithmic bytes): its launch duration over 20 launches
+    back to back between two events (one event pair per launch would add
+    the event overhead to each), after a fresh plan and sender pass so that
+    it reads what the sender wrote; the counter traffic recorded for it
+    under profiles/ while its sources hash the same."""
+    sp = stream.cuda_stream
+    dom = max(ab["stages"], key=lambda k: ab["stages"][k])
+
+    def pack():
+        if quant:
+            ep.dispatch_pack_quant(d, x_bf16, b.plan_ws, b.send, sp)
+        else:
+            ep.dispatch_pack(d, b.x, b.plan_ws, b.send, sp)
+
+    call = {"plan": lambda: ep.plan(d, b.idx, b.plan_ws, b.status, sp),
+            "pack": pack,
+            "recv": lambda: ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp),
+            "combine": lambda: ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, sp)}[dom]
+    ep.plan(d, b.idx, b.plan_ws, b.status, sp)
+    pack()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(20):
+        call()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    dom_ms = k0.elapsed_time(k1) / 20
+    achieved = ab["stages"][dom] / (dom_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(workload, "pack_quant" if dom == "pack" and quant else dom)
+    return {
+        "kernel": f"ep_dispatch_{dom}" if dom in ("pack", "recv") else f"ep_{dom}",
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "traffic_GBps": None if traffic is None else round(traffic / (dom_ms * 1e-3) / 1e9, 2),
+        "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+        "algorithmic_bytes": ab["stages"][dom],
+        "avg_us": round(dom_ms * 1e3, 2),
+        "avg_us_from": "20 launches back to back between two HIP events on the launch stream",
+    }
+
+
 def run_config(ep, torch, np, W, name: str, flush, warmup: int = 20) -> dict:
     """One workload under its protocol: dispatch + combine steps timed on
     the device, then the parity of its buffers with the oracle (the whole
@@ -893,6 +940,8 @@ def run_config(ep, torch, np, W, name: str, flush, warmup: int = 20) -> dict:
         res.update(flushed=False, us_back_to_back=round(b2b, 2))
     res["effective_GBps"] = round(ab["step"] / us / 1e3, 1)
     res["frac_of_hbm_peak"] = round(ab["step"] / us / 1e3 / HBM_PEAK_GBPS, 4)
+    if flushed:
+        res["roofline"] = dominant_roofline(ep, torch, d, b, sh, quant, x_bf16, ab, name, stream)
     if name in ("tiny", "tiny_zipf"):
         ref = oracle.run(wl, cap=ep.capacity(d))
         res["parity"] = bench_parity(ep, torch, np, d, b, sh, wl, quant, oracle_out=ref["out"])
@@ -1092,25 +1141,8 @@ def main() -> int:
     ab = algorithmic_bytes(sh, row_d, quant)
     eff = ab["step"] / (ms_per_step * 1e-3) / 1e9
 
-    # the dominant kernel: the stage with the largest algorithmic bytes
-    dom = max(ab["stages"], key=lambda k: ab["stages"][k])
-    # Its launch duration: 20 launches back to back between two events (one
-    # event pair per launch would add the event overhead to each), after a
-    # fresh plan and sender pass so that it reads what the sender wrote.
-    dom_call = {"plan": lambda: ep.plan(d, b.idx, b.plan_ws, b.status, sp),
-                "pack": pack,
-                "recv": lambda: ep.dispatch_recv(d, b.send, b.plan_ws, b.grouped, sp),
-                "combine": lambda: ep.combine(d, b.expert_out, b.weights, b.plan_ws, b.out, sp)}[dom]
-    ep.plan(d, b.idx, b.plan_ws, b.status, sp)
-    pack()
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record(stream)
-    for _ in range(20):
-        dom_call()
-    k1.record(stream)
-    torch.cuda.synchronize()
-    dom_ms = k0.elapsed_time(k1) / 20
-    achieved = ab["stages"][dom] / (dom_ms * 1e-3) / 1e9
+    # the dominant kernel against the roofline
+    roof = dominant_roofline(ep, torch, d, b, sh, quant, x_bf16, ab, args.config, stream)
 
     # the stand-in expert, outside the step (reported, not part of the metric)
     x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1189,7 +1221,6 @@ def main() -> int:
     parity = bench_parity(ep, torch, np, d, b, sh, wl, quant, oracle_out=oracle_out)
     parity["status_after_timed_steps"] = status_after
 
-    traffic = recorded_traffic(args.config, "pack_quant" if dom == "pack" and quant else dom)
     res = {
         "metric": METRIC,
         "value": round(eff, 2),
@@ -1230,20 +1261,7 @@ def main() -> int:
         "stages_from": "the four separate calls, back to back, after the timed steps",
         "instrumented_step_us_p10_p50_p90": pcts(np, steps_us),
         "wall_ms": round(wall_ms, 3),
-        "roofline": {
-            "kernel": f"ep_dispatch_{dom}" if dom in ("pack", "recv") else f"ep_{dom}",
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "traffic_GBps": None if traffic is None else round(traffic / (dom_ms * 1e-3) / 1e9, 2),
-            "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
-            "algorithmic_bytes": ab["stages"][dom],
-            "avg_us": round(dom_ms * 1e3, 2),
-            "avg_us_from": "20 launches back to back between two HIP events on the launch stream",
-        },
+        "roofline": roof,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "parity": parity,
         "cpu_baseline": cpu,
