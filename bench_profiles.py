@@ -79,9 +79,10 @@ def trace(workload: str, stats_csv: str, args: str) -> str:
            command(args, "--kernel-trace --stats"),
            f"python3 bench_profiles.py trace {workload} <stats csv> \"{args}\"", "```", "",
            "rocprofv3 kernel statistics over every dispatch of the run: warm-up, back-to-back",
-           "and flushed steps, the per-stage loop of four separate calls, the dominant kernel's",
-           "20 launches, the stand-in expert, the copy probe and the torch kernels that evict",
-           "the caches between flushed steps.", "",
+           "and flushed steps, the per-stage loop of four separate calls, 20 launches of the",
+           "dominant kernel (of the headline and of each flushed workload in configs), the",
+           "stand-in expert, the copy probe and the torch kernels that evict the caches",
+           "between flushed steps.", "",
            "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
