@@ -815,6 +815,146 @@ def measure_sender_probe(ep, torch, np, W, flush) -> dict:
     return res
 
 
+def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
+    """The access shapes the sender, receiver and combine were chosen on,
+    through the library's access-pattern probe (ep_probe_pattern). Each
+    figure is the median of `reps` launches, each alone between two HIP
+    events (back to back unless stated):
+      - fills of 1 GiB: one piece of 1, 4, 14 or 64 KB per wave in output
+        order, and 1 KB pieces walked grid-stride by 2048 or 8192 waves;
+      - copies of the decode size (32768 rows of 14 KB, 470 MB out): linear,
+        rows permuted at random, and sender-like (each of the 4096 token rows
+        read 8 times, in the send order of the decode routing: per source,
+        slots stably sorted by expert) with cached loads and the XCD
+        renumbering, without the renumbering, and with non-temporal loads;
+        1, 2, 7 and 14 KB per wave;
+      - the combine's mix: 4096 rows of 14 KB, each the xor of 8 rows from 8
+        linear regions (470 MB read, 59 MB written), 1, 2, 7 and 14 KB per
+        wave, 2 or 8 rows in flight, cached and non-temporal loads; the same
+        470 MB read only;
+      - memory-side cache reuse: 32, 128 and 512 MB read (non-temporal and
+        cached loads) right after a fill of the same bytes, right after a
+        read of them, and after a flush."""
+    import gc
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    COPY, FILL, READ = ep.EP_PROBE_COPY, ep.EP_PROBE_FILL, ep.EP_PROBE_READ
+    NTL, XCD = ep.EP_PROBE_NT_LOADS, ep.EP_PROBE_XCD
+
+    def probe(dst, src, table, rows, src_rows, row, piece, **kw):
+        return lambda: ep.probe_pattern(dst, src, table, rows, src_rows, row, piece,
+                                        stream=sp, **kw)
+
+    def timed(fn, pre=None):
+        ts = []
+        for i in range(reps):
+            if pre is not None:
+                pre(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    def fig(fn, nbytes, pre=None):
+        us = timed(fn, pre)
+        return {"us": round(us, 2), "TBps": round(nbytes / us / 1e6, 3)}
+
+    res = {}
+    # Fills of 1 GiB.
+    GiB = 1 << 30
+    a = torch.empty(GiB + (1 << 20), dtype=torch.uint8, device="cuda")
+    fills = {}
+    for kb in (1, 4, 14, 64):
+        row = 14336 if kb == 14 else 65536
+        rows = GiB // row
+        fills[f"{kb}KB_per_wave"] = fig(probe(a, None, None, rows, 0, row, kb * 1024, mode=FILL),
+                                        rows * row)
+    for waves in (2048, 8192):
+        fills[f"1KB_grid_stride_{waves}_waves"] = fig(
+            probe(a, None, None, GiB // 65536, 0, 65536, 1024, mode=FILL, waves=waves), GiB)
+    res["fill_1GiB"] = fills
+    del a
+    torch.cuda.empty_cache()
+
+    # Copies at the decode size.
+    sh = W.CONFIGS["decode"]
+    N, T, R, row = sh.n_ranks, sh.tokens, sh.topk, 2 * sh.hidden
+    rng = np.random.default_rng(sh.seed)
+    idx = W.make_workload(sh).idx.reshape(N, T * R)
+    order = np.argsort(idx, axis=1, kind="stable")           # send row -> slot, per source
+    send_table = (np.arange(N)[:, None] * T + order // R).astype(np.int32).reshape(-1)
+    nrows = N * T * R
+    src_big = torch.randint(0, 255, (nrows, row), dtype=torch.uint8, device="cuda")
+    src_tok = src_big[:N * T]
+    dst = torch.empty_like(src_big)
+    perm = torch.from_numpy(rng.permutation(nrows).astype(np.int32)).cuda()
+    sendt = torch.from_numpy(send_table).cuda()
+    copy_bytes = 2 * nrows * row
+    send_bytes = N * T * row + nrows * row
+    copies = {}
+    for kb in (1, 2, 7, 14):
+        pb = kb * 1024
+        copies[f"{kb}KB_per_wave"] = {
+            "linear": fig(probe(dst, src_big, None, nrows, nrows, row, pb, flags=NTL),
+                          copy_bytes),
+            "rows_permuted": fig(probe(dst, src_big, perm, nrows, nrows, row, pb, flags=NTL),
+                                 copy_bytes),
+            "sender_like_cached_xcd": fig(
+                probe(dst, src_tok, sendt, nrows, N * T, row, pb, flags=XCD), send_bytes),
+            "sender_like_cached": fig(probe(dst, src_tok, sendt, nrows, N * T, row, pb),
+                                      send_bytes),
+            "sender_like_nt_xcd": fig(
+                probe(dst, src_tok, sendt, nrows, N * T, row, pb, flags=NTL | XCD), send_bytes),
+        }
+    res["copy_decode_size"] = {
+        "bytes": {"linear_and_permuted": copy_bytes, "sender_like": send_bytes},
+        "figures": copies}
+
+    # The combine's 8:1 mix over the same 470 MB.
+    out_rows = N * T
+    out = dst[:out_rows]
+    mix_bytes = nrows * row + out_rows * row
+    mix = {}
+    for kb, inflight in ((1, 8), (2, 8), (7, 2), (14, 2), (14, 8)):
+        for name, fl in (("cached", 0), ("nt", NTL)):
+            mix[f"{kb}KB_per_wave_{inflight}_in_flight_{name}"] = fig(
+                probe(out, src_big, None, out_rows, nrows, row, kb * 1024, fan_in=8,
+                      in_flight=inflight, flags=fl), mix_bytes)
+    for name, fl in (("cached", 0), ("nt", NTL)):
+        mix[f"read_only_1KB_{name}"] = fig(
+            probe(out, src_big, None, nrows, nrows, row, 1024, mode=READ, flags=fl),
+            nrows * row)
+    res["combine_mix_decode_size"] = {"bytes": mix_bytes, "figures": mix}
+    del src_big, src_tok, dst, out, perm, sendt
+    gc.collect()
+    torch.cuda.empty_cache()
+
+    # Reuse from the memory-side cache.
+    reuse = {}
+    for mb in (32, 128, 512):
+        n = mb << 20
+        buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+        rows = n // 65536
+        fill = probe(buf, None, None, rows, 0, 65536, 1024, mode=FILL)
+        entry = {}
+        for name, fl in (("nt", NTL), ("cached", 0)):
+            rd = probe(sink, buf, None, rows, rows, 65536, 1024, mode=READ, flags=fl)
+            entry[f"{name}_after_fill"] = fig(rd, n, pre=lambda i: fill())
+            entry[f"{name}_after_read"] = fig(rd, n, pre=lambda i: (flush(i), rd()))
+            entry[f"{name}_after_flush"] = fig(rd, n, pre=lambda i: (fill(), flush(i)))
+        reuse[f"{mb}MB"] = entry
+        del buf, sink
+        torch.cuda.empty_cache()
+    res["mall_reuse"] = reuse
+    return res
+
+
 def setup(ep, torch, np, W, name: str):
     """Workload, caller-owned buffers, inputs in HBM and the stand-in
     expert's output (computed once, outside any timing)."""
@@ -987,6 +1127,10 @@ def main() -> int:
     ap.add_argument("--sender-probe", action="store_true",
                     help="measure what limits the quantising sender on the prefill workload "
                          "(public calls only) and print one JSON line")
+    ap.add_argument("--pattern-probe", action="store_true",
+                    help="measure the access shapes behind the kernels' designs (fills, "
+                         "copies, the combine's 8:1 mix, memory-side cache reuse) with the "
+                         "library's access-pattern probe and print one JSON line")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle CPU work for the baseline (0 = skip; the parity "
                          "check then runs the oracle once)")
@@ -1007,6 +1151,10 @@ def main() -> int:
         probe = measure_probe(ep, torch, np, W, [n for n in args.probe.split(",") if n],
                               Flusher(torch))
         print(json.dumps({"probe": probe}), flush=True)
+        return 0
+    if args.pattern_probe:
+        print(json.dumps({"pattern_probe": measure_pattern_probe(ep, torch, np, W,
+                                                                 Flusher(torch))}), flush=True)
         return 0
     if args.sender_probe:
         print(json.dumps({"sender_probe": measure_sender_probe(ep, torch, np, W, Flusher(torch))}),

@@ -15,6 +15,9 @@ for that launch gives the factor that turns the counter into bytes. The JSON
 records, per stage, the source hash of the kernels it was measured on;
 bench.py only reports the traffic while the built kernels still hash the same.
 
+A fourth tabulates `bench.py --pattern-probe` (fills, copies, the combine's
+mix and memory-side cache reuse with the library's access-pattern probe).
+
 A third summary tabulates counter runs of `bench.py --probe` (the senders
 back to back, after a cache flush and after a flush plus a read of the token
 rows; the copy probe at 0.5-3 GiB).
@@ -23,6 +26,7 @@ Usage (after the rocprofv3 runs, whose commands the summaries quote):
   python3 bench_profiles.py trace WORKLOAD STATS_CSV "BENCH_ARGS"
   python3 bench_profiles.py traffic WORKLOAD FETCH_CSV WRITE_CSV STATS_CSV "BENCH_ARGS"
   python3 bench_profiles.py probe TITLE WORKLOADS TIMING_JSON COUNTER_CSV...
+  python3 bench_profiles.py pattern TIMING_JSON   (bench.py --pattern-probe)
 """
 from __future__ import annotations
 
@@ -273,6 +277,59 @@ def probe(title: str, workloads: str, timing_json: str, counter_csvs: list) -> s
     return path
 
 
+def pattern(timing_json: str) -> str:
+    """Tables of one `bench.py --pattern-probe` run -> profiles/access_pattern_probe.md."""
+    with open(timing_json) as fh:
+        t = json.loads(fh.read().strip().splitlines()[-1])["pattern_probe"]
+
+    def cell(f):
+        return f"{f['us']} ({f['TBps']})"
+
+    out = ["# Access-pattern probe", "",
+           "The access shapes the sender, receiver and combine were chosen on, measured with",
+           "the library's `ep_probe_pattern` (each wave moves one piece of the output, 16",
+           "bytes per lane at a time, non-temporal stores). Each figure is the median of 5",
+           "launches, each alone between two HIP events, back to back unless stated: µs",
+           "(TB/s of the bytes given).", "",
+           "Commands (MI355X, one GPU):", "", "```",
+           "python3 /root/repo/bench.py --pattern-probe > <timing json>",
+           "python3 bench_profiles.py pattern <timing json>", "```", "",
+           "## Fills of 1 GiB (bytes written)", "", "| shape | µs (TB/s) |", "|---|---|"]
+    for k, f in t["fill_1GiB"].items():
+        out.append(f"| {k.replace('_', ' ')} | {cell(f)} |")
+    c = t["copy_decode_size"]
+    b = c["bytes"]
+    out += ["", "## Copies of the decode size: 32768 rows of 14 KB written", "",
+            f"Bytes: {b['linear_and_permuted']} (read + write) for the linear and permuted "
+            f"copies; {b['sender_like']} (token rows once + writes) for the sender-like ones, "
+            "which read each of 4096 token rows 8 times in the decode routing's send order.",
+            "", "| per wave | linear (nt loads) | rows permuted (nt) | sender-like: cached, XCD "
+            "order | cached | nt, XCD order |", "|---|---|---|---|---|---|"]
+    for k, f in c["figures"].items():
+        out.append(f"| {k.split('_')[0]} | {cell(f['linear'])} | {cell(f['rows_permuted'])} | "
+                   f"{cell(f['sender_like_cached_xcd'])} | {cell(f['sender_like_cached'])} | "
+                   f"{cell(f['sender_like_nt_xcd'])} |")
+    m = t["combine_mix_decode_size"]
+    out += ["", "## The combine's 8:1 mix at the decode size", "",
+            f"4096 rows of 14 KB, each the xor of 8 rows from 8 linear regions: {m['bytes']} "
+            "bytes (470 MB read, 59 MB written); the read-only lines read the 470 MB alone.",
+            "", "| shape | µs (TB/s) |", "|---|---|"]
+    for k, f in m["figures"].items():
+        out.append(f"| {k.replace('_', ' ')} | {cell(f)} |")
+    out += ["", "## Reuse from the memory-side cache", "",
+            "A buffer read with 1 KB per wave right after a fill of the same bytes, right "
+            "after a read of them, and after a flush (1 GiB fill + 1 GiB read).", "",
+            "| size | loads | after fill | after read | after flush |", "|---|---|---|---|---|"]
+    for size, e in t["mall_reuse"].items():
+        for loads in ("nt", "cached"):
+            out.append(f"| {size} | {loads} | {cell(e[loads + '_after_fill'])} | "
+                       f"{cell(e[loads + '_after_read'])} | {cell(e[loads + '_after_flush'])} |")
+    path = os.path.join(PROFILES, "access_pattern_probe.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    return path
+
+
 def main(argv) -> int:
     if len(argv) >= 4 and argv[0] == "trace":
         print(trace(argv[1], argv[2], argv[3]))
@@ -282,6 +339,9 @@ def main(argv) -> int:
         return 0
     if len(argv) >= 5 and argv[0] == "probe":
         print(probe(argv[1], argv[2], argv[3], argv[4:]))
+        return 0
+    if len(argv) >= 2 and argv[0] == "pattern":
+        print(pattern(argv[1]))
         return 0
     print(__doc__, file=sys.stderr)
     return 2

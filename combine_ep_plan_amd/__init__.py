@@ -28,6 +28,8 @@ EP_STATUS_BAD_REGION = 4
 EP_PAYLOAD_BF16 = 0
 EP_PAYLOAD_FP8_B128 = 1
 EP_KV_STATIC_SLOTS = 64
+EP_PROBE_COPY, EP_PROBE_FILL, EP_PROBE_READ = 0, 1, 2
+EP_PROBE_NT_LOADS, EP_PROBE_XCD = 1, 2
 
 # Every entry point the C header declares (checked by the tests).
 EXPORTS = (
@@ -41,7 +43,7 @@ EXPORTS = (
     "ep_expert_stub", "ep_combine",
     "ep_combine_presum", "ep_kv_plan", "ep_kv_push", "ep_kv_push_staged",
     "ep_kv_push_staged_static",
-    "ep_probe_copy", "ep_status_string",
+    "ep_probe_copy", "ep_probe_pattern", "ep_status_string",
     "ep_last_error",
 )
 
@@ -110,6 +112,8 @@ def _load() -> ctypes.CDLL:
         "ep_kv_push_staged_static": (ctypes.c_int, [ctypes.c_int32, P, I64, I64, P, I64, P, I64,
                                                     ctypes.c_int32, P, P, P]),
         "ep_probe_copy": (ctypes.c_int, [P, P, ctypes.c_size_t, P]),
+        "ep_probe_pattern": (ctypes.c_int, [P, P, P, I64, I64, I64, I64, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, I64, P]),
         "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "ep_last_error": (ctypes.c_char_p, []),
     }
@@ -361,6 +365,16 @@ def kv_push_staged_static(ranks: int, regions, n_regions: int, total_bytes: int,
 
 def probe_copy(dst, src, nbytes: int, stream=None) -> None:
     _check(_lib.ep_probe_copy(_addr(dst), _addr(src), nbytes, _stream(stream)), "ep_probe_copy")
+
+
+def probe_pattern(dst, src, table, rows: int, src_rows: int, row_bytes: int, piece_bytes: int,
+                  fan_in: int = 1, in_flight: int = 0, mode: int = EP_PROBE_COPY,
+                  flags: int = 0, waves: int = 0, stream=None) -> None:
+    """in_flight 0 means all fan_in rows at once."""
+    _check(_lib.ep_probe_pattern(_addr(dst), _addr(src), _addr(table), int(rows), int(src_rows),
+                                 int(row_bytes), int(piece_bytes), int(fan_in),
+                                 int(in_flight or fan_in), int(mode), int(flags), int(waves),
+                                 _stream(stream)), "ep_probe_pattern")
 
 
 # ---------------------------------------------------------------------------

@@ -16,6 +16,7 @@
 #include <string>
 
 #include "ep_kernels.hpp"
+#include "ep_probe.hpp"
 
 namespace {
 
@@ -680,6 +681,66 @@ int ep_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) 
   EP_CHECK(check_ptr(src, scope.device(), "src", (int64_t)bytes));
   const hipError_t e = ep::launch_probe_copy(dst, src, bytes, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_probe_copy");
+  return EP_OK;
+}
+
+int ep_probe_pattern(void* dst, const void* src, const int32_t* table, int64_t rows,
+                     int64_t src_rows, int64_t row_bytes, int64_t piece_bytes, int fan_in,
+                     int in_flight, int mode, int flags, int64_t waves, hipStream_t stream) {
+  if (mode != EP_PROBE_COPY && mode != EP_PROBE_FILL && mode != EP_PROBE_READ)
+    return fail(EP_ERR_INVALID_ARG, "unknown probe mode");
+  if (flags & ~(EP_PROBE_NT_LOADS | EP_PROBE_XCD))
+    return fail(EP_ERR_INVALID_ARG, "unknown probe flags");
+  if (rows < 0 || src_rows < 0 || waves < 0)
+    return fail(EP_ERR_INVALID_ARG, "rows, src_rows and waves must be >= 0");
+  if (piece_bytes <= 0 || piece_bytes % 1024 != 0 || row_bytes <= 0 ||
+      row_bytes % piece_bytes != 0)
+    return fail(EP_ERR_INVALID_ARG,
+                "piece_bytes must be a positive multiple of 1024 that divides row_bytes");
+  if (mode == EP_PROBE_COPY ? (fan_in != 1 && fan_in != 2 && fan_in != 4 && fan_in != 8)
+                            : fan_in != 1)
+    return fail(EP_ERR_INVALID_ARG, "fan_in must be 1, 2, 4 or 8 (copy) or 1");
+  if ((in_flight != 1 && in_flight != 2 && in_flight != 4 && in_flight != 8) ||
+      fan_in % in_flight != 0)
+    return fail(EP_ERR_INVALID_ARG, "in_flight must be 1, 2, 4 or 8 and divide fan_in");
+  if (waves > 0 && (flags & EP_PROBE_XCD))
+    return fail(EP_ERR_INVALID_ARG, "the XCD renumbering applies to one piece per wave only");
+  if (ep::probe_inflight((int)piece_bytes, in_flight) == 0)
+    return fail(EP_ERR_UNSUPPORTED, "no probe kernel for this piece size and fan_in");
+  if (row_bytes > ((int64_t)1 << 30) || rows * (row_bytes / piece_bytes) >= ((int64_t)1 << 31) ||
+      src_rows >= ((int64_t)1 << 31) || waves >= kMaxWaves)
+    return fail(EP_ERR_UNSUPPORTED, "probe too large");
+  const bool reads = mode != EP_PROBE_FILL;
+  if (reads && rows > 0) {
+    if (table == nullptr && src_rows < rows * fan_in)
+      return fail(EP_ERR_INVALID_ARG, "src_rows must cover rows * fan_in without a table");
+    if (table != nullptr && src_rows < 1) return fail(EP_ERR_INVALID_ARG, "src_rows must be >= 1");
+  }
+  DeviceScope scope(stream);
+  if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");
+  EP_CHECK(check_ptr(dst, scope.device(), "dst",
+                     mode == EP_PROBE_READ ? (rows > 0 ? 256 : 0) : rows * row_bytes));
+  if (reads && rows > 0) {
+    EP_CHECK(check_ptr(src, scope.device(), "src", src_rows * row_bytes));
+    if (table != nullptr)
+      EP_CHECK(check_ptr(table, scope.device(), "table", rows * fan_in * 4));
+  }
+  ep::ProbeShape sh{};
+  sh.dst = dst;
+  sh.src = reads ? src : nullptr;
+  sh.table = reads ? table : nullptr;
+  sh.rows = (int32_t)rows;
+  sh.src_rows = (int32_t)src_rows;
+  sh.row_bytes = (int32_t)row_bytes;
+  sh.piece_bytes = (int32_t)piece_bytes;
+  sh.fan_in = fan_in;
+  sh.in_flight = in_flight;
+  sh.mode = mode;
+  sh.nt_loads = (flags & EP_PROBE_NT_LOADS) != 0;
+  sh.xcd = (flags & EP_PROBE_XCD) != 0;
+  sh.waves = (int32_t)waves;
+  const hipError_t e = ep::launch_probe_pattern(sh, stream);
+  if (e != hipSuccess) return fail_hip(e, "ep_probe_pattern");
   return EP_OK;
 }
 

@@ -100,6 +100,28 @@ def test_invalid_descriptors_fail_fast(bad, code):
         assert ep.last_error() != ""
 
 
+# ep_probe_pattern's argument checks, all taken before the device lookup:
+# (rows, src_rows, row_bytes, piece_bytes, fan_in, in_flight, mode, flags, waves).
+@pytest.mark.parametrize("args,code", [
+    ((4, 4, 14336, 1024, 1, 1, 3, 0, 0), ep.EP_ERR_INVALID_ARG),          # unknown mode
+    ((4, 4, 14336, 1024, 1, 1, 0, 4, 0), ep.EP_ERR_INVALID_ARG),          # unknown flag
+    ((-1, 4, 14336, 1024, 1, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),         # negative rows
+    ((4, 4, 14336, 1000, 1, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),          # piece not 1 KB steps
+    ((4, 4, 14336, 4096, 1, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),          # piece does not divide row
+    ((4, 12, 14336, 1024, 3, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),         # fan_in 3
+    ((4, 32, 14336, 1024, 8, 3, 0, 0, 0), ep.EP_ERR_INVALID_ARG),         # in_flight 3
+    ((4, 32, 14336, 1024, 2, 4, 0, 0, 0), ep.EP_ERR_INVALID_ARG),         # in_flight > fan_in
+    ((4, 4, 14336, 1024, 2, 2, 1, 0, 0), ep.EP_ERR_INVALID_ARG),          # fan_in on a fill
+    ((4, 4, 14336, 1024, 1, 1, 0, 2, 64), ep.EP_ERR_INVALID_ARG),         # XCD order + grid-stride
+    ((4, 7, 14336, 1024, 2, 2, 0, 0, 0), ep.EP_ERR_INVALID_ARG),          # linear inputs short
+    ((1 << 22, 4, 1 << 20, 1024, 1, 1, 1, 0, 0), ep.EP_ERR_UNSUPPORTED),  # 2^32 pieces
+])
+def test_probe_pattern_rejects_bad_shapes(args, code):
+    fake = 0x10000
+    assert ep.lib().ep_probe_pattern(fake, fake, None, *args, None) == code
+    assert ep.last_error() != ""
+
+
 def test_null_descriptor():
     assert ep.lib().ep_plan(None, None, None, None, None) == ep.EP_ERR_INVALID_ARG
     assert ep.lib().ep_recv_bound(None) == -1
