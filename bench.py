@@ -834,7 +834,13 @@ def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
         470 MB read only;
       - memory-side cache reuse: 32, 128 and 512 MB read (non-temporal and
         cached loads) right after a fill of the same bytes, right after a
-        read of them, and after a flush."""
+        read of them, and after a flush;
+      - the sender's two orders by bytes per source: 8 sources of 128 to
+        2048 token rows of 14 KB (1.8 to 29 MB each), top-8 of 256 experts,
+        uniform routing; send order (the gather above: cached loads, XCD
+        renumbering, 1 KB per wave) against token order (a scatter: each
+        token row read once, non-temporal loads, and written to its 8 send
+        rows, 1 KB or 14 KB per wave)."""
     import gc
 
     stream = torch.cuda.current_stream()
@@ -952,6 +958,36 @@ def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
         del buf, sink
         torch.cuda.empty_cache()
     res["mall_reuse"] = reuse
+
+    # Send order against token order by bytes per source.
+    SCATTER = ep.EP_PROBE_SCATTER
+    orders = {}
+    N, R, E = 8, 8, 256
+    for T in (128, 256, 512, 1024, 2048):
+        rng = np.random.default_rng(1000 + T)
+        idx = np.argsort(rng.random((N, T, E)), axis=-1, kind="stable")[..., :R]
+        order = np.argsort(idx.reshape(N, T * R), axis=1, kind="stable")
+        gather = (np.arange(N)[:, None] * T + order // R).astype(np.int32).reshape(-1)
+        pos = np.empty_like(order)
+        np.put_along_axis(pos, order, np.arange(T * R)[None, :], axis=1)
+        scatter = (np.arange(N)[:, None] * T * R + pos).astype(np.int32).reshape(-1)
+        src = torch.randint(0, 255, (N * T, row), dtype=torch.uint8, device="cuda")
+        dst = torch.empty((N * T * R, row), dtype=torch.uint8, device="cuda")
+        gt = torch.from_numpy(gather).cuda()
+        st = torch.from_numpy(scatter).cuda()
+        nb = N * T * row + N * T * R * row
+        orders[f"{T * row / 1e6:.1f}MB_per_source"] = {
+            "tokens": T,
+            "send_order_1KB": fig(probe(dst, src, gt, N * T * R, N * T, row, 1024, flags=XCD),
+                                  nb),
+            "token_order_1KB": fig(probe(dst, src, st, N * T, N * T * R, row, 1024, fan_in=R,
+                                         mode=SCATTER, flags=NTL), nb),
+            "token_order_14KB": fig(probe(dst, src, st, N * T, N * T * R, row, row, fan_in=R,
+                                          mode=SCATTER, flags=NTL), nb),
+        }
+        del src, dst, gt, st
+        torch.cuda.empty_cache()
+    res["sender_orders_by_source_size"] = orders
     return res
 
 

@@ -324,6 +324,18 @@ def pattern(timing_json: str) -> str:
         for loads in ("nt", "cached"):
             out.append(f"| {size} | {loads} | {cell(e[loads + '_after_fill'])} | "
                        f"{cell(e[loads + '_after_read'])} | {cell(e[loads + '_after_flush'])} |")
+    if "sender_orders_by_source_size" in t:
+        out += ["", "## The sender's orders by bytes per source", "",
+                "8 sources of T token rows of 14 KB, top-8 of 256 experts, uniform routing; "
+                "bytes: the token rows once plus the 8 T send rows of each source. Send order: "
+                "the gather (cached loads, XCD renumbering, 1 KB per wave). Token order: a "
+                "scatter (each token row read once with non-temporal loads and written to its "
+                "8 send rows).", "",
+                "| per source | T | send order, 1 KB | token order, 1 KB | token order, 14 KB |",
+                "|---|---|---|---|---|"]
+        for k, e in t["sender_orders_by_source_size"].items():
+            out.append(f"| {k.split('_')[0]} | {e['tokens']} | {cell(e['send_order_1KB'])} | "
+                       f"{cell(e['token_order_1KB'])} | {cell(e['token_order_14KB'])} |")
     path = os.path.join(PROFILES, "access_pattern_probe.md")
     with open(path, "w") as fh:
         fh.write("\n".join(out) + "\n")

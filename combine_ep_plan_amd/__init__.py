@@ -28,7 +28,7 @@ EP_STATUS_BAD_REGION = 4
 EP_PAYLOAD_BF16 = 0
 EP_PAYLOAD_FP8_B128 = 1
 EP_KV_STATIC_SLOTS = 64
-EP_PROBE_COPY, EP_PROBE_FILL, EP_PROBE_READ = 0, 1, 2
+EP_PROBE_COPY, EP_PROBE_FILL, EP_PROBE_READ, EP_PROBE_SCATTER = 0, 1, 2, 3
 EP_PROBE_NT_LOADS, EP_PROBE_XCD = 1, 2
 
 # Every entry point the C header declares (checked by the tests).
@@ -367,13 +367,16 @@ def probe_copy(dst, src, nbytes: int, stream=None) -> None:
     _check(_lib.ep_probe_copy(_addr(dst), _addr(src), nbytes, _stream(stream)), "ep_probe_copy")
 
 
-def probe_pattern(dst, src, table, rows: int, src_rows: int, row_bytes: int, piece_bytes: int,
-                  fan_in: int = 1, in_flight: int = 0, mode: int = EP_PROBE_COPY,
-                  flags: int = 0, waves: int = 0, stream=None) -> None:
-    """in_flight 0 means all fan_in rows at once."""
-    _check(_lib.ep_probe_pattern(_addr(dst), _addr(src), _addr(table), int(rows), int(src_rows),
-                                 int(row_bytes), int(piece_bytes), int(fan_in),
-                                 int(in_flight or fan_in), int(mode), int(flags), int(waves),
+def probe_pattern(dst, src, table, rows: int, indexed_rows: int, row_bytes: int,
+                  piece_bytes: int, fan_in: int = 1, in_flight: int = 0,
+                  mode: int = EP_PROBE_COPY, flags: int = 0, waves: int = 0,
+                  stream=None) -> None:
+    """in_flight 0 means all fan_in rows at once (1 for a scatter)."""
+    if not in_flight:
+        in_flight = 1 if mode == EP_PROBE_SCATTER else fan_in
+    _check(_lib.ep_probe_pattern(_addr(dst), _addr(src), _addr(table), int(rows),
+                                 int(indexed_rows), int(row_bytes), int(piece_bytes),
+                                 int(fan_in), int(in_flight), int(mode), int(flags), int(waves),
                                  _stream(stream)), "ep_probe_pattern")
 
 

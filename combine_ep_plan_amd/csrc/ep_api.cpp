@@ -685,43 +685,52 @@ int ep_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) 
 }
 
 int ep_probe_pattern(void* dst, const void* src, const int32_t* table, int64_t rows,
-                     int64_t src_rows, int64_t row_bytes, int64_t piece_bytes, int fan_in,
+                     int64_t indexed_rows, int64_t row_bytes, int64_t piece_bytes, int fan_in,
                      int in_flight, int mode, int flags, int64_t waves, hipStream_t stream) {
-  if (mode != EP_PROBE_COPY && mode != EP_PROBE_FILL && mode != EP_PROBE_READ)
+  if (mode != EP_PROBE_COPY && mode != EP_PROBE_FILL && mode != EP_PROBE_READ &&
+      mode != EP_PROBE_SCATTER)
     return fail(EP_ERR_INVALID_ARG, "unknown probe mode");
   if (flags & ~(EP_PROBE_NT_LOADS | EP_PROBE_XCD))
     return fail(EP_ERR_INVALID_ARG, "unknown probe flags");
-  if (rows < 0 || src_rows < 0 || waves < 0)
-    return fail(EP_ERR_INVALID_ARG, "rows, src_rows and waves must be >= 0");
+  if (rows < 0 || indexed_rows < 0 || waves < 0)
+    return fail(EP_ERR_INVALID_ARG, "rows, indexed_rows and waves must be >= 0");
   if (piece_bytes <= 0 || piece_bytes % 1024 != 0 || row_bytes <= 0 ||
       row_bytes % piece_bytes != 0)
     return fail(EP_ERR_INVALID_ARG,
                 "piece_bytes must be a positive multiple of 1024 that divides row_bytes");
-  if (mode == EP_PROBE_COPY ? (fan_in != 1 && fan_in != 2 && fan_in != 4 && fan_in != 8)
-                            : fan_in != 1)
-    return fail(EP_ERR_INVALID_ARG, "fan_in must be 1, 2, 4 or 8 (copy) or 1");
+  const bool fans = mode == EP_PROBE_COPY || mode == EP_PROBE_SCATTER;
+  if (fans ? (fan_in != 1 && fan_in != 2 && fan_in != 4 && fan_in != 8) : fan_in != 1)
+    return fail(EP_ERR_INVALID_ARG, "fan_in must be 1, 2, 4 or 8 (copy, scatter) or 1");
   if ((in_flight != 1 && in_flight != 2 && in_flight != 4 && in_flight != 8) ||
-      fan_in % in_flight != 0)
-    return fail(EP_ERR_INVALID_ARG, "in_flight must be 1, 2, 4 or 8 and divide fan_in");
+      fan_in % in_flight != 0 || (mode == EP_PROBE_SCATTER && in_flight != 1))
+    return fail(EP_ERR_INVALID_ARG,
+                "in_flight must be 1, 2, 4 or 8 and divide fan_in (1 for a scatter)");
   if (waves > 0 && (flags & EP_PROBE_XCD))
     return fail(EP_ERR_INVALID_ARG, "the XCD renumbering applies to one piece per wave only");
   if (ep::probe_inflight((int)piece_bytes, in_flight) == 0)
-    return fail(EP_ERR_UNSUPPORTED, "no probe kernel for this piece size and fan_in");
+    return fail(EP_ERR_UNSUPPORTED, "no probe kernel for this piece size and in_flight");
   if (row_bytes > ((int64_t)1 << 30) || rows * (row_bytes / piece_bytes) >= ((int64_t)1 << 31) ||
-      src_rows >= ((int64_t)1 << 31) || waves >= kMaxWaves)
+      indexed_rows >= ((int64_t)1 << 31) || waves >= kMaxWaves)
     return fail(EP_ERR_UNSUPPORTED, "probe too large");
   const bool reads = mode != EP_PROBE_FILL;
-  if (reads && rows > 0) {
-    if (table == nullptr && src_rows < rows * fan_in)
-      return fail(EP_ERR_INVALID_ARG, "src_rows must cover rows * fan_in without a table");
-    if (table != nullptr && src_rows < 1) return fail(EP_ERR_INVALID_ARG, "src_rows must be >= 1");
+  const bool indexed = mode != EP_PROBE_FILL;  // the table indexes src, or dst for a scatter
+  if (indexed && rows > 0) {
+    if (table == nullptr && indexed_rows < rows * fan_in)
+      return fail(EP_ERR_INVALID_ARG, "indexed_rows must cover rows * fan_in without a table");
+    if (table != nullptr && indexed_rows < 1)
+      return fail(EP_ERR_INVALID_ARG, "indexed_rows must be >= 1");
+  }
+  int64_t dst_bytes = rows * row_bytes, src_bytes = indexed_rows * row_bytes;
+  if (mode == EP_PROBE_READ) dst_bytes = rows > 0 ? 256 : 0;
+  if (mode == EP_PROBE_SCATTER) {
+    dst_bytes = rows > 0 ? indexed_rows * row_bytes : 0;
+    src_bytes = rows * row_bytes;
   }
   DeviceScope scope(stream);
   if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");
-  EP_CHECK(check_ptr(dst, scope.device(), "dst",
-                     mode == EP_PROBE_READ ? (rows > 0 ? 256 : 0) : rows * row_bytes));
+  EP_CHECK(check_ptr(dst, scope.device(), "dst", dst_bytes));
   if (reads && rows > 0) {
-    EP_CHECK(check_ptr(src, scope.device(), "src", src_rows * row_bytes));
+    EP_CHECK(check_ptr(src, scope.device(), "src", src_bytes));
     if (table != nullptr)
       EP_CHECK(check_ptr(table, scope.device(), "table", rows * fan_in * 4));
   }
@@ -730,7 +739,7 @@ int ep_probe_pattern(void* dst, const void* src, const int32_t* table, int64_t r
   sh.src = reads ? src : nullptr;
   sh.table = reads ? table : nullptr;
   sh.rows = (int32_t)rows;
-  sh.src_rows = (int32_t)src_rows;
+  sh.indexed_rows = (int32_t)indexed_rows;
   sh.row_bytes = (int32_t)row_bytes;
   sh.piece_bytes = (int32_t)piece_bytes;
   sh.fan_in = fan_in;

@@ -17,7 +17,10 @@
 //   fill: every piece written with a pattern, nothing read;
 //   read: rows read (from `table` or in order), nothing written except, for
 //         a pattern no probe input holds, one word per lane at dst (keeps the
-//         loads live; dst holds 256 bytes).
+//         loads live; dst holds 256 bytes);
+//   scatter: source row i, piece p, read once and written to its fan_in
+//         output rows table[i * fan_in + k] (without a table, rows
+//         i * fan_in + k): the token-order sender's shape.
 #include "ep_device.hpp"
 #include "ep_probe.hpp"
 
@@ -31,12 +34,12 @@ struct ProbeArgs {
   u32x4* dst;
   const u32x4* src;
   const int32_t* table;
-  int32_t rows, src_rows;
+  int32_t rows, indexed_rows;
   int32_t row16, piece16;  // 16-byte chunks per row and per piece
   int32_t ppr;             // pieces per row
   uint32_t div_m, div_l;   // n / ppr = (mulhi(n, m) + n) >> l
   int32_t pieces;          // rows * ppr
-  int32_t fan_in;          // source rows per output row, a multiple of F
+  int32_t fan_in;          // source rows per output row (a multiple of F), or the reverse
   int32_t stride;          // waves of a grid-stride launch, 0 otherwise
   int32_t xcd, nb;         // XCD renumbering; launched blocks (a multiple of 8 with it)
 };
@@ -49,6 +52,9 @@ __device__ __forceinline__ u32x4 probe_load(const u32x4* p) {
 
 // One piece. V chunks per lane and F of the fan_in source rows are in
 // flight per batch.
+// The table is read-only for the launch: read through the constant address
+// space, each wave-uniform entry comes by one scalar load, as the sender's
+// send_slot entry does.
 template <int MODE, int V, int F, bool NT>
 __device__ __forceinline__ void probe_piece(const ProbeArgs& a, int w) {
   const int row = wave_uniform(
@@ -56,6 +62,25 @@ __device__ __forceinline__ void probe_piece(const ProbeArgs& a, int w) {
   const int pc = w - row * a.ppr;
   const int64_t off = (int64_t)pc * a.piece16 + lane_id();
   const int64_t out = (int64_t)row * a.row16 + off;
+  typedef const __attribute__((address_space(4))) int32_t* const_table;
+  if (MODE == kProbeScatter) {
+    const int64_t in = (int64_t)row * a.row16 + off;
+    for (int c0 = 0; c0 < a.piece16; c0 += kWave * V) {
+      u32x4 r[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) r[i] = probe_load<NT>(&a.src[in + c0 + kWave * i]);
+      asm volatile("" ::: "memory");
+      for (int k = 0; k < a.fan_in; ++k) {
+        int d = a.table ? ((const_table)a.table)[(int64_t)row * a.fan_in + k]
+                        : row * a.fan_in + k;
+        if ((uint32_t)d >= (uint32_t)a.indexed_rows) d = 0;  // any table entry stays in bounds
+        const int64_t o = (int64_t)d * a.row16 + off + c0;
+#pragma unroll
+        for (int i = 0; i < V; ++i) store_stream(&a.dst[o + kWave * i], r[i]);
+      }
+    }
+    return;
+  }
   if (MODE == kProbeFill) {
     const u32x4 v = {(uint32_t)w, (uint32_t)lane_id(), 0x5a5a5a5au, 0u};
     for (int c0 = 0; c0 < a.piece16; c0 += kWave * V) {
@@ -64,10 +89,6 @@ __device__ __forceinline__ void probe_piece(const ProbeArgs& a, int w) {
     }
     return;
   }
-  // The table is read-only for the launch: read through the constant
-  // address space, each wave-uniform entry comes by one scalar load, as the
-  // sender's send_slot entry does.
-  typedef const __attribute__((address_space(4))) int32_t* const_table;
   for (int c0 = 0; c0 < a.piece16; c0 += kWave * V) {
     u32x4 acc[V];
 #pragma unroll
@@ -78,7 +99,7 @@ __device__ __forceinline__ void probe_piece(const ProbeArgs& a, int w) {
       for (int j = 0; j < F; ++j) {
         const int k = k0 + j;
         int s = a.table ? ((const_table)a.table)[(int64_t)row * a.fan_in + k] : row + k * a.rows;
-        if ((uint32_t)s >= (uint32_t)a.src_rows) s = 0;  // any table entry stays in bounds
+        if ((uint32_t)s >= (uint32_t)a.indexed_rows) s = 0;  // any table entry stays in bounds
         const int64_t in = (int64_t)s * a.row16 + off + c0;
 #pragma unroll
         for (int i = 0; i < V; ++i) r[j][i] = probe_load<NT>(&a.src[in + kWave * i]);
@@ -159,7 +180,7 @@ hipError_t launch_probe_pattern(const ProbeShape& s, hipStream_t stream) {
   a.table = s.table;
   a.fan_in = s.fan_in;
   a.rows = s.rows;
-  a.src_rows = s.src_rows;
+  a.indexed_rows = s.indexed_rows;
   a.row16 = s.row_bytes / 16;
   a.piece16 = s.piece_bytes / 16;
   a.ppr = s.row_bytes / s.piece_bytes;
@@ -179,6 +200,7 @@ hipError_t launch_probe_pattern(const ProbeShape& s, hipStream_t stream) {
   switch (s.mode) {
     case kProbeFill: return launch_f<kProbeFill, 1>(a, v, false, stream);
     case kProbeRead: return launch_f<kProbeRead, 1>(a, v, s.nt_loads, stream);
+    case kProbeScatter: return launch_f<kProbeScatter, 1>(a, v, s.nt_loads, stream);
     case kProbeCopy:
       switch (s.in_flight) {
         case 1: return launch_f<kProbeCopy, 1>(a, v, s.nt_loads, stream);

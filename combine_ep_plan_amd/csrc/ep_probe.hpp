@@ -7,17 +7,18 @@
 
 namespace ep {
 
-enum ProbeMode { kProbeCopy = 0, kProbeFill = 1, kProbeRead = 2 };
+enum ProbeMode { kProbeCopy = 0, kProbeFill = 1, kProbeRead = 2, kProbeScatter = 3 };
 
 struct ProbeShape {
   void* dst;
   const void* src;
-  const int32_t* table;  // source row per (output row, input), or null
-  int32_t rows;          // output rows (rows read, for kProbeRead)
-  int32_t src_rows;      // rows of src
+  const int32_t* table;  // row per (walked row, input or output), or null
+  int32_t rows;          // rows walked: output rows (copy, fill), rows read (read, scatter)
+  int32_t indexed_rows;  // rows of the buffer the table indexes (src; dst for scatter)
   int32_t row_bytes;     // multiple of piece_bytes
   int32_t piece_bytes;   // multiple of 1024: the bytes one wave moves
-  int32_t fan_in;        // source rows per output row (copy: 1, 2, 4 or 8)
+  int32_t fan_in;        // source rows per output row (copy), output rows per source row
+                         // (scatter): 1, 2, 4 or 8
   int32_t in_flight;     // of them loaded together (divides fan_in)
   int32_t mode;          // ProbeMode
   bool nt_loads;         // non-temporal loads (else ordinary cached ones)

@@ -468,33 +468,38 @@ EP_API int ep_probe_copy(void *dst, const void *src, size_t bytes,
 
 /* Access-pattern probe: a bandwidth reference for measurements, not part of
  * the method. It moves data in the shapes the sender, receiver and combine
- * were chosen on: each wave handles one piece of piece_bytes of the output,
- * consecutive waves consecutive pieces (or, with waves > 0, that many waves
- * walk the pieces grid-stride), 16 bytes per lane at a time, with
- * non-temporal stores.
+ * were chosen on. A launch walks `rows` rows in pieces of piece_bytes; each
+ * wave handles one piece, consecutive waves consecutive pieces (or, with
+ * waves > 0, that many waves walk the pieces grid-stride), 16 bytes per lane
+ * at a time, with non-temporal stores. `table` (int32, fan_in entries per
+ * walked row, or NULL) indexes a buffer of indexed_rows rows; entries
+ * outside [0, indexed_rows) stand for row 0.
  *   EP_PROBE_COPY: dst row i = xor of fan_in (1, 2, 4 or 8) rows of src,
- *     rows table[i * fan_in + j] (entries outside [0, src_rows) read row 0)
- *     or, with table NULL, rows i + j * rows (fan_in = 1: a plain copy),
- *     loaded in_flight (1, 2, 4 or 8, dividing fan_in) rows at a time;
- *   EP_PROBE_FILL: dst rows written with a pattern, src not read (here and
- *     for EP_PROBE_READ, fan_in = in_flight = 1);
+ *     rows table[i * fan_in + j] or, with table NULL, rows i + j * rows
+ *     (fan_in = 1: a plain copy), loaded in_flight (1, 2, 4 or 8, dividing
+ *     fan_in) rows at a time; src holds indexed_rows rows, dst `rows`;
+ *   EP_PROBE_SCATTER: src row i written to dst rows table[i * fan_in + k]
+ *     (with table NULL, rows i * fan_in + k), read once (in_flight = 1); src
+ *     holds `rows` rows, dst indexed_rows;
+ *   EP_PROBE_FILL: dst rows written with a pattern, src not read;
  *   EP_PROBE_READ: src rows (table[i] or i) read; dst (256 bytes) is
  *     written only where a lane's xor of its data equals 0x9e3779b9.
+ *   Fill and read take fan_in = in_flight = 1.
  * Flags: EP_PROBE_NT_LOADS (non-temporal loads; else ordinary cached ones),
  * EP_PROBE_XCD (blocks renumbered as the sender's: XCD x takes the x-th
  * eighth of the pieces; one piece per wave only).
- * Layout: rows of row_bytes, row-major; table int32 [rows][fan_in]. All
- * buffers are caller-owned device memory on the stream's GPU.
- * row_bytes must be a multiple of piece_bytes, piece_bytes of 1024. Returns
- * EP_ERR_INVALID_ARG for a bad size, mode, flag or buffer,
- * EP_ERR_UNSUPPORTED beyond 2^31 pieces. */
+ * Rows are row_bytes long, row-major; all buffers are caller-owned device
+ * memory on the stream's GPU. row_bytes must be a multiple of piece_bytes,
+ * piece_bytes of 1024. Returns EP_ERR_INVALID_ARG for a bad size, mode, flag
+ * or buffer, EP_ERR_UNSUPPORTED beyond 2^31 pieces. */
 #define EP_PROBE_COPY 0
 #define EP_PROBE_FILL 1
 #define EP_PROBE_READ 2
+#define EP_PROBE_SCATTER 3
 #define EP_PROBE_NT_LOADS 1
 #define EP_PROBE_XCD 2
 EP_API int ep_probe_pattern(void *dst, const void *src, const int32_t *table,
-                            int64_t rows, int64_t src_rows, int64_t row_bytes,
+                            int64_t rows, int64_t indexed_rows, int64_t row_bytes,
                             int64_t piece_bytes, int fan_in, int in_flight, int mode,
                             int flags, int64_t waves, hipStream_t stream);
 

@@ -101,9 +101,9 @@ def test_invalid_descriptors_fail_fast(bad, code):
 
 
 # ep_probe_pattern's argument checks, all taken before the device lookup:
-# (rows, src_rows, row_bytes, piece_bytes, fan_in, in_flight, mode, flags, waves).
+# (rows, indexed_rows, row_bytes, piece_bytes, fan_in, in_flight, mode, flags, waves).
 @pytest.mark.parametrize("args,code", [
-    ((4, 4, 14336, 1024, 1, 1, 3, 0, 0), ep.EP_ERR_INVALID_ARG),          # unknown mode
+    ((4, 4, 14336, 1024, 1, 1, 4, 0, 0), ep.EP_ERR_INVALID_ARG),          # unknown mode
     ((4, 4, 14336, 1024, 1, 1, 0, 4, 0), ep.EP_ERR_INVALID_ARG),          # unknown flag
     ((-1, 4, 14336, 1024, 1, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),         # negative rows
     ((4, 4, 14336, 1000, 1, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),          # piece not 1 KB steps
@@ -114,6 +114,8 @@ def test_invalid_descriptors_fail_fast(bad, code):
     ((4, 4, 14336, 1024, 2, 2, 1, 0, 0), ep.EP_ERR_INVALID_ARG),          # fan_in on a fill
     ((4, 4, 14336, 1024, 1, 1, 0, 2, 64), ep.EP_ERR_INVALID_ARG),         # XCD order + grid-stride
     ((4, 7, 14336, 1024, 2, 2, 0, 0, 0), ep.EP_ERR_INVALID_ARG),          # linear inputs short
+    ((4, 32, 14336, 1024, 8, 2, 3, 0, 0), ep.EP_ERR_INVALID_ARG),         # scatter in_flight 2
+    ((4, 31, 14336, 1024, 8, 1, 3, 0, 0), ep.EP_ERR_INVALID_ARG),         # scatter targets short
     ((1 << 22, 4, 1 << 20, 1024, 1, 1, 1, 0, 0), ep.EP_ERR_UNSUPPORTED),  # 2^32 pieces
 ])
 def test_probe_pattern_rejects_bad_shapes(args, code):

@@ -2,8 +2,9 @@
 
 The probe is a measurement reference, not a step of the method, so it has
 no oracle: its results are checked against numpy definitions of each mode
-(copy: xor of the named source rows; fill: the pattern each wave writes;
-read: dst written only where a lane's data xors to the key).
+(copy: xor of the named source rows; scatter: each source row at its named
+output rows; fill: the pattern each wave writes; read: dst written only
+where a lane's data xors to the key).
 """
 import numpy as np
 import pytest
@@ -21,9 +22,9 @@ def rand_rows(rng, n, row=ROW):
     return rng.integers(0, 256, size=(n, row), dtype=np.uint8)
 
 
-def run(dst, src, table, rows, src_rows, piece, fan_in=1, mode=ep.EP_PROBE_COPY, flags=0,
+def run(dst, src, table, rows, indexed_rows, piece, fan_in=1, mode=ep.EP_PROBE_COPY, flags=0,
         waves=0, row=ROW, in_flight=0):
-    ep.probe_pattern(dst, src, table, rows, src_rows, row, piece, fan_in=fan_in,
+    ep.probe_pattern(dst, src, table, rows, indexed_rows, row, piece, fan_in=fan_in,
                      in_flight=in_flight, mode=mode, flags=flags, waves=waves)
     torch.cuda.synchronize()
     return dst.cpu().numpy()
@@ -77,6 +78,40 @@ def test_linear_mix_of_eight_regions():
     got = run(dst, src, None, rows, 8 * rows, 7168, 8, flags=ep.EP_PROBE_NT_LOADS, in_flight=2)
     want = xor_rows(a, np.arange(rows)[:, None] + rows * np.arange(8)[None, :])
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("piece,flags", [(1024, ep.EP_PROBE_NT_LOADS), (14336, 0),
+                                         (2048, ep.EP_PROBE_XCD)])
+def test_scatter(piece, flags):
+    rng = np.random.default_rng(piece + 7 * flags)
+    rows, fan, out_rows = 23, 8, 23 * 8
+    a = rand_rows(rng, rows)
+    # Every output row named once (a send order), two of them out of range.
+    idx = rng.permutation(out_rows).astype(np.int32).reshape(rows, fan)
+    src = torch.from_numpy(a).cuda()
+    dst = torch.zeros((out_rows, ROW), dtype=torch.uint8, device="cuda")
+    got = run(dst, src, torch.from_numpy(idx).cuda(), rows, out_rows, piece, fan,
+              mode=ep.EP_PROBE_SCATTER, flags=flags)
+    want = np.zeros_like(got)
+    for i in range(rows):
+        for k in range(fan):
+            want[idx[i, k]] = a[i]
+    assert np.array_equal(got, want)
+    # Without a table, row i goes to rows i * fan .. i * fan + fan - 1; an
+    # entry outside the output (row 0 stands in) lands on row 0.
+    dst.zero_()
+    got = run(dst, src, None, rows, out_rows, piece, fan, mode=ep.EP_PROBE_SCATTER, flags=flags)
+    assert np.array_equal(got, np.repeat(a, fan, axis=0))
+    idx2 = np.arange(out_rows, dtype=np.int32).reshape(rows, fan)
+    idx2[5, 3] = out_rows + 9
+    dst.zero_()
+    got = run(dst, src, torch.from_numpy(idx2).cuda(), rows, out_rows, piece, fan,
+              mode=ep.EP_PROBE_SCATTER, flags=flags)
+    want = np.repeat(a, fan, axis=0)
+    want[5 * fan + 3] = 0
+    assert np.array_equal(got[1:], want[1:])
+    # Row 0 is written by two sources; each piece holds one of them.
+    assert np.all((got[0] == a[0]) | (got[0] == a[5]))
 
 
 @pytest.mark.parametrize("piece,waves", [(1024, 0), (4096, 0), (65536, 0), (1024, 40)])
