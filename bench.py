@@ -822,6 +822,8 @@ def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
     events (back to back unless stated):
       - fills of 1 GiB: one piece of 1, 4, 14 or 64 KB per wave in output
         order, and 1 KB pieces walked grid-stride by 2048 or 8192 waves;
+      - copies of 1 GiB: 1 KB per wave, the library's copy probe (7 KB per
+        wave) and torch's device-to-device copy;
       - copies of the decode size (32768 rows of 14 KB, 470 MB out): linear,
         rows permuted at random, and sender-like (each of the 4096 token rows
         read 8 times, in the send order of the decode routing: per source,
@@ -884,7 +886,17 @@ def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
         fills[f"1KB_grid_stride_{waves}_waves"] = fig(
             probe(a, None, None, GiB // 65536, 0, 65536, 1024, mode=FILL, waves=waves), GiB)
     res["fill_1GiB"] = fills
-    del a
+    # Copies of 1 GiB (bytes read + written): the pattern probe's linear copy,
+    # the library's copy probe (7 KB per wave) and torch's device copy.
+    b = torch.empty_like(a)
+    rows = GiB // 65536
+    res["copy_1GiB"] = {
+        "1KB_per_wave_nt_loads": fig(probe(b, a, None, rows, rows, 65536, 1024, flags=NTL),
+                                     2 * GiB),
+        "ep_probe_copy_7KB_per_wave": fig(lambda: ep.probe_copy(b, a, GiB, sp), 2 * GiB),
+        "torch_copy_": fig(lambda: b[:GiB].copy_(a[:GiB]), 2 * GiB),
+    }
+    del a, b
     torch.cuda.empty_cache()
 
     # Copies at the decode size.

@@ -297,6 +297,14 @@ def pattern(timing_json: str) -> str:
            "## Fills of 1 GiB (bytes written)", "", "| shape | µs (TB/s) |", "|---|---|"]
     for k, f in t["fill_1GiB"].items():
         out.append(f"| {k.replace('_', ' ')} | {cell(f)} |")
+    if "copy_1GiB" in t:
+        out += ["", "## Copies of 1 GiB (bytes read + written)", "", "| copy | µs (TB/s) |",
+                "|---|---|"]
+        labels = {"1KB_per_wave_nt_loads": "access-pattern probe, 1 KB per wave, nt loads",
+                  "ep_probe_copy_7KB_per_wave": "`ep_probe_copy` (7 KB per wave)",
+                  "torch_copy_": "torch `copy_`"}
+        for k, f in t["copy_1GiB"].items():
+            out.append(f"| {labels.get(k, k)} | {cell(f)} |")
     c = t["copy_decode_size"]
     b = c["bytes"]
     out += ["", "## Copies of the decode size: 32768 rows of 14 KB written", "",
