@@ -711,7 +711,11 @@ def measure_sender_probe(ep, torch, np, W, flush) -> dict:
         read of its token rows;
       - that source with 1, 2 or 4 rows per token (E = 32 R experts, uniform
         distinct ids drawn from a fixed seed): the time of the token reads and
-        the quantisation against that of the extra rows.
+        the quantisation against that of the extra rows;
+      - the same loads and code-row stores with no arithmetic and no scale
+        rows (the access-pattern probe's wide scatter at the plan's send
+        positions), 1 or 7 KB of codes per wave, cached or non-temporal
+        loads, back to back and after a flush.
     Each figure is the median of 5 launches, each timed alone between two
     HIP events. The byte-equality checks compare the two-pass and
     per-source send buffers with the fused sender's."""
@@ -810,6 +814,27 @@ def measure_sender_probe(ep, torch, np, W, flush) -> dict:
         rsweep[f"R={r},E={e_r}"] = {"back_to_back": timed([fn, fn])[1]}
         del send_r, plan_r
     res["one_source_rows_per_token_us"] = rsweep
+    # The fused sender's loads and code-row stores without its arithmetic and
+    # scale rows: each bf16 token row read once, narrowed 2:1 (xor of
+    # adjacent 16-byte chunks) and written to its R send rows at the plan's
+    # stable positions, in token order (the access-pattern probe's wide
+    # scatter). It overwrites the code plane, so it runs last.
+    order = np.argsort(wl.idx.reshape(N, T * R), axis=1, kind="stable")
+    pos = np.empty_like(order)
+    np.put_along_axis(pos, order, np.arange(T * R)[None, :], axis=1)
+    table = torch.from_numpy(
+        (np.arange(N)[:, None] * T * R + pos).astype(np.int32).reshape(-1)).cuda()
+    codes = send[0].view(N * T * R, rows[0])
+    bare = {}
+    for kb in (1, 7):
+        for name, fl in (("cached", 0), ("nt", ep.EP_PROBE_NT_LOADS)):
+            fn = lambda: ep.probe_pattern(codes, x, table, N * T, N * T * R, rows[0], kb * 1024,
+                                          fan_in=R, mode=ep.EP_PROBE_SCATTER_WIDE, flags=fl,
+                                          stream=sp)
+            bare[f"{kb}KB_per_wave_{name}_loads"] = {"back_to_back": timed([fn, fn])[1],
+                                                     "after_flush": timed([fn], flush)[0]}
+    res["bare_scatter_bytes"] = N * T * 2 * H + N * T * R * rows[0]
+    res["bare_scatter_us"] = bare
     torch.cuda.synchronize()
     res["status_after"] = int(status.item())
     return res

@@ -28,7 +28,7 @@ EP_STATUS_BAD_REGION = 4
 EP_PAYLOAD_BF16 = 0
 EP_PAYLOAD_FP8_B128 = 1
 EP_KV_STATIC_SLOTS = 64
-EP_PROBE_COPY, EP_PROBE_FILL, EP_PROBE_READ, EP_PROBE_SCATTER = 0, 1, 2, 3
+EP_PROBE_COPY, EP_PROBE_FILL, EP_PROBE_READ, EP_PROBE_SCATTER, EP_PROBE_SCATTER_WIDE = range(5)
 EP_PROBE_NT_LOADS, EP_PROBE_XCD = 1, 2
 
 # Every entry point the C header declares (checked by the tests).
@@ -373,7 +373,7 @@ def probe_pattern(dst, src, table, rows: int, indexed_rows: int, row_bytes: int,
                   stream=None) -> None:
     """in_flight 0 means all fan_in rows at once (1 for a scatter)."""
     if not in_flight:
-        in_flight = 1 if mode == EP_PROBE_SCATTER else fan_in
+        in_flight = 1 if mode in (EP_PROBE_SCATTER, EP_PROBE_SCATTER_WIDE) else fan_in
     _check(_lib.ep_probe_pattern(_addr(dst), _addr(src), _addr(table), int(rows),
                                  int(indexed_rows), int(row_bytes), int(piece_bytes),
                                  int(fan_in), int(in_flight), int(mode), int(flags), int(waves),

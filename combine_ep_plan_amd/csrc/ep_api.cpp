@@ -687,8 +687,8 @@ int ep_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) 
 int ep_probe_pattern(void* dst, const void* src, const int32_t* table, int64_t rows,
                      int64_t indexed_rows, int64_t row_bytes, int64_t piece_bytes, int fan_in,
                      int in_flight, int mode, int flags, int64_t waves, hipStream_t stream) {
-  if (mode != EP_PROBE_COPY && mode != EP_PROBE_FILL && mode != EP_PROBE_READ &&
-      mode != EP_PROBE_SCATTER)
+  const bool scatter = mode == EP_PROBE_SCATTER || mode == EP_PROBE_SCATTER_WIDE;
+  if (mode != EP_PROBE_COPY && mode != EP_PROBE_FILL && mode != EP_PROBE_READ && !scatter)
     return fail(EP_ERR_INVALID_ARG, "unknown probe mode");
   if (flags & ~(EP_PROBE_NT_LOADS | EP_PROBE_XCD))
     return fail(EP_ERR_INVALID_ARG, "unknown probe flags");
@@ -698,18 +698,18 @@ int ep_probe_pattern(void* dst, const void* src, const int32_t* table, int64_t r
       row_bytes % piece_bytes != 0)
     return fail(EP_ERR_INVALID_ARG,
                 "piece_bytes must be a positive multiple of 1024 that divides row_bytes");
-  const bool fans = mode == EP_PROBE_COPY || mode == EP_PROBE_SCATTER;
+  const bool fans = mode == EP_PROBE_COPY || scatter;
   if (fans ? (fan_in != 1 && fan_in != 2 && fan_in != 4 && fan_in != 8) : fan_in != 1)
     return fail(EP_ERR_INVALID_ARG, "fan_in must be 1, 2, 4 or 8 (copy, scatter) or 1");
   if ((in_flight != 1 && in_flight != 2 && in_flight != 4 && in_flight != 8) ||
-      fan_in % in_flight != 0 || (mode == EP_PROBE_SCATTER && in_flight != 1))
+      fan_in % in_flight != 0 || (scatter && in_flight != 1))
     return fail(EP_ERR_INVALID_ARG,
                 "in_flight must be 1, 2, 4 or 8 and divide fan_in (1 for a scatter)");
   if (waves > 0 && (flags & EP_PROBE_XCD))
     return fail(EP_ERR_INVALID_ARG, "the XCD renumbering applies to one piece per wave only");
-  if (ep::probe_inflight((int)piece_bytes, in_flight) == 0)
+  if (ep::probe_inflight((int)piece_bytes, mode == EP_PROBE_SCATTER_WIDE ? 2 : in_flight) == 0)
     return fail(EP_ERR_UNSUPPORTED, "no probe kernel for this piece size and in_flight");
-  if (row_bytes > ((int64_t)1 << 30) || rows * (row_bytes / piece_bytes) >= ((int64_t)1 << 31) ||
+  if (row_bytes > ((int64_t)1 << 29) || rows * (row_bytes / piece_bytes) >= ((int64_t)1 << 31) ||
       indexed_rows >= ((int64_t)1 << 31) || waves >= kMaxWaves)
     return fail(EP_ERR_UNSUPPORTED, "probe too large");
   const bool reads = mode != EP_PROBE_FILL;
@@ -722,9 +722,9 @@ int ep_probe_pattern(void* dst, const void* src, const int32_t* table, int64_t r
   }
   int64_t dst_bytes = rows * row_bytes, src_bytes = indexed_rows * row_bytes;
   if (mode == EP_PROBE_READ) dst_bytes = rows > 0 ? 256 : 0;
-  if (mode == EP_PROBE_SCATTER) {
+  if (scatter) {
     dst_bytes = rows > 0 ? indexed_rows * row_bytes : 0;
-    src_bytes = rows * row_bytes;
+    src_bytes = rows * row_bytes * (mode == EP_PROBE_SCATTER_WIDE ? 2 : 1);
   }
   DeviceScope scope(stream);
   if (scope.error() != hipSuccess) return fail_hip(scope.error(), "device");

@@ -20,7 +20,10 @@
 //         loads live; dst holds 256 bytes);
 //   scatter: source row i, piece p, read once and written to its fan_in
 //         output rows table[i * fan_in + k] (without a table, rows
-//         i * fan_in + k): the token-order sender's shape.
+//         i * fan_in + k): the token-order sender's shape;
+//   scatter-wide: the same from source rows twice as long, each output
+//         chunk the xor of two adjacent source chunks (a 2:1 narrowing, as
+//         the quantising sender reads bf16 and writes one byte per value).
 #include "ep_device.hpp"
 #include "ep_probe.hpp"
 
@@ -63,12 +66,17 @@ __device__ __forceinline__ void probe_piece(const ProbeArgs& a, int w) {
   const int64_t off = (int64_t)pc * a.piece16 + lane_id();
   const int64_t out = (int64_t)row * a.row16 + off;
   typedef const __attribute__((address_space(4))) int32_t* const_table;
-  if (MODE == kProbeScatter) {
-    const int64_t in = (int64_t)row * a.row16 + off;
+  if (MODE == kProbeScatter || MODE == kProbeScatterWide) {
+    constexpr int S = MODE == kProbeScatterWide ? 2 : 1;  // source chunks per output chunk
+    const int64_t in = ((int64_t)row * a.row16 + off) * S;
     for (int c0 = 0; c0 < a.piece16; c0 += kWave * V) {
       u32x4 r[V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) r[i] = probe_load<NT>(&a.src[in + c0 + kWave * i]);
+      for (int i = 0; i < V; ++i) {
+        const int64_t c = in + (int64_t)(c0 + kWave * i) * S;
+        r[i] = probe_load<NT>(&a.src[c]);
+        if (S == 2) r[i] ^= probe_load<NT>(&a.src[c + 1]);
+      }
       asm volatile("" ::: "memory");
       for (int k = 0; k < a.fan_in; ++k) {
         int d = a.table ? ((const_table)a.table)[(int64_t)row * a.fan_in + k]
@@ -196,11 +204,12 @@ hipError_t launch_probe_pattern(const ProbeShape& s, hipStream_t stream) {
   a.xcd = s.xcd ? 1 : 0;
   if (s.xcd) nb = (nb + 7) / 8 * 8;
   a.nb = (int32_t)nb;
-  const int v = probe_inflight(s.piece_bytes, s.in_flight);
+  const int v = probe_inflight(s.piece_bytes, s.mode == kProbeScatterWide ? 2 : s.in_flight);
   switch (s.mode) {
     case kProbeFill: return launch_f<kProbeFill, 1>(a, v, false, stream);
     case kProbeRead: return launch_f<kProbeRead, 1>(a, v, s.nt_loads, stream);
     case kProbeScatter: return launch_f<kProbeScatter, 1>(a, v, s.nt_loads, stream);
+    case kProbeScatterWide: return launch_f<kProbeScatterWide, 1>(a, v, s.nt_loads, stream);
     case kProbeCopy:
       switch (s.in_flight) {
         case 1: return launch_f<kProbeCopy, 1>(a, v, s.nt_loads, stream);

@@ -7,7 +7,13 @@
 
 namespace ep {
 
-enum ProbeMode { kProbeCopy = 0, kProbeFill = 1, kProbeRead = 2, kProbeScatter = 3 };
+enum ProbeMode {
+  kProbeCopy = 0,
+  kProbeFill = 1,
+  kProbeRead = 2,
+  kProbeScatter = 3,
+  kProbeScatterWide = 4
+};
 
 struct ProbeShape {
   void* dst;

@@ -481,6 +481,9 @@ EP_API int ep_probe_copy(void *dst, const void *src, size_t bytes,
  *   EP_PROBE_SCATTER: src row i written to dst rows table[i * fan_in + k]
  *     (with table NULL, rows i * fan_in + k), read once (in_flight = 1); src
  *     holds `rows` rows, dst indexed_rows;
+ *   EP_PROBE_SCATTER_WIDE: the same from src rows of 2 * row_bytes, each
+ *     16-byte output chunk c the xor of src chunks 2c and 2c + 1 (the 2:1
+ *     narrowing of a bf16 -> one-byte sender);
  *   EP_PROBE_FILL: dst rows written with a pattern, src not read;
  *   EP_PROBE_READ: src rows (table[i] or i) read; dst (256 bytes) is
  *     written only where a lane's xor of its data equals 0x9e3779b9.
@@ -496,6 +499,7 @@ EP_API int ep_probe_copy(void *dst, const void *src, size_t bytes,
 #define EP_PROBE_FILL 1
 #define EP_PROBE_READ 2
 #define EP_PROBE_SCATTER 3
+#define EP_PROBE_SCATTER_WIDE 4
 #define EP_PROBE_NT_LOADS 1
 #define EP_PROBE_XCD 2
 EP_API int ep_probe_pattern(void *dst, const void *src, const int32_t *table,

@@ -114,6 +114,26 @@ def test_scatter(piece, flags):
     assert np.all((got[0] == a[0]) | (got[0] == a[5]))
 
 
+@pytest.mark.parametrize("piece,flags", [(1024, 0), (7168, ep.EP_PROBE_NT_LOADS)])
+def test_scatter_wide(piece, flags):
+    """Source rows twice as long: output chunk c = source chunk 2c xor 2c + 1."""
+    rng = np.random.default_rng(piece + 3)
+    rows, fan, out_rows, row = 19, 8, 19 * 8, 7168
+    a = rand_rows(rng, rows, 2 * row)
+    idx = rng.permutation(out_rows).astype(np.int32).reshape(rows, fan)
+    src = torch.from_numpy(a).cuda()
+    dst = torch.zeros((out_rows, row), dtype=torch.uint8, device="cuda")
+    got = run(dst, src, torch.from_numpy(idx).cuda(), rows, out_rows, piece, fan,
+              mode=ep.EP_PROBE_SCATTER_WIDE, flags=flags, row=row)
+    c = a.reshape(rows, -1, 2, 16)
+    narrow = (c[:, :, 0] ^ c[:, :, 1]).reshape(rows, row)
+    want = np.zeros_like(got)
+    for i in range(rows):
+        for k in range(fan):
+            want[idx[i, k]] = narrow[i]
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("piece,waves", [(1024, 0), (4096, 0), (65536, 0), (1024, 40)])
 def test_fill_pattern(piece, waves):
     row = 65536
