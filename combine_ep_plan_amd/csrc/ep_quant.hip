@@ -35,6 +35,16 @@ __device__ __forceinline__ int wave_index() {
   return wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
 }
 
+// A send position the whole wave reads (its index is wave-uniform), taken
+// through the constant address space so that it comes by a scalar load. The
+// plan wrote the table in an earlier launch; this one only reads it. With a
+// vector load, the wait for the entry also waits for the wave's earlier row
+// stores, which the same counter tracks on gfx950, so a token's R rows went
+// out one after the other.
+__device__ __forceinline__ int send_pos_at(const int32_t* send_pos, size_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)send_pos)[i];
+}
+
 // OCP e4m3fn code of q (|q| <= 448), round to nearest, ties to even. For
 // |q| >= 2^-6 with 2^E <= |q| < 2^(E+1): N = rne(|q| * 2^(3-E)) in [8, 16],
 // code = (E + 6) * 8 + N (N = 16 carries into the next exponent). Below 2^-6
@@ -142,7 +152,7 @@ __device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x
                                            uint8_t* __restrict__ codes, float* __restrict__ scales,
                                            const int32_t* __restrict__ send_pos, int NT, int T,
                                            int R, int H, int nseg, float* tok_scale) {
-  const int tok = w / nseg;
+  const int tok = wave_uniform(w / nseg);
   if (tok >= NT) return;
   const int lane = lane_id();
   const int n16 = H / 8;
@@ -171,7 +181,7 @@ __device__ __forceinline__ void quant_wave(int w, const uint16_t* __restrict__ x
   const int seg_blocks = nblk - blk0 < kQBlocks ? nblk - blk0 : kQBlocks;
   if (!ROW_SCALES && lane < seg_blocks) tok_scale[blk0 + lane] = my_scale;
   for (int k = 0; k < R; ++k) {
-    const int p = send_pos[(size_t)tok * R + k];
+    const int p = send_pos_at(send_pos, (size_t)tok * R + k);
     if (p < 0 || p >= TR) continue;
     const size_t row = (size_t)s * TR + p;
     uint64_t* crow = (uint64_t*)(codes + row * H);  // 8 codes per chunk
@@ -222,8 +232,8 @@ __global__ __launch_bounds__(kTokThreads) void pack_quant_tok_kernel(
   const int nblk = H / 128;
   const int TR = T * R;
   const int s = tok / T;
-  for (int k = wv; k < R; k += kTokWaves) {
-    const int pos = p.send_pos[(size_t)tok * R + k];
+  for (int k = wave_uniform(wv); k < R; k += kTokWaves) {
+    const int pos = send_pos_at(p.send_pos, (size_t)tok * R + k);
     if (pos < 0 || pos >= TR) continue;
     if (lane < nblk)
       __builtin_nontemporal_store(tok_scale[lane], &scales[((size_t)s * TR + pos) * nblk + lane]);
