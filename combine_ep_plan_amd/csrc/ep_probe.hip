@@ -3,11 +3,11 @@
 // 16-byte chunks l, l + 64, ... of its wave's piece; non-temporal stores).
 // Measurement only: no step of dispatch or combine runs here.
 //
-// A launch splits its output into pieces of piece_bytes, in output order.
-// By default wave w moves piece w and exits, so consecutive waves write
-// consecutive pieces; with `waves` set, that many waves walk the pieces
-// grid-stride. The XCD option renumbers blocks as the sender does, so XCD x
-// takes the x-th eighth of the pieces.
+// A launch walks `rows` rows (output rows; source rows for read and the
+// scatters) in pieces of piece_bytes. By default wave w moves piece w and
+// exits, so consecutive waves take consecutive pieces; with `waves` set,
+// that many waves walk the pieces grid-stride. The XCD option renumbers
+// blocks as the sender does, so XCD x takes the x-th eighth of the pieces.
 //
 // Modes:
 //   copy: out row i, piece p = the xor of its fan_in source rows' piece p,
@@ -40,7 +40,7 @@ struct ProbeArgs {
   int32_t rows, indexed_rows;
   int32_t row16, piece16;  // 16-byte chunks per row and per piece
   int32_t ppr;             // pieces per row
-  uint32_t div_m, div_l;   // n / ppr = (mulhi(n, m) + n) >> l
+  uint32_t div_m, div_l;   // n / ppr = (mulhi(n, m) + n) >> l (Granlund-Montgomery)
   int32_t pieces;          // rows * ppr
   int32_t fan_in;          // source rows per output row (a multiple of F), or the reverse
   int32_t stride;          // waves of a grid-stride launch, 0 otherwise
@@ -53,11 +53,10 @@ __device__ __forceinline__ u32x4 probe_load(const u32x4* p) {
   else return *p;
 }
 
-// One piece. V chunks per lane and F of the fan_in source rows are in
-// flight per batch.
-// The table is read-only for the launch: read through the constant address
-// space, each wave-uniform entry comes by one scalar load, as the sender's
-// send_slot entry does.
+// One piece w. V chunks per lane, and F of the fan_in source rows, are in
+// flight per batch. The table is read-only for the launch; read through the
+// constant address space, each wave-uniform entry comes by one scalar load,
+// as the sender's send_slot entry does.
 template <int MODE, int V, int F, bool NT>
 __device__ __forceinline__ void probe_piece(const ProbeArgs& a, int w) {
   const int row = wave_uniform(
