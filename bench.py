@@ -855,6 +855,8 @@ def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
         slots stably sorted by expert) with cached loads and the XCD
         renumbering, without the renumbering, and with non-temporal loads;
         1, 2, 7 and 14 KB per wave;
+      - the receiver's row pairs at the decode size in receive order (the
+        library's) and in send order (a scatter);
       - the combine's mix: 4096 rows of 14 KB, each the xor of 8 rows from 8
         linear regions (470 MB read, 59 MB written), 1, 2, 7 and 14 KB per
         wave, 2 or 8 rows in flight, cached and non-temporal loads; the same
@@ -957,6 +959,30 @@ def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
     res["copy_decode_size"] = {
         "bytes": {"linear_and_permuted": copy_bytes, "sender_like": send_bytes},
         "figures": copies}
+
+    # The receiver's row pairs (send row -> grouped row of the decode
+    # routing) in two orders, 1 KB per wave, non-temporal loads: receive
+    # order (grouped rows written in order, send rows read as the table
+    # says) and send order (send rows read in order, grouped rows written
+    # where they belong: a scatter of one row each).
+    TR = T * R
+    pos = np.empty_like(order)
+    np.put_along_axis(pos, order, np.arange(TR)[None, :], axis=1)
+    send_row = (np.arange(N)[:, None] * TR + pos).reshape(-1)    # slot -> send row
+    recv_order = np.argsort(idx.reshape(-1), kind="stable")      # grouped row -> slot
+    grouped_of_slot = np.empty(nrows, np.int64)
+    grouped_of_slot[recv_order] = np.arange(nrows)
+    slot_of_send_row = (np.arange(N)[:, None] * TR + order).reshape(-1)
+    gather_t = torch.from_numpy(send_row[recv_order].astype(np.int32)).cuda()
+    scatter_t = torch.from_numpy(grouped_of_slot[slot_of_send_row].astype(np.int32)).cuda()
+    res["receiver_orders_decode_size"] = {
+        "bytes": copy_bytes,
+        "receive_order": fig(probe(dst, src_big, gather_t, nrows, nrows, row, 1024, flags=NTL),
+                             copy_bytes),
+        "send_order": fig(probe(dst, src_big, scatter_t, nrows, nrows, row, 1024,
+                                mode=ep.EP_PROBE_SCATTER, flags=NTL), copy_bytes),
+    }
+    del gather_t, scatter_t
 
     # The combine's 8:1 mix over the same 470 MB.
     out_rows = N * T

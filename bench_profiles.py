@@ -317,6 +317,16 @@ def pattern(timing_json: str) -> str:
         out.append(f"| {k.split('_')[0]} | {cell(f['linear'])} | {cell(f['rows_permuted'])} | "
                    f"{cell(f['sender_like_cached_xcd'])} | {cell(f['sender_like_cached'])} | "
                    f"{cell(f['sender_like_nt_xcd'])} |")
+    if "receiver_orders_decode_size" in t:
+        ro = t["receiver_orders_decode_size"]
+        out += ["", "## The receiver's row pairs at the decode size", "",
+                f"The decode routing's 32768 (send row, grouped row) pairs, {ro['bytes']} bytes "
+                "(read + write), 1 KB per wave, non-temporal loads. Receive order writes the "
+                "grouped rows in order and reads the send rows the table names (the library's "
+                "receiver); send order reads the send rows in order and scatters each to its "
+                "grouped row.", "", "| order | µs (TB/s) |", "|---|---|",
+                f"| receive order | {cell(ro['receive_order'])} |",
+                f"| send order | {cell(ro['send_order'])} |"]
     m = t["combine_mix_decode_size"]
     out += ["", "## The combine's 8:1 mix at the decode size", "",
             f"4096 rows of 14 KB, each the xor of 8 rows from 8 linear regions: {m['bytes']} "
