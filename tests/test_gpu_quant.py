@@ -57,6 +57,12 @@ QUANT_SHAPES = [
     W.Shape("q_wide", 3, 6, 8320, 12, 3, payload=W.PAYLOAD_FP8_B128, expert="dequant", seed=10),
     W.Shape("q_wide16k", 2, 5, 16384, 8, 2, payload=W.PAYLOAD_FP8_B128, expert="dequant",
             seed=11),
+    # more send rows per token than the workgroup has waves: the scale rows
+    # go out in several rounds per wave (top-20, and the largest top-k)
+    W.Shape("q_topk20", 2, 12, 1024, 32, 20, payload=W.PAYLOAD_FP8_B128, expert="dequant",
+            seed=12),
+    W.Shape("q_topk64", 2, 5, 512, 64, 64, payload=W.PAYLOAD_FP8_B128, expert="dequant",
+            seed=13),
 ]
 
 
