@@ -464,10 +464,12 @@ def measure_split(ep, torch, d, b, sh, P: int, steps: int, warmup: int) -> dict:
     }
 
 
-def measure_presum(ep, torch, np, d, b, sh, wl, steps: int, warmup: int) -> dict:
+def measure_presum(ep, torch, np, d, b, sh, wl, alpha, steps: int, warmup: int) -> dict:
     """Combine with partial sums on the expert side next to the plain
-    combine: time, and the rows a multi-GPU combine would move back (one per
-    (token, rank) pair instead of one per slot)."""
+    combine: time, the rows a multi-GPU combine would move back (one per
+    (token, rank) pair instead of one per slot), and how far the partial
+    sums' extra roundings move the result (every element, against the plain
+    combine, relative to sum_k |w_k y_k|)."""
     import statistics as st
 
     N, T, R, H, E = sh.n_ranks, sh.tokens, sh.topk, sh.hidden, sh.n_experts
@@ -496,12 +498,34 @@ def measure_presum(ep, torch, np, d, b, sh, wl, steps: int, warmup: int) -> dict
     t_plain = timed(lambda: ep.combine(d, b.expert_out, b.weights, b.plan_ws, out, sp))
     t_pre = timed(lambda: ep.combine_presum(d, b.expert_out, b.weights, b.plan_ws, partial,
                                             out, sp))
+    # Accuracy: the partial-sum combine against the plain one, per element,
+    # relative to sum_k |w_k y_k| (the plain combine of |y| with |w|: the
+    # library computes the denominators too). The plain combine itself is
+    # within the parity bar of the exact sum.
+    def f32(t):
+        return (t.to(torch.int32) << 16).view(torch.float32)
+
+    ep.combine(d, b.expert_out, b.weights, b.plan_ws, out, sp)
+    plain = f32(out)
+    ep.combine_presum(d, b.expert_out, b.weights, b.plan_ws, partial, out, sp)
+    pre = f32(out)
+    # |y| in place (the expert rows can be ~100 GB at prefill, no room for a
+    # copy), then the stand-in expert writes them back as they were.
+    b.expert_out.bitwise_and_(0x7FFF)
+    ep.combine(d, b.expert_out, b.weights.abs(), b.plan_ws, out, sp)
+    den = f32(out)
+    ep.expert_stub(d, b.grouped, alpha, b.plan_ws, b.expert_out, sp)
+    torch.cuda.synchronize()
+    live = den > 0
+    rel = ((pre - plain).abs() / den.clamp_min(1e-30))[live]
     row = 2 * H
     NT, NTR = N * T, N * T * R
     one_gpu = NTR * row + 2 * pairs * row + NT * row + 4 * NTR
     return {
         "combine_us": round(t_plain, 2),
         "presum_combine_us": round(t_pre, 2),
+        "presum_vs_plain_max_rel_to_sum_abs": float(rel.max().item()) if rel.numel() else 0.0,
+        "presum_vs_plain_mean_rel_to_sum_abs": float(rel.mean().item()) if rel.numel() else 0.0,
         "rows_returned": pairs,
         "rows_returned_plain": NTR,
         "returned_fraction": round(pairs / NTR, 4),
@@ -1421,7 +1445,7 @@ def main() -> int:
 
     presum = None
     if args.presum:
-        presum = measure_presum(ep, torch, np, d, b, sh, wl, args.steps, args.warmup)
+        presum = measure_presum(ep, torch, np, d, b, sh, wl, alpha, args.steps, args.warmup)
 
     staged = None
     if args.staged:
