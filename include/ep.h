@@ -69,7 +69,7 @@ extern "C" {
 /* Return codes (host side). */
 #define EP_OK 0
 #define EP_ERR_INVALID_ARG (-1)     /* bad descriptor, size or null pointer */
-#define EP_ERR_UNSUPPORTED (-2)     /* valid but outside this build's limits */
+#define EP_ERR_UNSUPPORTED (-2)     /* valid but outside the library's limits */
 #define EP_ERR_DEVICE_MISMATCH (-3) /* a buffer is not on the stream's GPU */
 #define EP_ERR_HIP (-4)             /* a HIP runtime call failed */
 
@@ -83,7 +83,7 @@ extern "C" {
 #define EP_PAYLOAD_FP8_B128 1 /* plane 0: H OCP e4m3fn codes (H bytes);
                                  plane 1: H/128 fp32 block scales (H/32 B) */
 
-/* Largest sizes this build accepts (EP_ERR_UNSUPPORTED beyond them). */
+/* Largest sizes the library accepts (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_EXPERTS 2048
 #define EP_MAX_TOPK 64
 
