@@ -73,7 +73,7 @@ def read_stats(path: str):
     return rows, {short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
 
 
-def trace(workload: str, stats_csv: str, args: str) -> str:
+def trace(workload: str, stats_csv: str, args: str, out_dir: str = None) -> str:
     """Kernel statistics of one run; with the per-dispatch trace beside the
     statistics file, also grouped by kernel and grid size, which tells the
     workloads of one run apart (each launches its kernels on its own grid)."""
@@ -110,7 +110,7 @@ def trace(workload: str, stats_csv: str, args: str) -> str:
         for (name, grid), ts in groups.items():
             out.append(f"| {name} | {grid} | {len(ts)} | {sum(ts) / len(ts):.2f} | "
                        f"{min(ts):.2f} | {max(ts):.2f} |")
-    path = os.path.join(PROFILES, f"{workload}_kernel_trace.md")
+    path = os.path.join(out_dir or PROFILES, f"{workload}_kernel_trace.md")
     with open(path, "w") as fh:
         fh.write("\n".join(out) + "\n")
     return path
@@ -130,7 +130,8 @@ def counter_means(path: str) -> dict:
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
-def traffic(workload: str, fetch_csv: str, write_csv: str, stats_csv: str, args: str):
+def traffic(workload: str, fetch_csv: str, write_csv: str, stats_csv: str, args: str,
+            out_dir: str = None):
     import bench
     import ep_workloads as W
 
@@ -191,8 +192,8 @@ def traffic(workload: str, fetch_csv: str, write_csv: str, stats_csv: str, args:
            "touches for the sender).",
            "traffic_" + workload + ".json holds these figures with a source hash per stage; "
            "bench.py reports a stage's traffic only while its kernels hash the same."]
-    p_md = os.path.join(PROFILES, f"{workload}_hbm_traffic.md")
-    p_js = os.path.join(PROFILES, f"traffic_{workload}.json")
+    p_md = os.path.join(out_dir or PROFILES, f"{workload}_hbm_traffic.md")
+    p_js = os.path.join(out_dir or PROFILES, f"traffic_{workload}.json")
     with open(p_md, "w") as fh:
         fh.write("\n".join(md) + "\n")
     with open(p_js, "w") as fh:
@@ -277,7 +278,7 @@ def probe(title: str, workloads: str, timing_json: str, counter_csvs: list) -> s
     return path
 
 
-def pattern(timing_json: str) -> str:
+def pattern(timing_json: str, out_dir: str = None) -> str:
     """Tables of one `bench.py --pattern-probe` run -> profiles/access_pattern_probe.md."""
     with open(timing_json) as fh:
         t = json.loads(fh.read().strip().splitlines()[-1])["pattern_probe"]
@@ -354,7 +355,7 @@ def pattern(timing_json: str) -> str:
         for k, e in t["sender_orders_by_source_size"].items():
             out.append(f"| {k.split('_')[0]} | {e['tokens']} | {cell(e['send_order_1KB'])} | "
                        f"{cell(e['token_order_1KB'])} | {cell(e['token_order_14KB'])} |")
-    path = os.path.join(PROFILES, "access_pattern_probe.md")
+    path = os.path.join(out_dir or PROFILES, "access_pattern_probe.md")
     with open(path, "w") as fh:
         fh.write("\n".join(out) + "\n")
     return path
