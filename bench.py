@@ -881,6 +881,9 @@ def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
         1, 2, 7 and 14 KB per wave;
       - the receiver's row pairs at the decode size in receive order (the
         library's) and in send order (a scatter);
+      - workgroups of four waves against one wave at the decode size, 1 KB
+        per wave: linear copy, rows permuted, the receiver's pairs in
+        receive order, the combine's mix (8 rows in flight), fill and read;
       - the combine's mix: 4096 rows of 14 KB, each the xor of 8 rows from 8
         linear regions (470 MB read, 59 MB written), 1, 2, 7 and 14 KB per
         wave, 2 or 8 rows in flight, cached and non-temporal loads; the same
@@ -1006,6 +1009,29 @@ def measure_pattern_probe(ep, torch, np, W, flush, reps: int = 5) -> dict:
         "send_order": fig(probe(dst, src_big, scatter_t, nrows, nrows, row, 1024,
                                 mode=ep.EP_PROBE_SCATTER, flags=NTL), copy_bytes),
     }
+
+    # Workgroup size: the same shapes with workgroups of four waves (the
+    # library's default) and of one wave (the receiver's), 1 KB per wave,
+    # non-temporal loads.
+    out_rows = N * T
+    wg = {}
+    for name, fl in (("four_waves", NTL), ("one_wave", NTL | ep.EP_PROBE_ONE_WAVE)):
+        wg[name] = {
+            "linear_copy": fig(probe(dst, src_big, None, nrows, nrows, row, 1024, flags=fl),
+                               copy_bytes),
+            "rows_permuted": fig(probe(dst, src_big, perm, nrows, nrows, row, 1024, flags=fl),
+                                 copy_bytes),
+            "receiver_pairs_receive_order": fig(
+                probe(dst, src_big, gather_t, nrows, nrows, row, 1024, flags=fl), copy_bytes),
+            "combine_mix_8_in_flight": fig(
+                probe(dst[:out_rows], src_big, None, out_rows, nrows, row, 1024, fan_in=8,
+                      in_flight=8, flags=fl), nrows * row + out_rows * row),
+            "fill": fig(probe(dst, None, None, nrows, 0, row, 1024, mode=FILL,
+                              flags=fl & ep.EP_PROBE_ONE_WAVE), nrows * row),
+            "read": fig(probe(dst[:1], src_big, None, nrows, nrows, row, 1024, mode=READ,
+                              flags=fl), nrows * row),
+        }
+    res["workgroup_size_decode_size"] = wg
     del gather_t, scatter_t
 
     # The combine's 8:1 mix over the same 470 MB.

@@ -73,6 +73,27 @@ def read_stats(path: str):
     return rows, {short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
 
 
+LIBRARY_PREFIXES = ("plan_", "pack_", "recv_", "combine_", "expert_", "presum", "kv_", "staged_",
+                    "window_", "probe_")
+B2B_RUN = 20
+
+
+def back_to_back_runs(timeline):
+    """Maximal runs of consecutive dispatches (in start order) of one library
+    kernel on one grid, at least B2B_RUN long: [((name, grid), [durations])]."""
+    runs, cur = [], None
+    for _, key, t in sorted(timeline, key=lambda x: x[0]):
+        if cur is not None and cur[0] == key:
+            cur[1].append(t)
+            continue
+        if cur is not None and len(cur[1]) >= B2B_RUN and cur[0][0].startswith(LIBRARY_PREFIXES):
+            runs.append(cur)
+        cur = (key, [t])
+    if cur is not None and len(cur[1]) >= B2B_RUN and cur[0][0].startswith(LIBRARY_PREFIXES):
+        runs.append(cur)
+    return runs
+
+
 def trace(workload: str, stats_csv: str, args: str, out_dir: str = None) -> str:
     """Kernel statistics of one run; with the per-dispatch trace beside the
     statistics file, also grouped by kernel and grid size, which tells the
@@ -96,13 +117,14 @@ def trace(workload: str, stats_csv: str, args: str, out_dir: str = None) -> str:
                                 os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
     if os.path.exists(per_dispatch):
         groups = collections.OrderedDict()
+        timeline = []   # (start, key, duration) of every dispatch, library or not
         for r in csv.DictReader(open(per_dispatch)):
             name = short(r["Kernel_Name"])
-            if not name.startswith(("plan_", "pack_", "recv_", "combine_", "expert_", "presum",
-                                    "kv_", "staged_", "window_", "probe_")):
-                continue
             key = (name, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
             t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            timeline.append((int(r["Start_Timestamp"]), key, t))
+            if not name.startswith(LIBRARY_PREFIXES):
+                continue
             groups.setdefault(key, []).append(t)
         out += ["", "The library's kernels by launch grid (threads), in order of first launch:", "",
                 "| kernel | grid threads | calls | avg us | min us | max us |",
@@ -110,6 +132,17 @@ def trace(workload: str, stats_csv: str, args: str, out_dir: str = None) -> str:
         for (name, grid), ts in groups.items():
             out.append(f"| {name} | {grid} | {len(ts)} | {sum(ts) / len(ts):.2f} | "
                        f"{min(ts):.2f} | {max(ts):.2f} |")
+        runs = back_to_back_runs(timeline)
+        if runs:
+            out += ["", f"Runs of at least {B2B_RUN} consecutive launches of one library kernel "
+                    "on one grid, with no other dispatch between them (bench.py's roofline "
+                    "loops: 20 launches of a workload's dominant kernel between two events), "
+                    "in order:", "",
+                    "| kernel | grid threads | launches | avg us | min us | max us |",
+                    "|---|---|---|---|---|---|"]
+            for (name, grid), ts in runs:
+                out.append(f"| {name} | {grid} | {len(ts)} | {sum(ts) / len(ts):.2f} | "
+                           f"{min(ts):.2f} | {max(ts):.2f} |")
     path = os.path.join(out_dir or PROFILES, f"{workload}_kernel_trace.md")
     with open(path, "w") as fh:
         fh.write("\n".join(out) + "\n")
@@ -328,6 +361,19 @@ def pattern(timing_json: str, out_dir: str = None) -> str:
                 "grouped row.", "", "| order | µs (TB/s) |", "|---|---|",
                 f"| receive order | {cell(ro['receive_order'])} |",
                 f"| send order | {cell(ro['send_order'])} |"]
+    if "workgroup_size_decode_size" in t:
+        wg = t["workgroup_size_decode_size"]
+        labels = {"linear_copy": "linear copy", "rows_permuted": "rows permuted",
+                  "receiver_pairs_receive_order": "the receiver's pairs, receive order",
+                  "combine_mix_8_in_flight": "the combine's 8:1 mix, 8 rows in flight",
+                  "fill": "fill", "read": "read"}
+        out += ["", "## Workgroups of four waves against one at the decode size", "",
+                "The same shapes, 1 KB per wave, non-temporal loads; copies move 939524096 "
+                "bytes (read + write), the mix 528482304, fill and read 469762048.", "",
+                "| shape | four waves | one wave |", "|---|---|---|"]
+        for k in wg["four_waves"]:
+            out.append(f"| {labels.get(k, k)} | {cell(wg['four_waves'][k])} | "
+                       f"{cell(wg['one_wave'][k])} |")
     m = t["combine_mix_decode_size"]
     out += ["", "## The combine's 8:1 mix at the decode size", "",
             f"4096 rows of 14 KB, each the xor of 8 rows from 8 linear regions: {m['bytes']} "

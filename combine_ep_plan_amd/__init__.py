@@ -29,7 +29,7 @@ EP_PAYLOAD_BF16 = 0
 EP_PAYLOAD_FP8_B128 = 1
 EP_KV_STATIC_SLOTS = 64
 EP_PROBE_COPY, EP_PROBE_FILL, EP_PROBE_READ, EP_PROBE_SCATTER, EP_PROBE_SCATTER_WIDE = range(5)
-EP_PROBE_NT_LOADS, EP_PROBE_XCD = 1, 2
+EP_PROBE_NT_LOADS, EP_PROBE_XCD, EP_PROBE_ONE_WAVE = 1, 2, 4
 
 # Every entry point the C header declares (checked by the tests).
 EXPORTS = (

@@ -690,7 +690,7 @@ int ep_probe_pattern(void* dst, const void* src, const int32_t* table, int64_t r
   const bool scatter = mode == EP_PROBE_SCATTER || mode == EP_PROBE_SCATTER_WIDE;
   if (mode != EP_PROBE_COPY && mode != EP_PROBE_FILL && mode != EP_PROBE_READ && !scatter)
     return fail(EP_ERR_INVALID_ARG, "unknown probe mode");
-  if (flags & ~(EP_PROBE_NT_LOADS | EP_PROBE_XCD))
+  if (flags & ~(EP_PROBE_NT_LOADS | EP_PROBE_XCD | EP_PROBE_ONE_WAVE))
     return fail(EP_ERR_INVALID_ARG, "unknown probe flags");
   if (rows < 0 || indexed_rows < 0 || waves < 0)
     return fail(EP_ERR_INVALID_ARG, "rows, indexed_rows and waves must be >= 0");
@@ -747,6 +747,7 @@ int ep_probe_pattern(void* dst, const void* src, const int32_t* table, int64_t r
   sh.mode = mode;
   sh.nt_loads = (flags & EP_PROBE_NT_LOADS) != 0;
   sh.xcd = (flags & EP_PROBE_XCD) != 0;
+  sh.one_wave = (flags & EP_PROBE_ONE_WAVE) != 0;
   sh.waves = (int32_t)waves;
   const hipError_t e = ep::launch_probe_pattern(sh, stream);
   if (e != hipSuccess) return fail_hip(e, "ep_probe_pattern");

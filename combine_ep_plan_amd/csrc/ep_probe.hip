@@ -45,6 +45,7 @@ struct ProbeArgs {
   int32_t fan_in;          // source rows per output row (a multiple of F), or the reverse
   int32_t stride;          // waves of a grid-stride launch, 0 otherwise
   int32_t xcd, nb;         // XCD renumbering; launched blocks (a multiple of 8 with it)
+  int32_t wpb;             // waves per workgroup: 1 or kProbeWaves
 };
 
 template <bool NT>
@@ -133,7 +134,7 @@ template <int MODE, int V, int F, bool NT>
 __global__ __launch_bounds__(kProbeBlock) void probe_pattern_kernel(ProbeArgs a) {
   int b = blockIdx.x;
   if (a.xcd) b = (b & 7) * (a.nb >> 3) + (b >> 3);
-  const int first = b * kProbeWaves + wave_uniform((int)threadIdx.x / kWave);
+  const int first = b * a.wpb + wave_uniform((int)threadIdx.x / kWave);
   if (a.stride == 0) {
     if (first < a.pieces) probe_piece<MODE, V, F, NT>(a, first);
     return;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kProbeBlock) void probe_pattern_kernel(ProbeArgs a)
 
 template <int MODE, int V, int F>
 hipError_t launch_v(const ProbeArgs& a, bool nt, hipStream_t stream) {
-  const dim3 grid((unsigned)a.nb), block(kProbeBlock);
+  const dim3 grid((unsigned)a.nb), block((unsigned)(a.wpb * kWave));
   if constexpr (MODE == kProbeFill) {
     hipLaunchKernelGGL((probe_pattern_kernel<MODE, V, F, false>), grid, block, 0, stream, a);
   } else {
@@ -199,7 +200,8 @@ hipError_t launch_probe_pattern(const ProbeShape& s, hipStream_t stream) {
   if (a.pieces == 0) return hipSuccess;
   const int64_t waves = s.waves > 0 ? s.waves : a.pieces;
   a.stride = s.waves > 0 ? s.waves : 0;
-  int64_t nb = (waves + kProbeWaves - 1) / kProbeWaves;
+  a.wpb = s.one_wave ? 1 : kProbeWaves;
+  int64_t nb = (waves + a.wpb - 1) / a.wpb;
   a.xcd = s.xcd ? 1 : 0;
   if (s.xcd) nb = (nb + 7) / 8 * 8;
   a.nb = (int32_t)nb;

@@ -29,6 +29,7 @@ struct ProbeShape {
   int32_t mode;          // ProbeMode
   bool nt_loads;         // non-temporal loads (else ordinary cached ones)
   bool xcd;              // renumber blocks per XCD
+  bool one_wave;         // workgroups of one wave (else four)
   int32_t waves;         // 0: one piece per wave; > 0: that many waves, grid-stride
 };
 

@@ -490,7 +490,8 @@ EP_API int ep_probe_copy(void *dst, const void *src, size_t bytes,
  *   Fill and read take fan_in = in_flight = 1.
  * Flags: EP_PROBE_NT_LOADS (non-temporal loads; else ordinary cached ones),
  * EP_PROBE_XCD (blocks renumbered as the sender's: XCD x takes the x-th
- * eighth of the pieces; one piece per wave only).
+ * eighth of the pieces; one piece per wave only), EP_PROBE_ONE_WAVE
+ * (workgroups of one wave instead of four, as the receiver launches).
  * Rows are row_bytes long, row-major; all buffers are caller-owned device
  * memory on the stream's GPU. row_bytes must be a multiple of piece_bytes,
  * piece_bytes of 1024. Returns EP_ERR_INVALID_ARG for a bad size, mode, flag
@@ -502,6 +503,7 @@ EP_API int ep_probe_copy(void *dst, const void *src, size_t bytes,
 #define EP_PROBE_SCATTER_WIDE 4
 #define EP_PROBE_NT_LOADS 1
 #define EP_PROBE_XCD 2
+#define EP_PROBE_ONE_WAVE 4
 EP_API int ep_probe_pattern(void *dst, const void *src, const int32_t *table,
                             int64_t rows, int64_t indexed_rows, int64_t row_bytes,
                             int64_t piece_bytes, int fan_in, int in_flight, int mode,

@@ -104,7 +104,7 @@ def test_invalid_descriptors_fail_fast(bad, code):
 # (rows, indexed_rows, row_bytes, piece_bytes, fan_in, in_flight, mode, flags, waves).
 @pytest.mark.parametrize("args,code", [
     ((4, 4, 14336, 1024, 1, 1, 5, 0, 0), ep.EP_ERR_INVALID_ARG),          # unknown mode
-    ((4, 4, 14336, 1024, 1, 1, 0, 4, 0), ep.EP_ERR_INVALID_ARG),          # unknown flag
+    ((4, 4, 14336, 1024, 1, 1, 0, 8, 0), ep.EP_ERR_INVALID_ARG),          # unknown flag
     ((-1, 4, 14336, 1024, 1, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),         # negative rows
     ((4, 4, 14336, 1000, 1, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),          # piece not 1 KB steps
     ((4, 4, 14336, 4096, 1, 1, 0, 0, 0), ep.EP_ERR_INVALID_ARG),          # piece does not divide row

@@ -92,6 +92,8 @@ def test_pattern_tables_render_every_section(tmp_path):
          "copy_decode_size": {"bytes": {"linear_and_permuted": 1, "sender_like": 2},
                               "figures": {"1KB_per_wave": copies}},
          "receiver_orders_decode_size": {"bytes": 3, "receive_order": f, "send_order": f},
+         "workgroup_size_decode_size": {"four_waves": {"linear_copy": f, "fill": f},
+                                        "one_wave": {"linear_copy": f, "fill": f}},
          "combine_mix_decode_size": {"bytes": 4, "figures": {"read_only_1KB_nt": f}},
          "mall_reuse": {"32MB": reuse},
          "sender_orders_by_source_size": {"1.8MB_per_source": {
@@ -99,9 +101,37 @@ def test_pattern_tables_render_every_section(tmp_path):
     (tmp_path / "p.json").write_text("some log line\n" + json.dumps({"pattern_probe": t}) + "\n")
     text = open(bp.pattern(str(tmp_path / "p.json"), out_dir=str(tmp_path))).read()
     for head in ("## Fills of 1 GiB", "## Copies of 1 GiB", "## Copies of the decode size",
-                 "## The receiver's row pairs", "## The combine's 8:1 mix",
+                 "## The receiver's row pairs", "## Workgroups of four waves against one",
+                 "## The combine's 8:1 mix",
                  "## Reuse from the memory-side cache", "## The sender's orders"):
         assert head in text
     assert "| 1KB | 10.0 (1.0) |" in text
+    assert "| linear copy | 10.0 (1.0) | 10.0 (1.0) |" in text
     assert "| 32MB | cached | 10.0 (1.0) | 10.0 (1.0) | 10.0 (1.0) |" in text
     assert "| 1.8MB | 128 | 10.0 (1.0) |" in text
+
+
+def test_trace_lists_back_to_back_runs(tmp_path):
+    """The roofline loop's launches (20 or more of one kernel and grid with no
+    other dispatch between them) are tabulated apart from the in-step ones."""
+    recv = "void ep::(anonymous namespace)::recv_rows_kernel<false>(ep::RecvArgs)"
+    pack = "void ep::(anonymous namespace)::pack_gather_kernel<true, false>(ep::GatherArgs)"
+    stats(tmp_path / "run_kernel_stats.csv", [(recv, 23, 100000.0, 90.0), (pack, 3, 5000.0, 10.0)])
+    rows, t = [], 0
+    for k in range(2):                      # two steps: pack then recv (150 us)
+        rows += [(pack, 4096, t, t + 70000), (recv, 4096, t + 80000, t + 230000)]
+        t += 300000
+    rows.append((pack, 4096, t, t + 70000))  # the loop's own plan and sender pass
+    t += 80000
+    for k in range(21):                     # the roofline loop: 21 launches of 140 us
+        rows.append((recv, 4096, t, t + 140000))
+        t += 150000
+    rows.append((recv, 8192, t, t + 50000))  # another grid right after: not part of the run
+    write_csv(tmp_path / "run_kernel_trace.csv",
+              ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp",
+               "End_Timestamp"], [(n, g, 1, 1, a, b) for n, g, a, b in rows[::-1]])
+    text = open(bp.trace("toy", str(tmp_path / "run_kernel_stats.csv"), "--config toy",
+                         out_dir=str(tmp_path))).read()
+    assert "| recv_rows_kernel<false> | 4096 | 23 | 140.87 | 140.00 | 150.00 |" in text
+    assert "| recv_rows_kernel<false> | 4096 | 21 | 140.00 | 140.00 | 140.00 |" in text
+    assert text.count("| 21 | 140.00 |") == 1

@@ -39,7 +39,10 @@ def xor_rows(a, idx):
 
 @pytest.mark.parametrize("piece", [1024, 2048, 7168, 14336])
 @pytest.mark.parametrize("flags,waves", [(0, 0), (ep.EP_PROBE_NT_LOADS, 0),
-                                         (ep.EP_PROBE_XCD, 0), (0, 24)])
+                                         (ep.EP_PROBE_XCD, 0), (0, 24),
+                                         (ep.EP_PROBE_ONE_WAVE, 0),
+                                         (ep.EP_PROBE_ONE_WAVE | ep.EP_PROBE_XCD, 0),
+                                         (ep.EP_PROBE_ONE_WAVE | ep.EP_PROBE_NT_LOADS, 24)])
 def test_linear_copy(piece, flags, waves):
     rng = np.random.default_rng(piece + flags + waves)
     rows = 37
@@ -66,6 +69,10 @@ def test_table_copy_and_mix(fan_in, in_flight, piece):
     dst = torch.zeros((rows, ROW), dtype=torch.uint8, device="cuda")
     got = run(dst, src, table, rows, src_rows, piece, fan_in, flags=ep.EP_PROBE_XCD,
               in_flight=in_flight)
+    assert np.array_equal(got, xor_rows(a, want_idx))
+    dst.zero_()
+    got = run(dst, src, table, rows, src_rows, piece, fan_in,
+              flags=ep.EP_PROBE_ONE_WAVE | ep.EP_PROBE_NT_LOADS, in_flight=in_flight)
     assert np.array_equal(got, xor_rows(a, want_idx))
 
 
@@ -134,13 +141,14 @@ def test_scatter_wide(piece, flags):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("flags", [0, ep.EP_PROBE_ONE_WAVE])
 @pytest.mark.parametrize("piece,waves", [(1024, 0), (4096, 0), (65536, 0), (1024, 40)])
-def test_fill_pattern(piece, waves):
+def test_fill_pattern(piece, waves, flags):
     row = 65536
     rows = 5
     dst = torch.zeros((rows, row), dtype=torch.uint8, device="cuda")
     got = run(dst, None, None, rows, 0, piece, mode=ep.EP_PROBE_FILL, waves=waves,
-              row=row).view(np.uint32).reshape(-1, 4)
+              row=row, flags=flags).view(np.uint32).reshape(-1, 4)
     chunk = np.arange(rows * row // 16)
     per_piece = piece // 16
     w = chunk // per_piece
