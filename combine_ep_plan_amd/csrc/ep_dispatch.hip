@@ -31,9 +31,11 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWavesPerBlock * kWave;
-// The receiver runs one wave per workgroup. Measured on gfx950 against four
-// (same pieces, same order, 20 back-to-back launches): 143.5 against
-// 148.5 us at decode scale, 282 against 302 us on the all-to-one workload.
+// The receiver (and the staged transfer and unpack, the same 1 KB-piece
+// copies) run one wave per workgroup. Measured on gfx950 against four (same
+// pieces, same order, 20 back-to-back launches): 143.5 against 148.5 us at
+// decode scale, 282 against 302 us on the all-to-one workload; transfer +
+// unpack at decode 284-289 against 295-297 us.
 // The finer grain lets the dispatcher keep every CU's wave slots filled
 // with independent 1 KB pieces. The senders keep four-wave groups, since
 // their exchange blocks need a whole 256-thread block.
@@ -510,11 +512,11 @@ __device__ __forceinline__ void staged_wave(const StagedArgs& a, const MovePlane
 }
 
 template <bool TRANSFER>
-__global__ __launch_bounds__(kBlock) void staged_kernel(StagedArgs a) {
+__global__ __launch_bounds__(kRecvBlock) void staged_kernel(StagedArgs a) {
   int b = blockIdx.x;
   const int q = b < a.pl[0].blocks ? 0 : 1;
   if (q) b -= a.pl[0].blocks;
-  const int w = b * kWavesPerBlock + (int)threadIdx.x / kWave;
+  const int w = b * kRecvWaves + (int)threadIdx.x / kWave;
   if (w < a.pl[q].waves) staged_wave<TRANSFER>(a, a.pl[q], w);
 }
 
@@ -908,7 +910,8 @@ hipError_t launch_staged(const Dims& d, const void* const src[2], const PlanPtrs
                          void* const dst[2], hipStream_t stream) {
   if (d.NTR == 0) return hipSuccess;
   StagedArgs a{};
-  for (int q = 0; q < d.planes; ++q) a.pl[q] = move_plane(src[q], dst[q], d.row[q], d.NTR);
+  for (int q = 0; q < d.planes; ++q)
+    a.pl[q] = move_plane(src[q], dst[q], d.row[q], d.NTR, kRecvWaves);
   a.send_seg = p.send_seg;
   a.recv_off = p.recv_off;
   a.recv_rows = (const int2*)p.recv_rows;
@@ -918,7 +921,7 @@ hipError_t launch_staged(const Dims& d, const void* const src[2], const PlanPtrs
   a.NTR = (int)d.NTR;
   a.cap = d.cap;
   hipLaunchKernelGGL(staged_kernel<TRANSFER>, dim3((unsigned)(a.pl[0].blocks + a.pl[1].blocks)),
-                     dim3(kBlock), 0, stream, a);
+                     dim3(kRecvBlock), 0, stream, a);
   return hipGetLastError();
 }
 

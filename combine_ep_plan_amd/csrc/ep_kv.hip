@@ -13,8 +13,15 @@
 // A request's regions, concatenated in token order, form a byte stream;
 // region j covers stream bytes [first_j, first_j + bytes_j). One wave moves
 // one 7 KB piece of the stream for one rank, walking the (few) regions that
-// overlap the piece. Every region is checked against the pools before any
-// byte moves; a bad one is skipped and flagged.
+// overlap the piece; workgroups are one wave, as in the receiver (a copy).
+// The wave finds its first region with a 64-way search, one region per lane
+// and round, instead of a binary search's 7-10 dependent loads. Measured on
+// gfx950 at 16k tokens x 8 ranks (8.59 GB, 111 regions): 1498-1505 us
+// against 1548-1579 us with four-wave groups and the binary search; the
+// staged relay (launch-bound) 16.1 against 18.4 ms. 1 KB pieces lost
+// (2000-2300 us): each wave's table round trips then cover only 1 KB.
+// Every region is checked against the pools before any byte moves; a bad
+// one is skipped and flagged.
 #include <mutex>
 
 #include "ep_device.hpp"
@@ -31,7 +38,7 @@ static __device__ __align__(256) uint8_t scratch[kKvStaticSlots * kKvSlotBytes];
 
 namespace {
 
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 1;
 constexpr int kBlock = kWavesPerBlock * kWave;
 constexpr int kKvV = 7;
 constexpr int64_t kPiece = (int64_t)kWave * kKvV * 16;  // 7 KB
@@ -48,7 +55,7 @@ __device__ __forceinline__ bool region_ok(const ep_kv_region& g, int64_t src_byt
          g.src_off <= src_bytes - g.bytes && g.dst_off <= dst_bytes - g.bytes;
 }
 
-// Copy n16 (<= 448) 16-byte chunks with the wave.
+// Copy n16 (<= 64 kKvV) 16-byte chunks with the wave.
 __device__ __forceinline__ void wave_copy(const uint8_t* src, uint8_t* dst, int n16) {
   if (n16 <= 0) return;
   if (n16 > kWave) {
@@ -60,6 +67,36 @@ __device__ __forceinline__ void wave_copy(const uint8_t* src, uint8_t* dst, int 
     load_row16(r, (const u32x4*)src, 0, n16);
     store_row16(r, (u32x4*)dst, 0, n16);
   }
+}
+
+// Index of the first of the m regions that ends after stream byte p0 (m if
+// none). Region ends ascend in stream order. Each round, lane l tests
+// region lo + l * step and one ballot narrows [lo, hi] to one step; up to
+// 64 regions take one round, 4096 two. Every round shrinks the range, so
+// the loop ends for any table, and only regions below m are read.
+__device__ __forceinline__ int64_t first_region_after(const ep_kv_region* __restrict__ reg,
+                                                      int64_t m, int64_t p0) {
+  int64_t lo = 0, hi = m;  // the answer lies in [lo, hi]
+  const int lane = lane_id();
+  while (lo < hi) {
+    const int64_t step = (hi - lo + kWave - 1) / kWave;
+    const int64_t j = lo + (int64_t)lane * step;
+    bool after = true;  // lanes at or past hi: hi is an upper bound already
+    if (j < hi) {
+      const ep_kv_region g = reg[j];
+      after = g.first + g.bytes > p0;
+    }
+    const uint64_t mask = ballot(after);
+    if (mask == 0) {  // all 64 tested regions end at or before p0
+      lo += (int64_t)(kWave - 1) * step + 1;
+      continue;
+    }
+    const int k = __builtin_ctzll(mask);
+    const int64_t jk = lo + (int64_t)k * step;
+    if (jk < hi) hi = jk;
+    if (k > 0) lo += (int64_t)(k - 1) * step + 1;
+  }
+  return lo;
 }
 
 // Where the stream goes to or comes from: the region mapping into a pool,
@@ -81,12 +118,7 @@ __global__ __launch_bounds__(kBlock) void kv_copy_kernel(
   const int r = (int)(w / pieces);
   const int64_t p0 = lo + (w - (int64_t)r * pieces) * kPiece;
   const int64_t p1 = p0 + kPiece < hi ? p0 + kPiece : hi;
-  // first region ending after p0
-  int64_t a = 0, b = m;
-  while (a < b) {
-    const int64_t mid = (a + b) >> 1;
-    if (reg[mid].first + reg[mid].bytes <= p0) a = mid + 1; else b = mid;
-  }
+  const int64_t a = first_region_after(reg, m, p0);
   bool bad = false;
   for (int64_t j = a; j < m; ++j) {
     const ep_kv_region g = reg[j];
