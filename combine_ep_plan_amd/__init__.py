@@ -141,10 +141,16 @@ def make_desc(n_ranks, tokens, hidden, n_experts, topk,
 
 
 def _addr(t) -> Optional[int]:
+    """Address of a buffer: None, a raw device address, or a tensor, which
+    must be contiguous (the library reads every buffer as dense row-major
+    bytes; a strided view would be read as if it were dense)."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError(f"buffer of shape {tuple(t.shape)} and strides {t.stride()} is not "
+                         "contiguous: the library takes dense row-major buffers")
     return t.data_ptr()
 
 

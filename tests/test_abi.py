@@ -191,3 +191,19 @@ def test_window_list_view_follows_the_stated_rule(args, want):
     NTR = N * T * R
     assert v.win_list >= v.send_seg + 4 * NTR           # after the last table
     assert ep.plan_bytes(d) >= v.win_list - base + 8 * N * nwin * W_ * R
+
+
+def test_binding_rejects_strided_views():
+    """The library reads every buffer as dense row-major bytes, so the binding
+    refuses a strided view before anything reaches the C ABI."""
+    import torch
+
+    a = torch.zeros((8, 16), dtype=torch.int16)
+    assert ep._addr(a) == a.data_ptr()
+    assert ep._addr(a[2:5]) == a[2:5].data_ptr()          # a row slice stays dense
+    assert ep._addr(None) is None and ep._addr(0x1000) == 0x1000
+    for view in (a.t(), a[:, ::2], a[:, 3:7]):
+        with pytest.raises(ValueError, match="not contiguous"):
+            ep._addr(view)
+    with pytest.raises(ValueError, match="not contiguous"):
+        ep._planes([a, a.t()])
