@@ -97,11 +97,14 @@ int derive(const ep_desc* d, ep::Dims* o) {
     o->nwin = (int)((d->tokens + w - 1) / w);
   }
   // Bound on the copy grids: the row copies launch one wave per 1 KB piece
-  // of a row, at most 7x this count of 7 KB segments, so under 2^29 waves
-  // (int wave indices; grid.x below 2^27 blocks).
-  const int64_t segs = (o->row[0] + 7167) / 7168;
-  if (NTR * segs >= kMaxWaves)
-    return fail(EP_ERR_UNSUPPORTED, "rows x row segments must be < 2^26");
+  // of a row (a plane under 1 KB counts as one piece), so one launch stays
+  // under 2^26 waves: 2^32 work-items of 64 lanes, the most one dispatch
+  // can hold.
+  int64_t pieces = 0;
+  for (int q = 0; q < o->planes; ++q) pieces += (o->row[q] + 1023) / 1024;
+  if (NTR * pieces >= kMaxWaves)
+    return fail(EP_ERR_UNSUPPORTED,
+                "n_ranks * tokens * topk * (1 KB pieces per row) must be < 2^26");
   return EP_OK;
 }
 

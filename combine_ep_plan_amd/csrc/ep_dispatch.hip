@@ -37,8 +37,10 @@ constexpr int kBlock = kWavesPerBlock * kWave;
 // decode scale, 282 against 302 us on the all-to-one workload; transfer +
 // unpack at decode 284-289 against 295-297 us.
 // The finer grain lets the dispatcher keep every CU's wave slots filled
-// with independent 1 KB pieces. The senders keep four-wave groups, since
-// their exchange blocks need a whole 256-thread block.
+// with independent 1 KB pieces. The senders keep four-wave groups: with one
+// wave per group the send-order sender took 102-104 against 74-76 us at
+// decode scale (two waves: the same as four), and the count exchange that
+// runs in its first blocks needs 256 threads.
 constexpr int kRecvWaves = 1;
 constexpr int kRecvBlock = kRecvWaves * kWave;
 constexpr int kSegV = 7;   // 16-byte chunks per lane in a row segment

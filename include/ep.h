@@ -92,7 +92,8 @@ extern "C" {
  * N * T * max(R, E/N) ("Send and receive buffers"). Requirements:
  * all sizes > 0 except tokens >= 0, E % N == 0, H % 8 == 0 (bf16) or
  * H % 128 == 0 (fp8), R <= EP_MAX_TOPK, E <= EP_MAX_EXPERTS,
- * N * cap_rows < 2^31 and N * T * R < 2^26. */
+ * N * cap_rows < 2^31 and N * T * R * P < 2^26, where P is the number of
+ * 1 KB pieces of a dispatch row (ceil(bytes / 1024) per plane, summed). */
 typedef struct ep_desc {
     int32_t n_ranks;   /* N */
     int32_t tokens;    /* T, tokens per rank */

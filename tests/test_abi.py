@@ -81,6 +81,9 @@ def test_row_bytes_and_planes():
     (dict(n_experts=4096, n_ranks=4), ep.EP_ERR_UNSUPPORTED),
     (dict(topk=65, n_experts=128), ep.EP_ERR_UNSUPPORTED),
     (dict(n_ranks=64, tokens=1 << 20, topk=8, n_experts=512), ep.EP_ERR_UNSUPPORTED),
+    # 2^23 slots of 14 KB rows: 14 pieces each, over 2^26 waves in one copy
+    (dict(n_ranks=64, tokens=8192, topk=16, n_experts=256, hidden=7168),
+     ep.EP_ERR_UNSUPPORTED),
 ])
 def test_invalid_descriptors_fail_fast(bad, code):
     d = _desc(**bad)
@@ -207,3 +210,15 @@ def test_binding_rejects_strided_views():
             ep._addr(view)
     with pytest.raises(ValueError, match="not contiguous"):
         ep._planes([a, a.t()])
+
+
+def test_copy_grid_bound_counts_1kb_pieces():
+    """The copies launch one wave per 1 KB piece of every slot's row, so the
+    accepted sizes keep N T R times the pieces per row under 2^26 (one
+    launch under 2^32 work-items)."""
+    ok = _desc(n_ranks=64, tokens=4096, topk=16, n_experts=256, hidden=7168)   # 2^22 x 14
+    assert ep.plan_bytes(ok) > 0 and ep.recv_bound(ok) > 0
+    fp8 = _desc(n_ranks=64, tokens=8192, topk=16, n_experts=256, hidden=7168, payload=1)
+    assert ep.plan_bytes(fp8) == 0            # 2^23 x (7 + 1) pieces
+    narrow = _desc(n_ranks=64, tokens=8192, topk=7, n_experts=256, hidden=256)
+    assert ep.plan_bytes(narrow) > 0          # 512-byte rows: one piece each
