@@ -49,7 +49,10 @@ constexpr int kSeg = kWave * kSegV;  // 16-byte chunks per segment (7 KB)
 // gfx950 against non-temporal loads, pack took 405 vs 466 us at prefill
 // scale and 185 vs 211 us on the all-to-one workload, and was neutral at
 // decode scale. Every other copy reads non-temporally (its reads measured
-// faster that way: the receiver 157 vs 169 us at decode scale).
+// faster that way: the receiver 157 vs 169 us at decode scale; with one-wave
+// groups 142-148 vs 158-161 us, and cached reads of the send rows also
+// evicted the token rows from the memory-side cache, so the next step's
+// sender took 97-103 instead of 73 us).
 constexpr bool kPackNtLoads = false;
 
 struct Planes {
