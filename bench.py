@@ -1438,8 +1438,16 @@ def main() -> int:
     ab = algorithmic_bytes(sh, row_d, quant)
     eff = ab["step"] / (ms_per_step * 1e-3) / 1e9
 
-    # the dominant kernel against the roofline
+    # the dominant kernel against the roofline; beside its back-to-back
+    # launches, the same kernel inside a step (the four-call stage loop: the
+    # receiver right after the sender that wrote its rows)
     roof = dominant_roofline(ep, torch, d, b, sh, quant, x_bf16, ab, args.config, stream)
+    dom = max(ab["stages"], key=lambda k: ab["stages"][k])
+    in_step_ms = statistics.mean(per[dom])
+    roof["in_step_us"] = round(in_step_ms * 1e3, 2)
+    roof["in_step_frac"] = round(ab["stages"][dom] / (in_step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    roof["in_step_from"] = ("the same call inside the four-call steps of the stage loop, "
+                            "between two HIP events")
 
     # the stand-in expert, outside the step (reported, not part of the metric)
     x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -30,6 +30,9 @@ def test_bench_json_line_tiny():
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert 0 < rf["frac"] <= 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert rf["in_step_us"] > 0 and 0 < rf["in_step_frac"] <= 1
+    want = rf["algorithmic_bytes"] / (rf["in_step_us"] * 1e3) / rf["peak"]
+    assert abs(rf["in_step_frac"] - want) < 1e-4 + 1e-2 * want
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0 and cb["sample"]
     assert cb["threads"] == 1 and cb["host_nproc"] >= 1 and isinstance(cb["host_cpu_model"], str)
